@@ -1,0 +1,543 @@
+// Causal multi-head attention of the GPT-2 step, flash style (gfx950 MFMA).
+//
+// Per sequence b and head h: S = q k^T / sqrt(hs), future positions masked, P = softmax(S)
+// row-wise, y = P v ("Code you'll write": F.scaled_dot_product_attention(q, k, v,
+// is_causal=True) with the default scale). The T x T matrix never leaves the chip: keys and
+// values stream through LDS in 64-row tiles and the softmax is kept online (running max and
+// running sum, rescaling the partial output; chapter 2:00:19-2:06:39 describes the method).
+// The forward stores the row log-sum-exp; the backward recomputes P from it.
+//
+// Layouts: qkv [B*T, 3C] with q | k | v and head h in columns h*hs..h*hs+hs of each third
+// (the split/view of the attention excerpt, read in place: no transpose kernel); y, dy
+// [B*T, C]; lse [B, H, T] fp32.
+//
+// MFMA data flow. A wave computes S^T = K Q^T: its 16x16 accumulator gives lane l the
+// column query (l & 15) and the rows key 4*(l>>4)+i. That is exactly a B-operand fragment
+// of a product that sums over keys, so O^T = V^T P^T takes P straight from registers, with
+// the V^T fragment read in the matching key order from a transposed LDS copy of V. The
+// backward uses the same device: dK/dV per key block (S = Q K^T so P sums over queries),
+// and dQ per query block (S^T again) -- two kernels instead of atomics, so dQ is
+// deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+constexpr int A_THREADS = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T, int COLS>
+struct Tile {  // LDS tile of up to 64 rows x COLS elements, rows padded by 16 bytes
+    static constexpr int STRIDE = COLS * (int)sizeof(T) + 16;
+    static constexpr int BYTES = 64 * STRIDE;
+};
+
+// 8 consecutive elements (k sub-range of lane group g within a 32-wide k step)
+template <typename T>
+DEV typename FragT<T>::type frag_nat(const char* base, int stride, int row, int ks, int lane) {
+    const char* p = base + row * stride + (ks * 32 + (lane >> 4) * 8) * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) return __builtin_bit_cast(bf16x8, ld16(p));
+    else return frag_from_halves(*(const float4*)p, *(const float4*)(p + 16));
+}
+// elements {32s + 4g + 0..3} and {32s + 16 + 4g + 0..3}: the key/query order of a fragment
+// built from two 16x16 accumulator blocks
+template <typename T>
+DEV typename FragT<T>::type frag_perm(const char* base, int stride, int row, int s, int lane) {
+    const int g = lane >> 4;
+    const char* p1 = base + row * stride + (s * 32 + 4 * g) * (int)sizeof(T);
+    const char* p2 = p1 + 16 * (int)sizeof(T);
+    if constexpr (sizeof(T) == 2) return frag_from_halves(*(const uint2*)p1, *(const uint2*)p2);
+    else return frag_from_halves(*(const float4*)p1, *(const float4*)p2);
+}
+template <typename T>
+DEV typename FragT<T>::type frag_global(const T* p) {
+    if constexpr (sizeof(T) == 2) return __builtin_bit_cast(bf16x8, ld16(p));
+    else return frag_from_halves(*(const float4*)p, *(const float4*)(p + 4));
+}
+template <typename T>
+DEV typename FragT<T>::type frag_zero() {
+    typename FragT<T>::type f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = from_f<T>(0.f);
+    return f;
+}
+// fragment from two accumulators: values 0..3 from a, 4..7 from b
+template <typename T>
+DEV typename FragT<T>::type frag_from_acc(const floatx4& a, const floatx4& b) {
+    typename FragT<T>::type f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { f[j] = from_f<T>(a[j]); f[4 + j] = from_f<T>(b[j]); }
+    return f;
+}
+template <typename T>
+DEV void store4v(T* p, const floatx4& v, float s) {
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 o;
+        o[0] = (bf16)(v[0] * s); o[1] = (bf16)(v[1] * s); o[2] = (bf16)(v[2] * s); o[3] = (bf16)(v[3] * s);
+        *(bf16x4*)p = o;
+    } else {
+        *(float4*)p = make_float4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    }
+}
+
+// Stage `rows64` rows (64 max) x HS columns of a strided source into LDS, natural and/or
+// transposed. Rows >= nvalid are zero. Natural: dst[r][c]. Transposed: dstT[c][r].
+template <typename T, int HS>
+DEV void stage_rows(const T* __restrict__ src, int64_t ld, int nvalid, char* nat, char* trn, int tid) {
+    constexpr int E = 16 / sizeof(T);
+    using TN = Tile<T, HS>;
+    using TT = Tile<T, 64>;
+    if (trn == nullptr) {
+        constexpr int CPR = HS / E;  // 16-byte chunks per row
+        for (int c = tid; c < 64 * CPR; c += A_THREADS) {
+            const int r = c / CPR, cc = c % CPR;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < nvalid) v = ld16(src + (int64_t)r * ld + cc * E);
+            st16(nat + r * TN::STRIDE + cc * 16, v);
+        }
+    } else {
+        constexpr int NB = (64 / E) * (HS / E);
+        for (int blk = tid; blk < NB; blk += A_THREADS) {
+            const int cb = blk % (HS / E), rb = blk / (HS / E);
+            uint4 in[8], out[8];
+#pragma unroll
+            for (int q = 0; q < E; ++q) {
+                const int r = rb * E + q;
+                in[q] = r < nvalid ? ld16(src + (int64_t)r * ld + cb * E) : make_uint4(0, 0, 0, 0);
+                if (nat) st16(nat + r * TN::STRIDE + cb * 16, in[q]);
+            }
+            transpose_block(in, out, (T*)nullptr);
+#pragma unroll
+            for (int j = 0; j < E; ++j) st16(trn + (cb * E + j) * TT::STRIDE + rb * 16, out[j]);
+        }
+    }
+}
+
+// ================================================================== forward
+template <typename T, int HS>
+__global__ void __launch_bounds__(A_THREADS) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ y,
+                                                             float* __restrict__ lse, int T_, int H, float sc) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using TK = Tile<T, HS>;
+    using TV = Tile<T, 64>;
+    char* sK = smem;
+    char* sVt = smem + TK::BYTES;
+    constexpr int KS = HS / 32, DB = HS / 16;
+
+    const int nqb = (T_ + 127) / 128;
+    const int qblk = nqb - 1 - blockIdx.x;  // longest blocks first
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * T_ * ld;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+    const int col = lane & 15, g = lane >> 4;
+
+    typename FragT<T>::type qf[2][KS];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qb][ks] = q < T_ ? frag_global<T>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<T>();
+    }
+    floatx4 o[DB][2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+    int kend = q0 + 128 < T_ ? q0 + 128 : T_;
+    const int nchunk = (kend + 63) / 64;
+    const bool wave_live = qw0 < T_;
+    for (int c = 0; c < nchunk; ++c) {
+        const int k0 = c * 64;
+        const int nvalid = T_ - k0 < 64 ? T_ - k0 : 64;
+        __syncthreads();
+        stage_rows<T, HS>(base + (int64_t)k0 * ld + C + h * HS, ld, nvalid, sK, nullptr, tid);
+        stage_rows<T, HS>(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nvalid, nullptr, sVt, tid);
+        __syncthreads();
+        if (!wave_live || k0 > qw0 + 31) continue;
+        floatx4 s[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = s[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const auto kf = frag_nat<T>(sK, TK::STRIDE, kb * 16 + col, ks, lane);
+                mma8(s[kb][0], kf, qf[0][ks]);
+                mma8(s[kb][1], kf, qf[1][ks]);
+            }
+        }
+        const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int q = qw0 + qb * 16 + col;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = s[kb][qb][i] * sc;
+                    if (need_mask) {
+                        const int key = k0 + kb * 16 + g * 4 + i;
+                        if (key > q || key >= T_) v = -INFINITY;
+                    }
+                    s[kb][qb][i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = group4_max(mx);
+            const float mnew = fmaxf(mrun[qb], mx);
+            const float alpha = mrun[qb] == -INFINITY ? 0.f : exp2f(mrun[qb] - mnew);
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = s[kb][qb][i] == -INFINITY ? 0.f : exp2f(s[kb][qb][i] - mnew);
+                    s[kb][qb][i] = p;
+                    ls += p;
+                }
+            lrun[qb] = lrun[qb] * alpha + ls;
+            mrun[qb] = mnew;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) o[d][qb] *= alpha;
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const auto p0 = frag_from_acc<T>(s[2 * st][0], s[2 * st + 1][0]);
+            const auto p1 = frag_from_acc<T>(s[2 * st][1], s[2 * st + 1][1]);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+                const auto vf = frag_perm<T>(sVt, TV::STRIDE, d * 16 + col, st, lane);
+                mma8(o[d][0], vf, p0);
+                mma8(o[d][1], vf, p1);
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        const float ltot = group4_sum(lrun[qb]);
+        if (q >= T_) continue;
+        const float inv = 1.0f / ltot;
+        T* yr = y + ((int64_t)b * T_ + q) * C + h * HS;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) store4v<T>(yr + d * 16 + g * 4, o[d][qb], inv);
+        if (g == 0) lse[(int64_t)bh * T_ + q] = (mrun[qb] + log2f(ltot)) * kLn2;
+    }
+}
+
+// ================================================================== backward
+// D[b,h,t] = sum_d dy * y (row sums of dO o O, the softmax-gradient correction term)
+template <typename T, int HS>
+__global__ void attn_bwd_pre_kernel(const T* __restrict__ y, const T* __restrict__ dy, float* __restrict__ D,
+                                    int BT, int T_, int H) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over BT*H
+    if (i >= (int64_t)BT * H) return;
+    const int row = (int)(i / H), h = (int)(i % H);
+    const int C = H * HS;
+    const T* a = y + (int64_t)row * C + h * HS;
+    const T* b = dy + (int64_t)row * C + h * HS;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < HS; ++d) s += to_f<T>(a[d]) * to_f<T>(b[d]);
+    const int bb = row / T_, t = row % T_;
+    D[((int64_t)bb * H + h) * T_ + t] = s;
+}
+
+// dK, dV for 128 keys per workgroup (32 per wave), looping over 64-query chunks.
+template <typename T, int HS>
+__global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dy,
+                                                                 const float* __restrict__ lse,
+                                                                 const float* __restrict__ D, T* __restrict__ dqkv,
+                                                                 int T_, int H, float sc, float scale) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using TN = Tile<T, HS>;
+    using TT = Tile<T, 64>;
+    char* sQ = smem;
+    char* sQt = sQ + TN::BYTES;
+    char* sO = sQt + TT::BYTES;     // dO natural
+    char* sOt = sO + TN::BYTES;     // dO transposed
+    float* sL = (float*)(sOt + TT::BYTES);
+    float* sD = sL + 64;
+    constexpr int KS = HS / 32, DB = HS / 16;
+
+    const int nkb = (T_ + 127) / 128;
+    const int kblk = blockIdx.x;  // early key blocks see the most queries: launch them first
+    (void)nkb;
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * T_ * ld;
+    const T* dyb = dy + (int64_t)b * T_ * C;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int k0 = kblk * 128, kw0 = k0 + wave * 32;
+
+    typename FragT<T>::type kf[2][KS], vf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + kb * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int64_t off = (int64_t)key * ld + h * HS + ks * 32 + g * 8;
+            kf[kb][ks] = key < T_ ? frag_global<T>(base + off + C) : frag_zero<T>();
+            vf[kb][ks] = key < T_ ? frag_global<T>(base + off + 2 * C) : frag_zero<T>();
+        }
+    }
+    floatx4 dk[DB][2], dv[DB][2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dk[d][kb] = dv[d][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int nqc = (T_ + 63) / 64;
+    const bool wave_live = kw0 < T_;
+    for (int qc = k0 / 64; qc < nqc; ++qc) {
+        const int q0 = qc * 64;
+        const int nvalid = T_ - q0 < 64 ? T_ - q0 : 64;
+        __syncthreads();
+        stage_rows<T, HS>(base + (int64_t)q0 * ld + h * HS, ld, nvalid, sQ, sQt, tid);
+        stage_rows<T, HS>(dyb + (int64_t)q0 * C + h * HS, C, nvalid, sO, sOt, tid);
+        if (tid < 64) {
+            const bool ok = tid < nvalid;
+            sL[tid] = ok ? lse[(int64_t)bh * T_ + q0 + tid] * kLog2e : 0.f;
+            sD[tid] = ok ? D[(int64_t)bh * T_ + q0 + tid] : 0.f;
+        }
+        __syncthreads();
+        if (!wave_live || q0 + 63 < kw0) continue;
+        floatx4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[qb][kb] = dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const auto qa = frag_nat<T>(sQ, TN::STRIDE, qb * 16 + col, ks, lane);
+                const auto oa = frag_nat<T>(sO, TN::STRIDE, qb * 16 + col, ks, lane);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma8(s[qb][kb], qa, kf[kb][ks]);
+                    mma8(dp[qb][kb], oa, vf[kb][ks]);
+                }
+            }
+        }
+        // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ql = qb * 16 + g * 4 + i;
+                const int q = q0 + ql;
+                const float L = sL[ql], Dq = sD[ql];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int key = kw0 + kb * 16 + col;
+                    const float p = (key <= q && q < T_) ? exp2f(s[qb][kb][i] * sc - L) : 0.f;
+                    s[qb][kb][i] = p;
+                    dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
+                }
+            }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            typename FragT<T>::type pf[2], df[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                pf[kb] = frag_from_acc<T>(s[2 * st][kb], s[2 * st + 1][kb]);
+                df[kb] = frag_from_acc<T>(dp[2 * st][kb], dp[2 * st + 1][kb]);
+            }
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+                const auto oat = frag_perm<T>(sOt, TT::STRIDE, d * 16 + col, st, lane);
+                const auto qat = frag_perm<T>(sQt, TT::STRIDE, d * 16 + col, st, lane);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma8(dv[d][kb], oat, pf[kb]);
+                    mma8(dk[d][kb], qat, df[kb]);
+                }
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + kb * 16 + col;
+        if (key >= T_) continue;
+        T* r = dqkv + ((int64_t)b * T_ + key) * ld + h * HS;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+            store4v<T>(r + C + d * 16 + g * 4, dk[d][kb], scale);
+            store4v<T>(r + 2 * C + d * 16 + g * 4, dv[d][kb], 1.0f);
+        }
+    }
+}
+
+// dQ for 128 queries per workgroup (32 per wave), looping over 64-key chunks.
+template <typename T, int HS>
+__global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dy,
+                                                                const float* __restrict__ lse,
+                                                                const float* __restrict__ D, T* __restrict__ dqkv,
+                                                                int T_, int H, float sc, float scale) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    using TN = Tile<T, HS>;
+    using TT = Tile<T, 64>;
+    char* sK = smem;
+    char* sKt = sK + TN::BYTES;
+    char* sV = sKt + TT::BYTES;
+    constexpr int KS = HS / 32, DB = HS / 16;
+
+    const int nqb = (T_ + 127) / 128;
+    const int qblk = nqb - 1 - blockIdx.x;
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const T* base = qkv + (int64_t)b * T_ * ld;
+    const T* dyb = dy + (int64_t)b * T_ * C;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+
+    typename FragT<T>::type qf[2][KS], of[2][KS];
+    float L[2], Dq[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        const bool ok = q < T_;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qf[qb][ks] = ok ? frag_global<T>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<T>();
+            of[qb][ks] = ok ? frag_global<T>(dyb + (int64_t)q * C + h * HS + ks * 32 + g * 8) : frag_zero<T>();
+        }
+        L[qb] = ok ? lse[(int64_t)bh * T_ + q] * kLog2e : 0.f;
+        Dq[qb] = ok ? D[(int64_t)bh * T_ + q] : 0.f;
+    }
+    floatx4 dq[DB][2];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) dq[d][0] = dq[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    int kend = q0 + 128 < T_ ? q0 + 128 : T_;
+    const int nchunk = (kend + 63) / 64;
+    const bool wave_live = qw0 < T_;
+    for (int c = 0; c < nchunk; ++c) {
+        const int k0 = c * 64;
+        const int nvalid = T_ - k0 < 64 ? T_ - k0 : 64;
+        __syncthreads();
+        stage_rows<T, HS>(base + (int64_t)k0 * ld + C + h * HS, ld, nvalid, sK, sKt, tid);
+        stage_rows<T, HS>(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nvalid, sV, nullptr, tid);
+        __syncthreads();
+        if (!wave_live || k0 > qw0 + 31) continue;
+        floatx4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const auto ka = frag_nat<T>(sK, TN::STRIDE, kb * 16 + col, ks, lane);
+                const auto va = frag_nat<T>(sV, TN::STRIDE, kb * 16 + col, ks, lane);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    mma8(s[kb][qb], ka, qf[qb][ks]);
+                    mma8(dp[kb][qb], va, of[qb][ks]);
+                }
+            }
+        }
+        // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q = qw0 + qb * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = k0 + kb * 16 + g * 4 + i;
+                    const float p = (key <= q && key < T_) ? exp2f(s[kb][qb][i] * sc - L[qb]) : 0.f;
+                    dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
+                }
+            }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const auto d0 = frag_from_acc<T>(dp[2 * st][0], dp[2 * st + 1][0]);
+            const auto d1 = frag_from_acc<T>(dp[2 * st][1], dp[2 * st + 1][1]);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+                const auto kat = frag_perm<T>(sKt, TT::STRIDE, d * 16 + col, st, lane);
+                mma8(dq[d][0], kat, d0);
+                mma8(dq[d][1], kat, d1);
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        if (q >= T_) continue;
+        T* r = dqkv + ((int64_t)b * T_ + q) * ld + h * HS;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) store4v<T>(r + d * 16 + g * 4, dq[d][qb], scale);
+    }
+}
+
+template <typename T, int HS> constexpr size_t fwd_lds() { return Tile<T, HS>::BYTES + Tile<T, 64>::BYTES; }
+template <typename T, int HS> constexpr size_t dkv_lds() { return 2 * (Tile<T, HS>::BYTES + Tile<T, 64>::BYTES) + 128 * sizeof(float); }
+template <typename T, int HS> constexpr size_t dq_lds() { return 2 * Tile<T, HS>::BYTES + Tile<T, 64>::BYTES; }
+
+template <typename T, int HS>
+static hipError_t fwd_launch(const void* qkv, void* y, float* lse, int B, int T_, int H, hipStream_t s) {
+    const float sc = kLog2e / sqrtf((float)HS);
+    dim3 grid((T_ + 127) / 128, B * H);
+    attn_fwd_kernel<T, HS><<<grid, dim3(A_THREADS), fwd_lds<T, HS>(), s>>>((const T*)qkv, (T*)y, lse, T_, H, sc);
+    return hipGetLastError();
+}
+
+template <typename T, int HS>
+static hipError_t bwd_launch(const void* qkv, const void* y, const void* dy, const float* lse, float* D, void* dqkv,
+                             int B, int T_, int H, hipStream_t s) {
+    const float sc = kLog2e / sqrtf((float)HS);
+    const float scale = 1.0f / sqrtf((float)HS);
+    const int64_t n = (int64_t)B * T_ * H;
+    attn_bwd_pre_kernel<T, HS><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>((const T*)y, (const T*)dy, D,
+                                                                                      B * T_, T_, H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 grid((T_ + 127) / 128, B * H);
+    attn_bwd_dkv_kernel<T, HS><<<grid, dim3(A_THREADS), dkv_lds<T, HS>(), s>>>((const T*)qkv, (const T*)dy, lse,
+                                                                              (const float*)D, (T*)dqkv, T_, H, sc, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_bwd_dq_kernel<T, HS><<<grid, dim3(A_THREADS), dq_lds<T, HS>(), s>>>((const T*)qkv, (const T*)dy, lse,
+                                                                            (const float*)D, (T*)dqkv, T_, H, sc, scale);
+    return hipGetLastError();
+}
+
+hipError_t attention_forward(const void* qkv, void* y, float* lse, int B, int T_, int H, int hs, int is_bf16,
+                             hipStream_t s) {
+    if (hs == 64) return is_bf16 ? fwd_launch<bf16, 64>(qkv, y, lse, B, T_, H, s) : fwd_launch<float, 64>(qkv, y, lse, B, T_, H, s);
+    if (hs == 32) return is_bf16 ? fwd_launch<bf16, 32>(qkv, y, lse, B, T_, H, s) : fwd_launch<float, 32>(qkv, y, lse, B, T_, H, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t attention_backward(const void* qkv, const void* y, const void* dy, const float* lse, float* D, void* dqkv,
+                              int B, int T_, int H, int hs, int is_bf16, hipStream_t s) {
+    if (hs == 64)
+        return is_bf16 ? bwd_launch<bf16, 64>(qkv, y, dy, lse, D, dqkv, B, T_, H, s)
+                       : bwd_launch<float, 64>(qkv, y, dy, lse, D, dqkv, B, T_, H, s);
+    if (hs == 32)
+        return is_bf16 ? bwd_launch<bf16, 32>(qkv, y, dy, lse, D, dqkv, B, T_, H, s)
+                       : bwd_launch<float, 32>(qkv, y, dy, lse, D, dqkv, B, T_, H, s);
+    return hipErrorInvalidValue;
+}
+
+void attention_setup() {
+#define ASET(T, HS)                                                                                                  \
+    (void)hipFuncSetAttribute((const void*)attn_fwd_kernel<T, HS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fwd_lds<T, HS>()); \
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dkv_kernel<T, HS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dkv_lds<T, HS>()); \
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<T, HS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds<T, HS>());
+    ASET(bf16, 64) ASET(bf16, 32) ASET(float, 64) ASET(float, 32)
+#undef ASET
+}
+
+}  // namespace gpt2k

@@ -1,0 +1,147 @@
+// Device-side building blocks shared by the kernels of the GPT-2 step (gfx950 / CDNA4).
+//
+// Storage types: `float` (fp32 check mode) and `bf16` (= __bf16, the bf16 mode). Every
+// conversion float -> bf16 rounds to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+//
+// Matrix products use 16x16 MFMA tiles on wave64. Operand fragments are "8 consecutive
+// k values per lane": lane l covers row/column (l & 15) and the k sub-range owned by lane
+// group g = l >> 4. For bf16 one v_mfma_f32_16x16x32_bf16 consumes the 8 values; for fp32
+// eight v_mfma_f32_16x16x4f32 consume them one at a time. Because the sum over k is
+// order-free, it only matters that the A and B fragments of a product assign k the same way.
+// The 16x16 fp32 accumulator holds, in lane l, rows 4*(l>>4)+i (i = 0..3) of column (l & 15).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+
+#define DEV __device__ __forceinline__
+
+// ------------------------------------------------------------------ conversions
+template <typename T> DEV float to_f(T x);
+template <> DEV float to_f<float>(float x) { return x; }
+template <> DEV float to_f<bf16>(bf16 x) { return (float)x; }
+
+template <typename T> DEV T from_f(float x);
+template <> DEV float from_f<float>(float x) { return x; }
+template <> DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// 8-value fragment type of a storage type
+template <typename T> struct FragT;
+template <> struct FragT<bf16> { typedef bf16x8 type; };
+template <> struct FragT<float> { typedef floatx8 type; };
+
+DEV void mma8(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+DEV void mma8(floatx4& acc, const floatx8& a, const floatx8& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+}
+
+// Build a fragment from two 4-element halves (used where a lane's 8 k values are two
+// separate runs of 4).
+DEV bf16x8 frag_from_halves(const uint2& lo, const uint2& hi) {
+    uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    return __builtin_bit_cast(bf16x8, u);
+}
+DEV floatx8 frag_from_halves(const float4& lo, const float4& hi) {
+    floatx8 r;
+    r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+    r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+    return r;
+}
+
+// 16-byte vector of a storage type
+template <typename T> struct Vec16 { typedef uint4 type; static constexpr int N = 16 / sizeof(T); };
+
+// ------------------------------------------------------------------ reductions
+DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+// reduce over the 4 lane groups (lanes l, l^16, l^32, l^48) that share a 16x16 column
+DEV float group4_sum(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+DEV float group4_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Block-wide sum for a block of NT threads (NT multiple of 64); every thread gets the result.
+template <int NT>
+DEV float block_sum(float v, float* red /* >= NT/64 floats of shared memory */) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) s += red[i];
+    return s;
+}
+
+// ------------------------------------------------------------------ 16-byte transposes
+// Transpose an E x E block of storage elements held as E rows of 16 bytes (E = 8 for bf16,
+// 4 for fp32): out[j] holds column j (element r of out[j] = element j of in[r]).
+DEV void transpose_block(const uint4 (&in)[8], uint4 (&out)[8], bf16*) {
+    // element (r, j) of the input lives in word j/2 of in[r], half j&1
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t a = ((const uint32_t*)&in[2 * p])[w];
+            const uint32_t b = ((const uint32_t*)&in[2 * p + 1])[w];
+            o[p] = __builtin_amdgcn_perm(b, a, sel);
+        }
+        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+DEV void transpose_block(const uint4 (&in)[8], uint4 (&out)[8], float*) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = ((const uint32_t*)&in[r])[j];
+        out[j] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+DEV uint4 ld16(const void* p) { return *(const uint4*)p; }
+DEV void st16(void* p, const uint4& v) { *(uint4*)p = v; }
+
+// ------------------------------------------------------------------ GELU (tanh form)
+// 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) and its derivative.
+constexpr float kGeluC = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float kGeluA = 0.044715f;
+DEV float tanh_fast(float w) {
+    // tanh(w) = 1 - 2/(exp(2w)+1), exact enough in fp32 and saturating for large |w|
+    const float e = __expf(2.0f * w);
+    return 1.0f - 2.0f / (e + 1.0f);
+}
+DEV float gelu_f(float u) {
+    const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
+    return 0.5f * u * (1.0f + t);
+}
+DEV float gelu_grad_f(float u) {
+    const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
+    return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluC * (1.0f + 3.0f * kGeluA * u * u);
+}

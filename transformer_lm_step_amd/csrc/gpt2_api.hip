@@ -1,0 +1,762 @@
+// C ABI of the GPT-2 training-step library: configuration, canonical parameter layout,
+// workspace carving, and the launch sequences of forward, backward and the optimizer.
+// Everything here is host code; every operation of the step runs in the kernels of
+// gemm.hip, attention.hip and rows.hip on the handle's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "kernels.h"
+
+using namespace gpt2k;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+// strict: also the shape requirements of the kernels (needed to size or create a handle);
+// otherwise only what the parameter layout needs (counting functions)
+bool config_ok(const gpt2_config* c, std::string* why, bool strict = true) {
+    auto bad = [&](const char* m) { if (why) *why = m; return false; };
+    if (!c) return bad("config is null");
+    if (c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1 || c->mlp_hidden < 1 || c->block_size < 1 ||
+        c->vocab_size < 1 || c->max_batch < 1)
+        return bad("config fields must be positive");
+    if (c->n_embd % c->n_head) return bad("n_embd must be a multiple of n_head");
+    if (c->padded_vocab_size < c->vocab_size) return bad("padded_vocab_size must be >= vocab_size");
+    if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return bad("dtype must be GPT2_FP32 or GPT2_BF16");
+    if (!strict) return true;
+    const int hs = c->n_embd / c->n_head;
+    if (hs != 64 && hs != 32) return bad("head size n_embd/n_head must be 32 or 64");
+    if (c->n_embd % 8 || c->mlp_hidden % 8) return bad("n_embd and mlp_hidden must be multiples of 8");
+    if (c->n_embd > 2048) return bad("n_embd above 2048 is not supported by the LayerNorm kernels");
+    if (c->padded_vocab_size % 8) return bad("padded_vocab_size must be a multiple of 8");
+    if (c->padded_vocab_size >= (1 << 18)) return bad("padded_vocab_size must be below 262144");
+    if ((int64_t)c->max_batch * c->block_size > (1 << 30)) return bad("max_batch*block_size too large");
+    return true;
+}
+
+struct Layout {
+    // parameter arena
+    int64_t n_params = 0, decay_end = 0;
+    int64_t wte = 0, wpe = 0, lnf_w = 0, lnf_b = 0;
+    std::vector<int64_t> w_qkv, w_o, w_fc, w_pr, ln1_w, ln1_b, b_qkv, b_o, ln2_w, ln2_b, b_fc, b_pr;
+};
+
+Layout make_layout(const gpt2_config* c) {
+    Layout L;
+    const int64_t C = c->n_embd, F = c->mlp_hidden, Vp = c->padded_vocab_size;
+    int64_t o = 0;
+    L.wte = o; o += Vp * C;
+    L.wpe = o; o += (int64_t)c->block_size * C;
+    for (int l = 0; l < c->n_layer; ++l) {
+        L.w_qkv.push_back(o); o += 3 * C * C;
+        L.w_o.push_back(o); o += C * C;
+        L.w_fc.push_back(o); o += F * C;
+        L.w_pr.push_back(o); o += C * F;
+    }
+    L.decay_end = o;
+    for (int l = 0; l < c->n_layer; ++l) {
+        L.ln1_w.push_back(o); o += C;
+        L.ln1_b.push_back(o); o += C;
+        L.b_qkv.push_back(o); o += 3 * C;
+        L.b_o.push_back(o); o += C;
+        L.ln2_w.push_back(o); o += C;
+        L.ln2_b.push_back(o); o += C;
+        L.b_fc.push_back(o); o += F;
+        L.b_pr.push_back(o); o += C;
+    }
+    L.lnf_w = o; o += C;
+    L.lnf_b = o; o += C;
+    L.n_params = o;
+    return L;
+}
+
+// name/offset/shape of tensor i of the canonical arena
+bool tensor_info(const gpt2_config* c, int i, std::string* name, int64_t* off, int64_t* r, int64_t* cc) {
+    const Layout L = make_layout(c);
+    const int64_t C = c->n_embd, F = c->mlp_hidden;
+    const int nl = c->n_layer;
+    char buf[96];
+    if (i < 0) return false;
+    if (i == 0) { *name = "wte"; *off = L.wte; *r = c->padded_vocab_size; *cc = C; return true; }
+    if (i == 1) { *name = "wpe"; *off = L.wpe; *r = c->block_size; *cc = C; return true; }
+    i -= 2;
+    if (i < 4 * nl) {
+        const int l = i / 4, j = i % 4;
+        static const char* nm[4] = {"attn.c_attn.weight", "attn.c_proj.weight", "mlp.c_fc.weight", "mlp.c_proj.weight"};
+        snprintf(buf, sizeof(buf), "h.%d.%s", l, nm[j]);
+        *name = buf;
+        const int64_t offs[4] = {L.w_qkv[l], L.w_o[l], L.w_fc[l], L.w_pr[l]};
+        const int64_t rows[4] = {3 * C, C, F, C}, cols[4] = {C, C, C, F};
+        *off = offs[j]; *r = rows[j]; *cc = cols[j];
+        return true;
+    }
+    i -= 4 * nl;
+    if (i < 8 * nl) {
+        const int l = i / 8, j = i % 8;
+        static const char* nm[8] = {"ln_1.weight", "ln_1.bias", "attn.c_attn.bias", "attn.c_proj.bias",
+                                    "ln_2.weight", "ln_2.bias", "mlp.c_fc.bias", "mlp.c_proj.bias"};
+        snprintf(buf, sizeof(buf), "h.%d.%s", l, nm[j]);
+        *name = buf;
+        const int64_t offs[8] = {L.ln1_w[l], L.ln1_b[l], L.b_qkv[l], L.b_o[l], L.ln2_w[l], L.ln2_b[l], L.b_fc[l], L.b_pr[l]};
+        const int64_t len[8] = {C, C, 3 * C, C, C, C, F, C};
+        *off = offs[j]; *r = len[j]; *cc = 0;
+        return true;
+    }
+    i -= 8 * nl;
+    if (i == 0) { *name = "ln_f.weight"; *off = L.lnf_w; *r = C; *cc = 0; return true; }
+    if (i == 1) { *name = "ln_f.bias"; *off = L.lnf_b; *r = C; *cc = 0; return true; }
+    return false;
+}
+
+// split-K factor of a weight-gradient product: enough workgroups for 256 CUs, at least
+// 4 K-tiles per split, at most 16 splits
+int choose_split(int M, int N, int K, bool bf16) {
+    const int BK = bf16 ? 64 : 32;
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int ktiles = (K + BK - 1) / BK;
+    int s = (1024 + tiles - 1) / tiles;
+    if (s > 16) s = 16;
+    if (s > ktiles / 4) s = ktiles / 4;
+    if (s < 1) s = 1;
+    return s;
+}
+
+struct Plan {
+    size_t total = 0;
+    // offsets in bytes
+    size_t params, grads, m, v, shadow, idx, tgt;
+    std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
+    size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dres_t, dln, datt, dqkv, du, Dbuf;
+    size_t splitk, lnpart, cspart, normpart, normcoef, ebscratch;
+};
+
+Plan make_plan(const gpt2_config* c) {
+    Plan P;
+    const Layout L = make_layout(c);
+    const bool bf = c->dtype == GPT2_BF16;
+    const size_t es = bf ? 2 : 4;
+    const int64_t BT = (int64_t)c->max_batch * c->block_size;
+    const int64_t C = c->n_embd, F = c->mlp_hidden, Vp = c->padded_vocab_size, H = c->n_head;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o += (bytes + 255) & ~(size_t)255; return r; };
+    P.params = take(L.n_params * 4);
+    P.grads = take(L.n_params * 4);
+    P.m = take(L.n_params * 4);
+    P.v = take(L.n_params * 4);
+    P.shadow = bf ? take(L.decay_end * 2) : 0;
+    P.idx = take(BT * 4);
+    P.tgt = take(BT * 4);
+    for (int l = 0; l <= c->n_layer; ++l) P.x_in.push_back(take(BT * C * 4));
+    for (int l = 0; l < c->n_layer; ++l) {
+        P.x_mid.push_back(take(BT * C * 4));
+        P.h1.push_back(take(BT * C * es));
+        P.mean1.push_back(take(BT * 4));
+        P.rstd1.push_back(take(BT * 4));
+        P.qkv.push_back(take(BT * 3 * C * es));
+        P.att.push_back(take(BT * C * es));
+        P.lse.push_back(take(BT * H * 4));
+        P.h2.push_back(take(BT * C * es));
+        P.mean2.push_back(take(BT * 4));
+        P.rstd2.push_back(take(BT * 4));
+        P.u.push_back(take(BT * F * es));
+        P.a.push_back(take(BT * F * es));
+    }
+    P.hf = take(BT * C * es);
+    P.meanf = take(BT * 4);
+    P.rstdf = take(BT * 4);
+    P.logits = take(BT * Vp * es);
+    P.loss_rows = take(BT * 4);
+    P.loss = take(256);
+    P.dres = take(BT * C * 4);
+    P.dres_t = take(BT * C * es);
+    P.dln = take(BT * C * 4);
+    P.datt = take(BT * C * es);
+    P.dqkv = take(BT * 3 * C * es);
+    P.du = take(BT * F * es);
+    P.Dbuf = take(BT * H * 4);
+    size_t sk = 0;
+    const int shapes[4][2] = {{(int)(3 * C), (int)C}, {(int)C, (int)C}, {(int)F, (int)C}, {(int)C, (int)F}};
+    for (auto& s : shapes) {
+        const int ns = choose_split(s[0], s[1], (int)BT, bf);
+        if (ns > 1) sk = std::max(sk, (size_t)ns * s[0] * s[1] * 4);
+    }
+    P.splitk = take(sk ? sk : 256);
+    P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 2 * C * 4);
+    P.cspart = take((size_t)colsum_partial_floats((int)BT, (int)std::max(3 * C, F)) * 4);
+    P.normpart = take((size_t)norm_blocks() * 4);
+    P.normcoef = take(256);
+    P.ebscratch = take(embed_backward_scratch_bytes((int)BT, (int)C));
+    P.total = o;
+    return P;
+}
+
+const char* kClasses[] = {"embed_fwd", "layernorm_fwd", "gemm_qkv", "attn_fwd", "gemm_attn_proj", "gemm_fc",
+                          "gemm_mlp_proj", "gemm_lm_head", "cross_entropy", "loss_mean", "gemm_lm_head_dx",
+                          "gemm_lm_head_dw", "layernorm_bwd", "ln_param_grad", "gemm_dw", "bias_grad", "gemm_dx",
+                          "attn_bwd", "embed_bwd", "grad_norm", "adamw", nullptr};
+
+}  // namespace
+
+struct gpt2 {
+    gpt2_config cfg;
+    Layout L;
+    Plan P;
+    char* ws = nullptr;
+    hipStream_t stream = nullptr;
+    int dev = 0;
+    bool bf16 = false;
+    // state of the last forward
+    bool have_fwd = false;
+    int B = 0, T = 0;
+    // timing
+    bool timing = false;
+    std::string filter;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+    std::vector<int> ev_cls;
+    size_t ev_used = 0;
+    std::map<std::string, std::pair<double, int64_t>> times;
+
+    template <typename X> X* at(size_t off) const { return (X*)(ws + off); }
+    float* params() const { return at<float>(P.params); }
+    float* grads() const { return at<float>(P.grads); }
+    // weight operand of a product: the bf16 copy in bf16 mode, the fp32 master otherwise
+    const void* wop(int64_t off) const {
+        return bf16 ? (const void*)(at<uint16_t>(P.shadow) + off) : (const void*)(params() + off);
+    }
+};
+
+namespace {
+
+int class_index(const char* name) {
+    for (int i = 0; kClasses[i]; ++i)
+        if (!strcmp(kClasses[i], name)) return i;
+    return -1;
+}
+
+// run one launcher under the timing hook
+template <class Fn>
+int run(gpt2_t* h, const char* cls, Fn&& fn) {
+    const bool rec = h->timing && (h->filter.empty() || h->filter == cls);
+    size_t slot = 0;
+    if (rec) {
+        if (h->ev_used == h->ev.size()) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+                return set_error(GPT2_EHIP, "hipEventCreate failed");
+            h->ev.push_back({a, b});
+            h->ev_cls.push_back(0);
+        }
+        slot = h->ev_used++;
+        (void)hipEventRecord(h->ev[slot].first, h->stream);
+    }
+    const hipError_t e = fn();
+    if (rec) {
+        (void)hipEventRecord(h->ev[slot].second, h->stream);
+        h->ev_cls[slot] = class_index(cls);
+    }
+    if (e != hipSuccess) return set_error(GPT2_EHIP, "%s: %s", cls, hipGetErrorString(e));
+    return GPT2_OK;
+}
+
+#define TRY(x)                     \
+    do {                           \
+        const int _r = (x);        \
+        if (_r != GPT2_OK) return _r; \
+    } while (0)
+
+#define HIPTRY(x, what)                                                                   \
+    do {                                                                                  \
+        const hipError_t _e = (x);                                                        \
+        if (_e != hipSuccess) return set_error(GPT2_EHIP, "%s: %s", what, hipGetErrorString(_e)); \
+    } while (0)
+
+bool g_setup_done = false;
+
+}  // namespace
+
+// =================================================================== sizing
+extern "C" size_t gpt2_workspace_bytes(const gpt2_config* cfg) {
+    std::string why;
+    if (!config_ok(cfg, &why)) { set_error(GPT2_EINVAL, "%s", why.c_str()); return 0; }
+    return make_plan(cfg).total;
+}
+
+extern "C" int64_t gpt2_num_params(const gpt2_config* cfg) {
+    std::string why;
+    if (!config_ok(cfg, &why, false)) { set_error(GPT2_EINVAL, "%s", why.c_str()); return -1; }
+    return make_layout(cfg).n_params;
+}
+
+extern "C" int64_t gpt2_decay_end(const gpt2_config* cfg) {
+    std::string why;
+    if (!config_ok(cfg, &why, false)) { set_error(GPT2_EINVAL, "%s", why.c_str()); return -1; }
+    return make_layout(cfg).decay_end;
+}
+
+extern "C" int32_t gpt2_num_tensors(const gpt2_config* cfg) {
+    if (!config_ok(cfg, nullptr, false)) return -1;
+    return 12 * cfg->n_layer + 4;
+}
+
+extern "C" int32_t gpt2_num_decay_tensors(const gpt2_config* cfg) {
+    if (!config_ok(cfg, nullptr, false)) return -1;
+    return 4 * cfg->n_layer + 2;
+}
+
+extern "C" int gpt2_param_info(const gpt2_config* cfg, int32_t i, const char** name, int64_t* offset, int64_t shape[2]) {
+    std::string why;
+    if (!config_ok(cfg, &why, false)) return set_error(GPT2_EINVAL, "%s", why.c_str());
+    static thread_local std::map<std::string, std::string> names;  // stable storage for returned names
+    std::string nm;
+    int64_t off, r, c;
+    if (!tensor_info(cfg, i, &nm, &off, &r, &c)) return set_error(GPT2_EINVAL, "tensor index %d out of range", i);
+    auto it = names.emplace(nm, nm).first;
+    if (name) *name = it->second.c_str();
+    if (offset) *offset = off;
+    if (shape) { shape[0] = r; shape[1] = c; }
+    return GPT2_OK;
+}
+
+extern "C" double gpt2_cosine_lr(int64_t it, double max_lr, double min_lr, int64_t warmup_steps, int64_t max_steps) {
+    if (it < warmup_steps) return max_lr * (double)(it + 1) / (double)warmup_steps;
+    if (it > max_steps) return min_lr;
+    const double ratio = (double)(it - warmup_steps) / (double)(max_steps - warmup_steps);
+    const double coeff = 0.5 * (1.0 + std::cos(M_PI * ratio));
+    return min_lr + coeff * (max_lr - min_lr);
+}
+
+extern "C" const char* gpt2_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* gpt2_kernel_class(int32_t i) {
+    const int n = (int)(sizeof(kClasses) / sizeof(kClasses[0])) - 1;
+    return (i >= 0 && i < n) ? kClasses[i] : nullptr;
+}
+
+// =================================================================== lifetime
+extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, uint64_t seed, void* stream, gpt2_t** out) {
+    std::string why;
+    if (!out) return set_error(GPT2_EINVAL, "out is null");
+    *out = nullptr;
+    if (!config_ok(cfg, &why)) return set_error(GPT2_EINVAL, "%s", why.c_str());
+    if (!d_ws) return set_error(GPT2_EINVAL, "workspace is null");
+    if ((uintptr_t)d_ws & 255) return set_error(GPT2_EINVAL, "workspace must be 256-byte aligned");
+    gpt2_t* h = new gpt2_t();
+    h->cfg = *cfg;
+    h->L = make_layout(cfg);
+    h->P = make_plan(cfg);
+    if (ws_bytes < h->P.total) {
+        const size_t need = h->P.total;
+        delete h;
+        return set_error(GPT2_EINVAL, "workspace too small: %zu bytes given, %zu needed", ws_bytes, need);
+    }
+    h->ws = (char*)d_ws;
+    h->stream = (hipStream_t)stream;
+    h->bf16 = cfg->dtype == GPT2_BF16;
+    (void)hipGetDevice(&h->dev);
+    if (!g_setup_done) {
+        gemm_setup();
+        attention_setup();
+        rows_setup();
+        g_setup_done = true;
+    }
+    // parameters per the GPT-2 initialization, gradients and moments zero
+    const int n = gpt2_num_tensors(cfg);
+    const float resid_std = 0.02f / std::sqrt(2.0f * cfg->n_layer);
+    for (int i = 0; i < n; ++i) {
+        std::string nm;
+        int64_t off, r, c;
+        tensor_info(cfg, i, &nm, &off, &r, &c);
+        const int64_t cnt = c ? r * c : r;
+        float* p = h->params() + off;
+        hipError_t e;
+        if (c) {
+            const bool resid = nm.find("c_proj.weight") != std::string::npos;
+            e = init_normal(p, cnt, resid ? resid_std : 0.02f, seed, (uint64_t)off / 4, h->stream);
+        } else {
+            const bool gain = nm.find("ln_") != std::string::npos && nm.find(".weight") != std::string::npos;
+            e = fill(p, cnt, gain ? 1.0f : 0.0f, h->stream);
+        }
+        if (e != hipSuccess) { delete h; return set_error(GPT2_EHIP, "init: %s", hipGetErrorString(e)); }
+    }
+    const int64_t N = h->L.n_params;
+    hipError_t e = hipMemsetAsync(h->grads(), 0, N * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->at<float>(h->P.m), 0, N * 4, h->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(h->at<float>(h->P.v), 0, N * 4, h->stream);
+    if (e == hipSuccess && h->bf16) e = refresh_shadow(h->params(), h->at<char>(h->P.shadow), h->L.decay_end, h->stream);
+    if (e != hipSuccess) { delete h; return set_error(GPT2_EHIP, "init: %s", hipGetErrorString(e)); }
+    *out = h;
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_destroy(gpt2_t* h) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    for (auto& p : h->ev) { (void)hipEventDestroy(p.first); (void)hipEventDestroy(p.second); }
+    delete h;
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_set_stream(gpt2_t* h, void* stream) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    h->stream = (hipStream_t)stream;
+    return GPT2_OK;
+}
+
+// =================================================================== parameter I/O
+static int copy_arena(gpt2_t* h, void* dst, const void* src, size_t bytes, bool to_dev, int on_device) {
+    const hipMemcpyKind k = on_device ? hipMemcpyDeviceToDevice : (to_dev ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost);
+    HIPTRY(hipMemcpyAsync(dst, src, bytes, k, h->stream), "copy");
+    if (!on_device) HIPTRY(hipStreamSynchronize(h->stream), "synchronize");
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_set_params(gpt2_t* h, const float* src, int on_device) {
+    if (!h || !src) return set_error(GPT2_EINVAL, "null argument");
+    TRY(copy_arena(h, h->params(), src, h->L.n_params * 4, true, on_device));
+    if (h->bf16) HIPTRY(refresh_shadow(h->params(), h->at<char>(h->P.shadow), h->L.decay_end, h->stream), "shadow");
+    return GPT2_OK;
+}
+extern "C" int gpt2_get_params(gpt2_t* h, float* dst, int on_device) {
+    if (!h || !dst) return set_error(GPT2_EINVAL, "null argument");
+    return copy_arena(h, dst, h->params(), h->L.n_params * 4, false, on_device);
+}
+extern "C" int gpt2_get_grads(gpt2_t* h, float* dst, int on_device) {
+    if (!h || !dst) return set_error(GPT2_EINVAL, "null argument");
+    return copy_arena(h, dst, h->grads(), h->L.n_params * 4, false, on_device);
+}
+extern "C" int gpt2_set_grads(gpt2_t* h, const float* src, int on_device) {
+    if (!h || !src) return set_error(GPT2_EINVAL, "null argument");
+    return copy_arena(h, h->grads(), src, h->L.n_params * 4, true, on_device);
+}
+extern "C" int gpt2_get_moments(gpt2_t* h, float* m, float* v, int on_device) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    if (m) TRY(copy_arena(h, m, h->at<float>(h->P.m), h->L.n_params * 4, false, on_device));
+    if (v) TRY(copy_arena(h, v, h->at<float>(h->P.v), h->L.n_params * 4, false, on_device));
+    return GPT2_OK;
+}
+extern "C" int gpt2_set_moments(gpt2_t* h, const float* m, const float* v, int on_device) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    if (m) TRY(copy_arena(h, h->at<float>(h->P.m), m, h->L.n_params * 4, true, on_device));
+    if (v) TRY(copy_arena(h, h->at<float>(h->P.v), v, h->L.n_params * 4, true, on_device));
+    return GPT2_OK;
+}
+extern "C" float* gpt2_params_device(gpt2_t* h) { return h ? h->params() : nullptr; }
+extern "C" float* gpt2_grads_device(gpt2_t* h) { return h ? h->grads() : nullptr; }
+
+// =================================================================== forward
+extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T,
+                            float* d_logits, float* d_loss, float* h_loss) {
+    if (!h || !d_idx) return set_error(GPT2_EINVAL, "null argument");
+    const gpt2_config& c = h->cfg;
+    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
+    if (!d_targets && (d_loss || h_loss)) return set_error(GPT2_EINVAL, "a loss needs targets");
+    if (!d_targets && !d_logits) return set_error(GPT2_EINVAL, "without targets, d_logits is required");
+    h->have_fwd = false;
+    const int BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
+    const int bf = h->bf16;
+    const Layout& L = h->L;
+    const Plan& P = h->P;
+    float* prm = h->params();
+    hipStream_t s = h->stream;
+    int32_t* idx = h->at<int32_t>(P.idx);
+    int32_t* tgt = h->at<int32_t>(P.tgt);
+    HIPTRY(hipMemcpyAsync(idx, d_idx, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy idx");
+    if (d_targets) HIPTRY(hipMemcpyAsync(tgt, d_targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy targets");
+
+    TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<float>(P.x_in[0]), B, T, C, s); }));
+    for (int l = 0; l < c.n_layer; ++l) {
+        TRY(run(h, "layernorm_fwd", [&] {
+            return layernorm_forward(h->at<float>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
+                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), BT, C, bf, s);
+        }));
+        GemmDesc g;
+        g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
+        g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 0;
+        g.M = BT; g.N = 3 * C; g.K = C;
+        g.epi = EPI_BIAS_T; g.C = h->at<char>(P.qkv[l]); g.ldc = 3 * C; g.bias = prm + L.b_qkv[l];
+        TRY(run(h, "gemm_qkv", [&] { return gemm(g, bf, s); }));
+        TRY(run(h, "attn_fwd", [&] {
+            return attention_forward(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), h->at<float>(P.lse[l]), B, T, H, hs, bf, s);
+        }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.att[l]); g.lda = C;
+        g.B = h->wop(L.w_o[l]); g.ldb = C;
+        g.M = BT; g.N = C; g.K = C;
+        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.resid = h->at<float>(P.x_in[l]); g.ldr = C;
+        TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
+        TRY(run(h, "layernorm_fwd", [&] {
+            return layernorm_forward(h->at<float>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
+                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), BT, C, bf, s);
+        }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.h2[l]); g.lda = C;
+        g.B = h->wop(L.w_fc[l]); g.ldb = C;
+        g.M = BT; g.N = F; g.K = C;
+        g.epi = EPI_BIAS_GELU; g.C = h->at<char>(P.u[l]); g.C2 = h->at<char>(P.a[l]); g.ldc = F; g.bias = prm + L.b_fc[l];
+        TRY(run(h, "gemm_fc", [&] { return gemm(g, bf, s); }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.a[l]); g.lda = F;
+        g.B = h->wop(L.w_pr[l]); g.ldb = F;
+        g.M = BT; g.N = C; g.K = F;
+        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.resid = h->at<float>(P.x_mid[l]); g.ldr = C;
+        TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
+    }
+    TRY(run(h, "layernorm_fwd", [&] {
+        return layernorm_forward(h->at<float>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
+                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), BT, C, bf, s);
+    }));
+    {
+        GemmDesc g;
+        g.A = h->at<char>(P.hf); g.lda = C;
+        g.B = h->wop(L.wte); g.ldb = C;  // tied lm_head: logits = hf wte^T, no bias
+        g.M = BT; g.N = Vp; g.K = C;
+        g.epi = EPI_BIAS_T; g.C = h->at<char>(P.logits); g.ldc = Vp;
+        TRY(run(h, "gemm_lm_head", [&] { return gemm(g, bf, s); }));
+    }
+    if (d_targets) {
+        TRY(run(h, "cross_entropy", [&] {
+            return cross_entropy(h->at<char>(P.logits), tgt, h->at<float>(P.loss_rows), d_logits, BT, Vp, bf, s);
+        }));
+        float* dl = h->at<float>(P.loss);
+        TRY(run(h, "loss_mean", [&] { return mean_reduce(h->at<float>(P.loss_rows), BT, dl, s); }));
+        if (d_loss) HIPTRY(hipMemcpyAsync(d_loss, dl, 4, hipMemcpyDeviceToDevice, s), "copy loss");
+        if (h_loss) {
+            HIPTRY(hipMemcpyAsync(h_loss, dl, 4, hipMemcpyDeviceToHost, s), "copy loss");
+            HIPTRY(hipStreamSynchronize(s), "synchronize");
+        }
+        h->have_fwd = true;
+        h->B = B;
+        h->T = T;
+    } else {
+        HIPTRY(convert_to_f32(h->at<char>(P.logits), d_logits, (int64_t)BT * Vp, bf, s), "logits");
+    }
+    return GPT2_OK;
+}
+
+// =================================================================== backward
+extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    if (!h->have_fwd) return set_error(GPT2_ESTATE, "backward needs a preceding forward with targets");
+    const gpt2_config& c = h->cfg;
+    const int B = h->B, T = h->T, BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size;
+    const int H = c.n_head, hs = C / H;
+    const int bf = h->bf16;
+    const int acc = accumulate ? 1 : 0;
+    const Layout& L = h->L;
+    const Plan& P = h->P;
+    float* grd = h->grads();
+    float* prm = h->params();
+    hipStream_t s = h->stream;
+    float* dres = h->at<float>(P.dres);
+    char* dres_t = h->at<char>(P.dres_t);
+    float* dln = h->at<float>(P.dln);
+    float* lnpart = h->at<float>(P.lnpart);
+    float* cspart = h->at<float>(P.cspart);
+    void* skpart = h->at<char>(P.splitk);
+    const int lnblk = layernorm_backward_blocks(BT);
+
+    auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres) -> int {
+        TRY(run(h, "layernorm_bwd", [&] {
+            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres_t, accum_dres, lnpart, lnblk, BT, C, bf, s);
+        }));
+        // weight and bias gradients are adjacent in the arena
+        return run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, grd + w_off, acc, s); });
+    };
+    auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off) -> int {
+        GemmDesc g;
+        g.A = dy; g.lda = ldy; g.a_layout = 1;
+        g.B = x; g.ldb = ldx; g.b_layout = 1;
+        g.M = M; g.N = N; g.K = BT;
+        g.epi = EPI_F32; g.C = grd + off; g.ldc = N; g.alpha = 1.f; g.beta = acc;
+        g.nsplit = choose_split(M, N, BT, bf); g.partial = skpart;
+        return run(h, "gemm_dw", [&] { return gemm(g, bf, s); });
+    };
+    auto bias = [&](const void* dy, int dy_f32, int n, int64_t off) -> int {
+        return run(h, "bias_grad", [&] { return colsum(dy, dy_f32, bf, BT, n, cspart, grd + off, acc, s); });
+    };
+
+    // lm_head: dhf = s dz wte ; dwte (+)= s dz^T hf   (dz = (softmax - onehot)/BT from the forward)
+    {
+        GemmDesc g;
+        g.A = h->at<char>(P.logits); g.lda = Vp; g.a_layout = 0;
+        g.B = h->wop(L.wte); g.ldb = C; g.b_layout = 1;
+        g.M = BT; g.N = C; g.K = Vp;
+        g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = grad_scale; g.beta = 0;
+        TRY(run(h, "gemm_lm_head_dx", [&] { return gemm(g, bf, s); }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.logits); g.lda = Vp; g.a_layout = 1;
+        g.B = h->at<char>(P.hf); g.ldb = C; g.b_layout = 1;
+        g.M = Vp; g.N = C; g.K = BT;
+        g.epi = EPI_F32; g.C = grd + L.wte; g.ldc = C; g.alpha = grad_scale; g.beta = acc;
+        TRY(run(h, "gemm_lm_head_dw", [&] { return gemm(g, bf, s); }));
+    }
+    TRY(ln_bwd(h->at<float>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0));
+
+    for (int l = c.n_layer - 1; l >= 0; --l) {
+        // x_out = x_mid + a Wpr^T + bpr
+        TRY(dw(dres_t, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
+        TRY(bias(dres, 1, C, L.b_pr[l]));
+        {
+            GemmDesc g;
+            g.A = dres_t; g.lda = C; g.a_layout = 0;
+            g.B = h->wop(L.w_pr[l]); g.ldb = F; g.b_layout = 1;
+            g.M = BT; g.N = F; g.K = C;
+            g.epi = EPI_GELU_BWD; g.C = h->at<char>(P.du); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
+            TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
+        }
+        TRY(dw(h->at<char>(P.du), F, h->at<char>(P.h2[l]), C, F, C, L.w_fc[l]));
+        TRY(bias(h->at<char>(P.du), 0, F, L.b_fc[l]));
+        {
+            GemmDesc g;
+            g.A = h->at<char>(P.du); g.lda = F; g.a_layout = 0;
+            g.B = h->wop(L.w_fc[l]); g.ldb = C; g.b_layout = 1;
+            g.M = BT; g.N = C; g.K = F;
+            g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
+            TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
+        }
+        TRY(ln_bwd(h->at<float>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1));
+        // x_mid = x_in + y Wo^T + bo
+        TRY(dw(dres_t, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
+        TRY(bias(dres, 1, C, L.b_o[l]));
+        {
+            GemmDesc g;
+            g.A = dres_t; g.lda = C; g.a_layout = 0;
+            g.B = h->wop(L.w_o[l]); g.ldb = C; g.b_layout = 1;
+            g.M = BT; g.N = C; g.K = C;
+            g.epi = EPI_BIAS_T; g.C = h->at<char>(P.datt); g.ldc = C; g.alpha = 1.f;
+            TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
+        }
+        TRY(run(h, "attn_bwd", [&] {
+            return attention_backward(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), h->at<char>(P.datt),
+                                      h->at<float>(P.lse[l]), h->at<float>(P.Dbuf), h->at<char>(P.dqkv), B, T, H, hs, bf, s);
+        }));
+        TRY(dw(h->at<char>(P.dqkv), 3 * C, h->at<char>(P.h1[l]), C, 3 * C, C, L.w_qkv[l]));
+        TRY(bias(h->at<char>(P.dqkv), 0, 3 * C, L.b_qkv[l]));
+        {
+            GemmDesc g;
+            g.A = h->at<char>(P.dqkv); g.lda = 3 * C; g.a_layout = 0;
+            g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 1;
+            g.M = BT; g.N = C; g.K = 3 * C;
+            g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
+            TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
+        }
+        TRY(ln_bwd(h->at<float>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1));
+    }
+    // embeddings: token rows scatter-add on top of the lm_head gradient, position rows
+    if (!acc && T < c.block_size)
+        HIPTRY(fill(grd + L.wpe + (int64_t)T * C, (int64_t)(c.block_size - T) * C, 0.f, s), "zero wpe tail");
+    TRY(run(h, "embed_bwd", [&] {
+        return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc,
+                              h->at<char>(P.ebscratch), s);
+    }));
+    return GPT2_OK;
+}
+
+// =================================================================== optimizer
+extern "C" int gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float eps, float weight_decay,
+                               float max_grad_norm, int32_t t, float* d_grad_norm, float* h_grad_norm) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    if (t < 1) return set_error(GPT2_EINVAL, "AdamW step t must be >= 1");
+    const Plan& P = h->P;
+    hipStream_t s = h->stream;
+    float* coef = h->at<float>(P.normcoef);
+    const int64_t N = h->L.n_params;
+    TRY(run(h, "grad_norm", [&] { return grad_norm(h->grads(), N, h->at<float>(P.normpart), coef, max_grad_norm, s); }));
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
+    TRY(run(h, "adamw", [&] {
+        return adamw(h->params(), h->grads(), h->at<float>(P.m), h->at<float>(P.v), h->bf16 ? h->at<char>(P.shadow) : nullptr,
+                     N, h->L.decay_end, coef, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)std::sqrt(bc2), s);
+    }));
+    if (d_grad_norm) HIPTRY(hipMemcpyAsync(d_grad_norm, coef, 4, hipMemcpyDeviceToDevice, s), "copy norm");
+    if (h_grad_norm) {
+        HIPTRY(hipMemcpyAsync(h_grad_norm, coef, 4, hipMemcpyDeviceToHost, s), "copy norm");
+        HIPTRY(hipStreamSynchronize(s), "synchronize");
+    }
+    return GPT2_OK;
+}
+
+// =================================================================== diagnostics
+extern "C" int gpt2_timing_begin(gpt2_t* h, const char* name) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    if (name && class_index(name) < 0) return set_error(GPT2_EINVAL, "unknown kernel class %s", name);
+    h->timing = true;
+    h->filter = name ? name : "";
+    h->ev_used = 0;
+    h->times.clear();
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_timing_end(gpt2_t* h) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    h->timing = false;
+    HIPTRY(hipStreamSynchronize(h->stream), "synchronize");
+    for (size_t i = 0; i < h->ev_used; ++i) {
+        float ms = 0.f;
+        HIPTRY(hipEventElapsedTime(&ms, h->ev[i].first, h->ev[i].second), "event time");
+        auto& t = h->times[kClasses[h->ev_cls[i]]];
+        t.first += ms;
+        t.second += 1;
+    }
+    h->ev_used = 0;
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_timing_get(gpt2_t* h, const char* name, double* total_ms, int64_t* launches) {
+    if (!h || !name) return set_error(GPT2_EINVAL, "null argument");
+    auto it = h->times.find(name);
+    if (total_ms) *total_ms = it == h->times.end() ? 0.0 : it->second.first;
+    if (launches) *launches = it == h->times.end() ? 0 : it->second.second;
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_debug_tensor(gpt2_t* h, const char* which, int32_t layer, float* d_dst, int64_t* count) {
+    if (!h || !which || !count) return set_error(GPT2_EINVAL, "null argument");
+    const gpt2_config& c = h->cfg;
+    const int64_t BT = (int64_t)h->B * h->T;
+    if (BT == 0) return set_error(GPT2_ESTATE, "no forward yet");
+    const int64_t C = c.n_embd, F = c.mlp_hidden;
+    const Plan& P = h->P;
+    const bool lay = layer >= 0 && layer < c.n_layer;
+    size_t off = 0;
+    int64_t n = 0;
+    bool f32 = false;
+    std::string w = which;
+    if (w == "x_in" && layer >= 0 && layer <= c.n_layer) { off = P.x_in[layer]; n = BT * C; f32 = true; }
+    else if (w == "x_out") { off = P.x_in[c.n_layer]; n = BT * C; f32 = true; }
+    else if (w == "hf") { off = P.hf; n = BT * C; }
+    else if (w == "dz") { off = P.logits; n = BT * c.padded_vocab_size; }
+    else if (lay && w == "h1") { off = P.h1[layer]; n = BT * C; }
+    else if (lay && w == "qkv") { off = P.qkv[layer]; n = BT * 3 * C; }
+    else if (lay && w == "att") { off = P.att[layer]; n = BT * C; }
+    else if (lay && w == "lse") { off = P.lse[layer]; n = BT * c.n_head; f32 = true; }
+    else if (lay && w == "h2") { off = P.h2[layer]; n = BT * C; }
+    else if (lay && w == "u") { off = P.u[layer]; n = BT * F; }
+    else if (lay && w == "a") { off = P.a[layer]; n = BT * F; }
+    else return set_error(GPT2_EINVAL, "unknown tensor %s / layer %d", which, layer);
+    *count = n;
+    if (!d_dst) return GPT2_OK;
+    HIPTRY(convert_to_f32(h->ws + off, d_dst, n, f32 ? 0 : h->bf16, h->stream), "convert");
+    return GPT2_OK;
+}

@@ -1,0 +1,95 @@
+// Host-side launchers of the GPT-2 step kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt2k {
+
+// ------------------------------------------------------------------ GEMM
+enum Epi {
+    EPI_BIAS_T = 0,          // C(T)   = alpha*acc + bias[n]           (bias may be null)
+    EPI_BIAS_RESID_F32 = 1,  // C(f32) = resid[m][n] + acc + bias[n]
+    EPI_BIAS_GELU = 2,       // C(T)   = u = acc + bias[n];  C2(T) = gelu_tanh(u)
+    EPI_GELU_BWD = 3,        // C(T)   = acc * gelu_tanh'(aux[m][n])
+    EPI_F32 = 4,             // C(f32) = (beta ? C : 0) + alpha*acc
+    EPI_PARTIAL = 5,         // internal: split-K partials
+};
+
+struct GemmDesc {
+    const void* A = nullptr; int64_t lda = 0; int a_layout = 0;  // 0: A[m*lda+k], 1: A[k*lda+m]
+    const void* B = nullptr; int64_t ldb = 0; int b_layout = 0;  // 0: B[n*ldb+k], 1: B[k*ldb+n]
+    int M = 0, N = 0, K = 0;
+    int epi = EPI_BIAS_T;
+    void* C = nullptr; int64_t ldc = 0;
+    void* C2 = nullptr;
+    const float* bias = nullptr;
+    const float* resid = nullptr; int64_t ldr = 0;
+    const void* aux = nullptr; int64_t ldaux = 0;
+    float alpha = 1.f;
+    int beta = 0;
+    int nsplit = 1;          // split K into this many parts (EPI_F32 with ldc == N only)
+    void* partial = nullptr; // fp32 scratch of nsplit*M*N floats when nsplit > 1
+};
+
+hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+void gemm_setup();
+size_t gemm_lds_bytes();
+
+// ------------------------------------------------------------------ elementwise / rows
+hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, float* x,
+                         int B, int T, int C, hipStream_t s);
+// LayerNorm forward: out(T) = (x - mean) * rstd * w + b ; saves mean, rstd (fp32)
+hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
+                             float* rstd, int rows, int C, int is_bf16, hipStream_t s);
+// LayerNorm backward: dres (+)= dx ; dres_t = T copy of dres (may be null);
+// partial[blk][0:C] = sum dh*xhat, partial[blk][C:2C] = sum dh over the block's rows.
+hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
+                              const float* w, float* dres, void* dres_t, int accumulate_dres,
+                              float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
+int layernorm_backward_blocks(int rows);
+// out[c] (+)= sum_blk partial[blk][c] for c < n (fixed order); used for LN dw/db
+hipError_t sum_partials(const float* partial, int nblk, int n, float* out, int accumulate, hipStream_t s);
+// column sums of a [rows, n] matrix (storage T or f32) into out[n] (+)=, deterministic
+hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial,
+                  float* out, int accumulate, hipStream_t s);
+int colsum_partial_floats(int rows, int n);
+
+// cross-entropy over rows of logits(T) [n_rows, Vp]: loss_rows[r] = lse - z[y]; logits are
+// overwritten by dz = (softmax - onehot) / n_rows; optional fp32 copy of the logits.
+hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows, float* logits_f32,
+                         int n_rows, int Vp, int is_bf16, hipStream_t s);
+hipError_t convert_to_f32(const void* src, float* dst, int64_t n, int is_bf16, hipStream_t s);
+// mean of loss_rows -> *d_loss (single block, fixed order)
+hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s);
+
+// embedding backward (deterministic): dwte[idx[r]] += dx[r] in ascending r, dwpe[t] (+)= sum_b dx[b,t]
+size_t embed_backward_scratch_bytes(int rows, int C);
+void rows_setup();
+hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int T,
+                          int C, int accumulate_wpe, void* scratch, hipStream_t s);
+
+// global grad norm + clip coefficient, AdamW
+int norm_blocks();
+hipError_t grad_norm(const float* g, int64_t n, float* partial, float* d_norm_coef /* [2] */,
+                     float max_norm, hipStream_t s);
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow_bf16, int64_t n,
+                 int64_t n_decay, const float* d_norm_coef, float lr, float beta1, float beta2,
+                 float eps, float wd, float bc1, float bc2_sqrt, hipStream_t s);
+hipError_t refresh_shadow(const float* p, void* shadow_bf16, int64_t n, hipStream_t s);
+
+// device init: counter-based normals (Philox-4x32-10 + Box-Muller) times std, or constants
+hipError_t init_normal(float* p, int64_t n, float stdv, uint64_t seed, uint64_t offset, hipStream_t s);
+hipError_t fill(float* p, int64_t n, float v, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+// qkv(T) [B*T, 3C] (q | k | v, head h = columns h*hs..), y(T) [B*T, C], lse fp32 [B*H*T]
+hipError_t attention_forward(const void* qkv, void* y, float* lse, int B, int T, int H, int hs,
+                             int is_bf16, hipStream_t s);
+// dy(T) [B*T, C], D scratch fp32 [B*H*T], dqkv(T) [B*T, 3C]
+hipError_t attention_backward(const void* qkv, const void* y, const void* dy, const float* lse,
+                              float* D, void* dqkv, int B, int T, int H, int hs, int is_bf16,
+                              hipStream_t s);
+void attention_setup();
+
+}  // namespace gpt2k

@@ -1,0 +1,717 @@
+// Memory-bound kernels of the GPT-2 step: embedding forward/backward, LayerNorm
+// forward/backward, bias (column) sums, softmax cross-entropy, gradient norm, AdamW and
+// parameter initialization. Every reduction runs in a fixed order, so results are bitwise
+// reproducible run to run.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+
+// ================================================================== embedding forward
+// x[b,t,:] = wte[idx[b,t],:] + wpe[t,:] ("Code you'll write", forward pass: token and
+// position embeddings are added). One wave per token row, float4 accesses.
+__global__ void embed_forward_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
+                                     const float* __restrict__ wpe, float* __restrict__ x, int rows,
+                                     int T, int C) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int t = row % T;
+    const int64_t id = idx[row];
+    const int nv = C >> 2;
+    const float4* e = (const float4*)(wte + id * C);
+    const float4* p = (const float4*)(wpe + (int64_t)t * C);
+    float4* o = (float4*)(x + (int64_t)row * C);
+    for (int c = lane; c < nv; c += 64) {
+        const float4 a = e[c], b = p[c];
+        o[c] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+    }
+}
+
+hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, float* x, int B, int T,
+                         int C, hipStream_t s) {
+    const int rows = B * T;
+    hipLaunchKernelGGL(embed_forward_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe, x, rows, T, C);
+    return hipGetLastError();
+}
+
+// ================================================================== LayerNorm
+// nn.LayerNorm(C) with eps 1e-5 and the biased variance. One wave per row; the row stays in
+// registers (up to 8 float4 per lane: C <= 2048); mean, then centered variance.
+constexpr int LN_NV = 8;
+constexpr float LN_EPS = 1e-5f;
+
+template <typename T> DEV void store4(T* p, float a, float b, float c, float d);
+template <> DEV void store4<float>(float* p, float a, float b, float c, float d) { *(float4*)p = make_float4(a, b, c, d); }
+template <> DEV void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *(bf16x4*)p = v;
+}
+template <typename T> DEV float4 load4(const T* p);
+template <> DEV float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <> DEV float4 load4<bf16>(const bf16* p) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 v = *(const bf16x4*)p;
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
+template <typename T>
+__global__ void layernorm_forward_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                         const float* __restrict__ b, T* __restrict__ out,
+                                         float* __restrict__ mean, float* __restrict__ rstd, int rows, int C) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int nv = C >> 2;
+    const float4* xr = (const float4*)(x + (int64_t)row * C);
+    float4 v[LN_NV];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < LN_NV; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    }
+    const float mu = wave_sum(s) / (float)C;
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < LN_NV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nv) {
+            const float a = v[j].x - mu, bb = v[j].y - mu, cc = v[j].z - mu, d = v[j].w - mu;
+            s2 += (a * a + bb * bb) + (cc * cc + d * d);
+        }
+    }
+    const float var = wave_sum(s2) / (float)C;
+    const float r = 1.0f / sqrtf(var + LN_EPS);
+#pragma unroll
+    for (int j = 0; j < LN_NV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nv) {
+            const float4 ww = ((const float4*)w)[c], bb = ((const float4*)b)[c];
+            store4<T>(out + (int64_t)row * C + 4 * c, (v[j].x - mu) * r * ww.x + bb.x, (v[j].y - mu) * r * ww.y + bb.y,
+                      (v[j].z - mu) * r * ww.z + bb.z, (v[j].w - mu) * r * ww.w + bb.w);
+        }
+    }
+    if (lane == 0) { mean[row] = mu; rstd[row] = r; }
+}
+
+hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
+                             float* rstd, int rows, int C, int is_bf16, hipStream_t s) {
+    if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
+    dim3 g((rows + 3) / 4);
+    if (is_bf16) hipLaunchKernelGGL(layernorm_forward_kernel<bf16>, g, dim3(256), 0, s, x, w, b, (bf16*)out, mean, rstd, rows, C);
+    else hipLaunchKernelGGL(layernorm_forward_kernel<float>, g, dim3(256), 0, s, x, w, b, (float*)out, mean, rstd, rows, C);
+    return hipGetLastError();
+}
+
+// Backward through y = xhat*w + b, xhat = (x - mean)*rstd:
+//   dxhat = dh*w;  dx = rstd*(dxhat - mean(dxhat) - xhat*mean(dxhat*xhat))
+//   dw += sum_rows dh*xhat;  db += sum_rows dh
+// Waves take rows in a fixed stride; each wave's dw/db partial goes through LDS into one
+// partial row per block (fixed order), finished by sum_partials.
+constexpr int LNB_BLOCKS = 256;
+int layernorm_backward_blocks(int rows) { return rows < LNB_BLOCKS * 4 ? (rows + 3) / 4 : LNB_BLOCKS; }
+
+template <typename T>
+__global__ void layernorm_backward_kernel(const float* __restrict__ dh, const float* __restrict__ x,
+                                          const float* __restrict__ mean, const float* __restrict__ rstd,
+                                          const float* __restrict__ w, float* __restrict__ dres,
+                                          T* __restrict__ dres_t, int accumulate, float* __restrict__ partial,
+                                          int rows, int C) {
+    extern __shared__ float sred[];  // [4][2C]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nv = C >> 2;
+    const int nwaves = gridDim.x * 4;
+    float4 dw[LN_NV], db[LN_NV], wv[LN_NV];
+#pragma unroll
+    for (int j = 0; j < LN_NV; ++j) {
+        dw[j] = db[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int c = lane + 64 * j;
+        wv[j] = c < nv ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int row = blockIdx.x * 4 + wave; row < rows; row += nwaves) {
+        const float mu = mean[row], r = rstd[row];
+        const float4* dr = (const float4*)(dh + (int64_t)row * C);
+        const float4* xr = (const float4*)(x + (int64_t)row * C);
+        float4 xh[LN_NV], dxh[LN_NV];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < LN_NV; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nv) {
+                const float4 d = dr[c], xx = xr[c];
+                xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
+                dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
+                s1 += (dxh[j].x + dxh[j].y) + (dxh[j].z + dxh[j].w);
+                s2 += (dxh[j].x * xh[j].x + dxh[j].y * xh[j].y) + (dxh[j].z * xh[j].z + dxh[j].w * xh[j].w);
+                dw[j].x += d.x * xh[j].x; dw[j].y += d.y * xh[j].y; dw[j].z += d.z * xh[j].z; dw[j].w += d.w * xh[j].w;
+                db[j].x += d.x; db[j].y += d.y; db[j].z += d.z; db[j].w += d.w;
+            }
+        }
+        const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
+        float4* o = (float4*)(dres + (int64_t)row * C);
+#pragma unroll
+        for (int j = 0; j < LN_NV; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nv) {
+                float4 g = make_float4(r * (dxh[j].x - m1 - xh[j].x * m2), r * (dxh[j].y - m1 - xh[j].y * m2),
+                                       r * (dxh[j].z - m1 - xh[j].z * m2), r * (dxh[j].w - m1 - xh[j].w * m2));
+                if (accumulate) {
+                    const float4 old = o[c];
+                    g.x += old.x; g.y += old.y; g.z += old.z; g.w += old.w;
+                }
+                o[c] = g;
+                if (dres_t) store4<T>(dres_t + (int64_t)row * C + 4 * c, g.x, g.y, g.z, g.w);
+            }
+        }
+    }
+    // combine the 4 waves' partials in a fixed order
+#pragma unroll
+    for (int j = 0; j < LN_NV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nv) {
+            *(float4*)(sred + wave * 2 * C + 4 * c) = dw[j];
+            *(float4*)(sred + wave * 2 * C + C + 4 * c) = db[j];
+        }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
+        const float v = ((sred[c] + sred[2 * C + c]) + sred[4 * C + c]) + sred[6 * C + c];
+        partial[(int64_t)blockIdx.x * 2 * C + c] = v;
+    }
+}
+
+hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
+                              const float* w, float* dres, void* dres_t, int accumulate_dres, float* partial,
+                              int nblk, int rows, int C, int is_bf16, hipStream_t s) {
+    if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
+    const size_t lds = 8 * (size_t)C * sizeof(float);
+    if (is_bf16)
+        hipLaunchKernelGGL(layernorm_backward_kernel<bf16>, dim3(nblk), dim3(256), lds, s, dh, x, mean, rstd, w, dres,
+                           (bf16*)dres_t, accumulate_dres, partial, rows, C);
+    else
+        hipLaunchKernelGGL(layernorm_backward_kernel<float>, dim3(nblk), dim3(256), lds, s, dh, x, mean, rstd, w, dres,
+                           (float*)dres_t, accumulate_dres, partial, rows, C);
+    return hipGetLastError();
+}
+
+// out[c] (+)= sum over p of partial[p][c], p in increasing order within each of 8 slices,
+// slices combined in a fixed tree. Block: 32 columns x 8 slices.
+__global__ void sum_partials_kernel(const float* __restrict__ partial, int np, int n, float* __restrict__ out,
+                                    int accumulate) {
+    __shared__ float red[8][33];
+    const int col = blockIdx.x * 32 + (threadIdx.x & 31);
+    const int slice = threadIdx.x >> 5;
+    const int per = (np + 7) / 8;
+    const int p0 = slice * per;
+    int p1 = p0 + per;
+    if (p1 > np) p1 = np;
+    float acc = 0.f;
+    if (col < n)
+        for (int p = p0; p < p1; ++p) acc += partial[(int64_t)p * n + col];
+    red[slice][threadIdx.x & 31] = acc;
+    __syncthreads();
+    if (slice == 0 && col < n) {
+        const int c = threadIdx.x & 31;
+        const float v = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) +
+                        ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
+        out[col] = accumulate ? out[col] + v : v;
+    }
+}
+
+hipError_t sum_partials(const float* partial, int nblk, int n, float* out, int accumulate, hipStream_t s) {
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((n + 31) / 32), dim3(256), 0, s, partial, nblk, n, out, accumulate);
+    return hipGetLastError();
+}
+
+// column sums of x [rows, n]: stage 1 writes one partial row per row-slice, stage 2 is
+// sum_partials. Slices are fixed for a given (rows, n).
+constexpr int CS_SLICE_ROWS = 64;
+int colsum_partial_floats(int rows, int n) { return ((rows + CS_SLICE_ROWS - 1) / CS_SLICE_ROWS) * n; }
+
+template <typename X>
+__global__ void colsum_kernel(const X* __restrict__ x, int rows, int n, float* __restrict__ partial) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    const int slice = blockIdx.y;
+    if (col >= n) return;
+    const int r0 = slice * CS_SLICE_ROWS;
+    int r1 = r0 + CS_SLICE_ROWS;
+    if (r1 > rows) r1 = rows;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    int r = r0;
+    for (; r + 4 <= r1; r += 4) {
+        a0 += to_f<X>(x[(int64_t)r * n + col]);
+        a1 += to_f<X>(x[(int64_t)(r + 1) * n + col]);
+        a2 += to_f<X>(x[(int64_t)(r + 2) * n + col]);
+        a3 += to_f<X>(x[(int64_t)(r + 3) * n + col]);
+    }
+    for (; r < r1; ++r) a0 += to_f<X>(x[(int64_t)r * n + col]);
+    partial[(int64_t)slice * n + col] = (a0 + a1) + (a2 + a3);
+}
+
+hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial, float* out,
+                  int accumulate, hipStream_t s) {
+    const int ns = (rows + CS_SLICE_ROWS - 1) / CS_SLICE_ROWS;
+    dim3 g((n + 255) / 256, ns);
+    if (x_is_f32 || !is_bf16) hipLaunchKernelGGL(colsum_kernel<float>, g, dim3(256), 0, s, (const float*)x, rows, n, partial);
+    else hipLaunchKernelGGL(colsum_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, rows, n, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return sum_partials(partial, ns, n, out, accumulate, s);
+}
+
+// ================================================================== cross-entropy
+// Per row n of z [rows, Vp]: lse = log sum_j exp z_j (all Vp columns), loss_n = lse - z_{y_n},
+// then z is overwritten by dz = (softmax(z) - onehot(y)) / rows (F.cross_entropy with mean
+// reduction on the flattened logits). One workgroup per row, two passes (the second re-reads
+// the row from cache). The (max, sum) pairs are merged in a fixed order.
+template <typename T>
+__global__ void cross_entropy_kernel(T* __restrict__ z, const int32_t* __restrict__ targets,
+                                     float* __restrict__ loss_rows, float* __restrict__ z_f32, int rows, int Vp) {
+    constexpr int E = 16 / sizeof(T);
+    __shared__ float smax[256 / 64], ssum[256 / 64];
+    const int row = blockIdx.x;
+    T* zr = z + (int64_t)row * Vp;
+    const int nvec = Vp / E;
+    float mx = -INFINITY, sm = 0.f;
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+        const uint4 raw = ld16(zr + v * E);
+        const T* e = (const T*)&raw;
+        float vals[E];
+        float lm = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < E; ++q) { vals[q] = to_f<T>(e[q]); lm = fmaxf(lm, vals[q]); }
+        if (z_f32) {
+#pragma unroll
+            for (int q = 0; q < E; q += 4)
+                *(float4*)(z_f32 + (int64_t)row * Vp + v * E + q) = make_float4(vals[q], vals[q + 1], vals[q + 2], vals[q + 3]);
+        }
+        const float nm = fmaxf(mx, lm);
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < E; ++q) s += __expf(vals[q] - nm);
+        sm = sm * __expf(mx - nm) + s;
+        mx = nm;
+    }
+    // merge (mx, sm) across the wave, then across the 4 waves in order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float om = __shfl_xor(mx, o), os = __shfl_xor(sm, o);
+        const float nm = fmaxf(mx, om);
+        sm = (mx == -INFINITY ? 0.f : sm * __expf(mx - nm)) + (om == -INFINITY ? 0.f : os * __expf(om - nm));
+        mx = nm;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { smax[w] = mx; ssum[w] = sm; }
+    __syncthreads();
+    float M = smax[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, smax[i]);
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S += ssum[i] * __expf(smax[i] - M);
+    const float lse = M + __logf(S);
+    const int y = targets[row];
+    if (threadIdx.x == 0) loss_rows[row] = lse - to_f<T>(zr[y]);
+    __syncthreads();  // zr[y] read before any overwrite
+    const float inv_n = 1.0f / (float)rows;
+    for (int v = threadIdx.x; v < nvec; v += 256) {
+        uint4 raw = ld16(zr + v * E);
+        T* e = (T*)&raw;
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+            const int j = v * E + q;
+            const float p = __expf(to_f<T>(e[q]) - lse);
+            e[q] = from_f<T>((p - (j == y ? 1.f : 0.f)) * inv_n);
+        }
+        st16(zr + v * E, raw);
+    }
+}
+
+hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows, float* logits_f32, int n_rows,
+                         int Vp, int is_bf16, hipStream_t s) {
+    if (Vp % 8) return hipErrorInvalidValue;
+    if (is_bf16) hipLaunchKernelGGL(cross_entropy_kernel<bf16>, dim3(n_rows), dim3(256), 0, s, (bf16*)logits, targets, loss_rows, logits_f32, n_rows, Vp);
+    else hipLaunchKernelGGL(cross_entropy_kernel<float>, dim3(n_rows), dim3(256), 0, s, (float*)logits, targets, loss_rows, logits_f32, n_rows, Vp);
+    return hipGetLastError();
+}
+
+template <typename T>
+__global__ void convert_kernel(const T* __restrict__ src, float* __restrict__ dst, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = to_f<T>(src[i]);
+}
+hipError_t convert_to_f32(const void* src, float* dst, int64_t n, int is_bf16, hipStream_t s) {
+    if (is_bf16) hipLaunchKernelGGL(convert_kernel<bf16>, dim3(2048), dim3(256), 0, s, (const bf16*)src, dst, n);
+    else hipLaunchKernelGGL(convert_kernel<float>, dim3(2048), dim3(256), 0, s, (const float*)src, dst, n);
+    return hipGetLastError();
+}
+
+// mean of v[0..n): one block, each thread sums a contiguous slice, fixed tree across threads
+__global__ void mean_reduce_kernel(const float* __restrict__ v, int n, float* __restrict__ out) {
+    __shared__ double red[1024];
+    const int per = (n + 1023) / 1024;
+    const int i0 = threadIdx.x * per;
+    double s = 0.0;
+    for (int i = i0; i < i0 + per && i < n; ++i) s += v[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = (float)(red[0] / (double)n);
+}
+hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s) {
+    hipLaunchKernelGGL(mean_reduce_kernel, dim3(1), dim3(1024), 0, s, v, n, d_out);
+    return hipGetLastError();
+}
+
+// ================================================================== embedding backward
+// dwte[idx[r]] += dx[r] summed in ascending r per id, dwpe[t] (+)= sum_b dx[b,t].
+// The gradients of repeated ids add ("Code you'll write" ties wte to lm_head; chapter
+// 1:06:18-1:13:27: the two uses' gradients add up on the one tensor).
+// 1) one workgroup sorts the (id, row) keys of a chunk of <= 16384 rows in LDS (bitonic),
+//    cuts the sorted list into segments (same id, <= SEG rows, aligned to SEG) and runs
+//    (same id), 2) every segment's rows are summed in order into a partial row,
+// 3) every run adds its segments' partials in order to its wte row.
+constexpr int EB_CHUNK = 16384;  // rows per sort (keys: id << 14 | row, ids < 2^18)
+constexpr int EB_SEG = 32;
+constexpr int EB_THREADS = 1024;
+
+struct EbMeta {
+    int nseg, nrun;
+};
+
+size_t embed_backward_scratch_bytes(int rows, int C) {
+    const int n = rows < EB_CHUNK ? rows : EB_CHUNK;
+    const int maxseg = n;  // at most one segment per row
+    size_t b = 0;
+    b += 256;                                   // meta
+    b += (size_t)n * 4;                         // sorted rows
+    b += (size_t)(maxseg + 1) * 4;              // segment begin
+    b += (size_t)(n + 1) * 4 * 2;               // run id, run first segment
+    b = (b + 255) & ~(size_t)255;
+    b += (size_t)maxseg * C * 4;                // segment partial sums
+    return b;
+}
+
+__global__ void __launch_bounds__(EB_THREADS) eb_sort_kernel(const int32_t* __restrict__ idx, int n,
+                                                             EbMeta* meta, int32_t* __restrict__ srow,
+                                                             int32_t* __restrict__ seg_begin, int32_t* __restrict__ run_id,
+                                                             int32_t* __restrict__ run_seg) {
+    extern __shared__ uint32_t keys[];  // [np2]
+    __shared__ int cnt_s[EB_THREADS], cnt_r[EB_THREADS];
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < np2; i += EB_THREADS)
+        keys[i] = i < n ? ((uint32_t)idx[i] << 14) | (uint32_t)i : 0xFFFFFFFFu;
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < np2; i += EB_THREADS) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint32_t a = keys[i], b = keys[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // each thread owns a contiguous range of sorted positions
+    const int per = (n + EB_THREADS - 1) / EB_THREADS;
+    const int i0 = tid * per;
+    int i1 = i0 + per;
+    if (i1 > n) i1 = n;
+    int cs = 0, cr = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t id = keys[i] >> 14;
+        const bool run = i == 0 || (keys[i - 1] >> 14) != id;
+        const bool seg = run || (i % EB_SEG) == 0;
+        cs += seg;
+        cr += run;
+    }
+    cnt_s[tid] = cs;
+    cnt_r[tid] = cr;
+    __syncthreads();
+    // exclusive scans (thread 0, sequential over 1024 entries: cheap next to the sort)
+    if (tid == 0) {
+        int a = 0, b = 0;
+        for (int t = 0; t < EB_THREADS; ++t) {
+            const int x = cnt_s[t], y = cnt_r[t];
+            cnt_s[t] = a; cnt_r[t] = b;
+            a += x; b += y;
+        }
+        meta->nseg = a;
+        meta->nrun = b;
+        seg_begin[a] = n;
+        run_seg[b] = a;
+    }
+    __syncthreads();
+    int s = cnt_s[tid] - 1, r = cnt_r[tid] - 1;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t key = keys[i];
+        const uint32_t id = key >> 14;
+        const bool run = i == 0 || (keys[i - 1] >> 14) != id;
+        const bool seg = run || (i % EB_SEG) == 0;
+        if (seg) { ++s; seg_begin[s] = i; }
+        if (run) { ++r; run_id[r] = (int32_t)id; run_seg[r] = s; }
+        srow[i] = (int32_t)(key & 0x3FFF);
+    }
+}
+
+__global__ void eb_segment_kernel(const EbMeta* meta, const int32_t* __restrict__ srow,
+                                  const int32_t* __restrict__ seg_begin, const float* __restrict__ dx, int row0,
+                                  int C, float* __restrict__ part) {
+    const int nseg = meta->nseg;
+    const int nv = C >> 2;
+    for (int sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+        const int b = seg_begin[sg], e = seg_begin[sg + 1];
+        for (int c = threadIdx.x; c < nv; c += blockDim.x) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int i = b; i < e; ++i) {
+                const float4 v = ((const float4*)(dx + (int64_t)(row0 + srow[i]) * C))[c];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            ((float4*)(part + (int64_t)sg * C))[c] = acc;
+        }
+    }
+}
+
+__global__ void eb_run_kernel(const EbMeta* meta, const int32_t* __restrict__ run_id,
+                              const int32_t* __restrict__ run_seg, const float* __restrict__ part, int C,
+                              float* __restrict__ dwte) {
+    const int nrun = meta->nrun;
+    const int nv = C >> 2;
+    for (int r = blockIdx.x; r < nrun; r += gridDim.x) {
+        const int s0 = run_seg[r], s1 = run_seg[r + 1];
+        float4* dst = (float4*)(dwte + (int64_t)run_id[r] * C);
+        for (int c = threadIdx.x; c < nv; c += blockDim.x) {
+            float4 acc = dst[c];
+            for (int s = s0; s < s1; ++s) {
+                const float4 v = ((const float4*)(part + (int64_t)s * C))[c];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            dst[c] = acc;
+        }
+    }
+}
+
+__global__ void dwpe_kernel(const float* __restrict__ dx, float* __restrict__ dwpe, int B, int T, int C, int accumulate) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over T*C
+    if (i >= (int64_t)T * C) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += dx[(int64_t)b * T * C + i];
+    dwpe[i] = accumulate ? dwpe[i] + s : s;
+}
+
+hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int T, int C,
+                          int accumulate_wpe, void* scratch, hipStream_t s) {
+    const int rows = B * T;
+    char* p = (char*)scratch;
+    EbMeta* meta = (EbMeta*)p;
+    p += 256;
+    const int n_max = rows < EB_CHUNK ? rows : EB_CHUNK;
+    int32_t* srow = (int32_t*)p; p += (size_t)n_max * 4;
+    int32_t* seg_begin = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    int32_t* run_id = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    int32_t* run_seg = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    size_t off = (size_t)(p - (char*)scratch);
+    off = (off + 255) & ~(size_t)255;
+    float* part = (float*)((char*)scratch + off);
+    for (int r0 = 0; r0 < rows; r0 += EB_CHUNK) {
+        const int n = rows - r0 < EB_CHUNK ? rows - r0 : EB_CHUNK;
+        int np2 = 1;
+        while (np2 < n) np2 <<= 1;
+        hipLaunchKernelGGL(eb_sort_kernel, dim3(1), dim3(EB_THREADS), (size_t)np2 * 4, s, idx + r0, n, meta, srow,
+                           seg_begin, run_id, run_seg);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(eb_segment_kernel, dim3(2048), dim3(C / 4 < 256 ? ((C / 4 + 63) / 64) * 64 : 256), 0, s,
+                           meta, srow, seg_begin, dx, r0, C, part);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(eb_run_kernel, dim3(2048), dim3(C / 4 < 256 ? ((C / 4 + 63) / 64) * 64 : 256), 0, s,
+                           meta, run_id, run_seg, part, C, dwte);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t tc = (int64_t)T * C;
+    hipLaunchKernelGGL(dwpe_kernel, dim3((unsigned)((tc + 255) / 256)), dim3(256), 0, s, dx, dwpe, B, T, C, accumulate_wpe);
+    return hipGetLastError();
+}
+
+void rows_setup() {
+    // the id sort keeps up to EB_CHUNK 4-byte keys in LDS next to its static scan arrays
+    (void)hipFuncSetAttribute((const void*)eb_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, EB_CHUNK * 4);
+}
+
+// ================================================================== gradient norm + AdamW
+// norm = sqrt(sum g^2) over the whole gradient arena (wte once), clip coefficient
+// c = min(1, max_norm/(norm + 1e-6)) as clip_grad_norm_ computes it (chapter 2:14:58-2:25:57).
+constexpr int NORM_BLOCKS = 1024;
+int norm_blocks() { return NORM_BLOCKS; }
+
+__global__ void norm_partial_kernel(const float* __restrict__ g, int64_t n4, float* __restrict__ partial) {
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const float4 v = ((const float4*)g)[i];
+        s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+    s = block_sum<256>(s, red);
+    if (threadIdx.x == 0) partial[blockIdx.x] = s;
+}
+
+__global__ void norm_final_kernel(const float* __restrict__ partial, int np, const float* __restrict__ tail,
+                                  int ntail, float* __restrict__ out, float max_norm) {
+    __shared__ double red[1024];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < np; i += 1024) s += partial[i];
+    if (threadIdx.x == 0)
+        for (int i = 0; i < ntail; ++i) s += (double)tail[i] * tail[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double norm = sqrt(red[0]);
+        double c = (double)max_norm / (norm + 1e-6);
+        if (c > 1.0) c = 1.0;
+        out[0] = (float)norm;
+        out[1] = (float)c;
+    }
+}
+
+hipError_t grad_norm(const float* g, int64_t n, float* partial, float* d_norm_coef, float max_norm, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(norm_partial_kernel, dim3(NORM_BLOCKS), dim3(256), 0, s, g, n4, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(1024), 0, s, partial, NORM_BLOCKS, g + n4 * 4, (int)(n - n4 * 4),
+                       d_norm_coef, max_norm);
+    return hipGetLastError();
+}
+
+// AdamW, PyTorch form (chapter 52:38-1:06:18 shows its documentation; weight decay only on
+// the 2-D tensors, chapter 2:25:57-2:34:49): p *= 1 - lr*wd; m = b1 m + (1-b1) g;
+// v = b2 v + (1-b2) g^2; p -= (lr/bc1) * m / (sqrt(v)/sqrt(bc2) + eps), g = c * grad.
+// The bf16 copy of the 2-D weights used by the products is refreshed in the same pass.
+__global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
+                             float* __restrict__ v, bf16* __restrict__ shadow, int64_t n4, int64_t n_decay4,
+                             const float* __restrict__ norm_coef, float lr, float beta1, float beta2, float eps,
+                             float wd, float bc1, float bc2_sqrt) {
+    const float c = norm_coef[1];
+    const float step = lr / bc1;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        float4 pp = ((float4*)p)[i];
+        const float4 gg = ((const float4*)g)[i];
+        float4 mm = ((float4*)m)[i];
+        float4 vv = ((float4*)v)[i];
+        const bool dec = i < n_decay4;
+        const float keep = dec ? 1.0f - lr * wd : 1.0f;
+        float* pa = (float*)&pp;
+        const float* ga = (const float*)&gg;
+        float* ma = (float*)&mm;
+        float* va = (float*)&vv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float gq = c * ga[q];
+            pa[q] *= keep;
+            ma[q] = beta1 * ma[q] + (1.0f - beta1) * gq;
+            va[q] = beta2 * va[q] + (1.0f - beta2) * gq * gq;
+            const float den = sqrtf(va[q]) / bc2_sqrt + eps;
+            pa[q] -= step * (ma[q] / den);
+        }
+        ((float4*)p)[i] = pp;
+        ((float4*)m)[i] = mm;
+        ((float4*)v)[i] = vv;
+        if (shadow && dec) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 b;
+            b[0] = (bf16)pa[0]; b[1] = (bf16)pa[1]; b[2] = (bf16)pa[2]; b[3] = (bf16)pa[3];
+            ((bf16x4*)shadow)[i] = b;
+        }
+    }
+}
+
+hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n, int64_t n_decay,
+                 const float* d_norm_coef, float lr, float beta1, float beta2, float eps, float wd, float bc1,
+                 float bc2_sqrt, hipStream_t s) {
+    if ((n & 3) || (n_decay & 3)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(adamw_kernel, dim3(4096), dim3(256), 0, s, p, g, m, v, (bf16*)shadow, n / 4, n_decay / 4,
+                       d_norm_coef, lr, beta1, beta2, eps, wd, bc1, bc2_sqrt);
+    return hipGetLastError();
+}
+
+__global__ void shadow_kernel(const float* __restrict__ p, bf16* __restrict__ sh, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        sh[i] = (bf16)p[i];
+}
+hipError_t refresh_shadow(const float* p, void* shadow, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(shadow_kernel, dim3(4096), dim3(256), 0, s, p, (bf16*)shadow, n);
+    return hipGetLastError();
+}
+
+// ================================================================== initialization
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): 10 rounds of two 32x32->64 multiplies with the published multipliers and Weyl
+// key increments. Uniforms from the 4 outputs feed two Box-Muller transforms.
+DEV void philox_round(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+}
+
+__global__ void init_normal_kernel(float* __restrict__ p, int64_t n, float stdv, uint64_t seed, uint64_t offset) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i * 4 < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t ctr = offset + (uint64_t)i;
+        uint32_t c[4] = {(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u};
+        uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+#pragma unroll
+        for (int r = 0; r < 10; ++r) {
+            philox_round(c, k0, k1);
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        float z[4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float u1 = ((float)(c[2 * q] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+            const float u2 = ((float)(c[2 * q + 1] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+            const float rad = sqrtf(-2.0f * logf(u1));
+            float sn, cs;
+            sincosf(6.283185307179586f * u2, &sn, &cs);
+            z[2 * q] = rad * cs;
+            z[2 * q + 1] = rad * sn;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (i * 4 + q < n) p[i * 4 + q] = stdv * z[q];
+    }
+}
+hipError_t init_normal(float* p, int64_t n, float stdv, uint64_t seed, uint64_t offset, hipStream_t s) {
+    hipLaunchKernelGGL(init_normal_kernel, dim3(2048), dim3(256), 0, s, p, n, stdv, seed, offset);
+    return hipGetLastError();
+}
+
+__global__ void fill_kernel(float* __restrict__ p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+hipError_t fill(float* p, int64_t n, float v, hipStream_t s) {
+    hipLaunchKernelGGL(fill_kernel, dim3(2048), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace gpt2k
