@@ -1,0 +1,236 @@
+"""Benchmark of the GPT-2 training step on one MI355X.
+
+One timed step = forward with loss + backward + clip/AdamW of GPT-2 124M at B=16, T=1024 in
+bf16 mode (the "gpt2_step" workload; other workloads with --workload). Inputs are seeded
+synthetic Zipf(1.1) token batches already resident in device memory; parameters follow the
+GPT-2 initialization. Prints one JSON line.
+
+  value       tokens/s of the whole job (one GPU)
+  mfu         tokens/s * (6N + 6*L*T*C) / dense bf16 MFMA peak (2.5166e15 FLOP/s)
+  roofline    the kernel class with the largest share of step time, timed live with HIP
+              events on the library's stream during the timed steps: algorithmic FLOPs or
+              bytes per launch / mean launch time, against the MI355X peak
+  kernels     ms per step of every kernel class (same live timing)
+  cpu_baseline  the CPU oracle (float32 numpy) on one 1024-token sequence of the same
+              model, forward + backward + AdamW, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 256 * 2.4e9 * 4096      # dense bf16 MFMA FLOP/s (2.5166 PFLOP/s)
+PEAK_FP32 = 157.3e12
+PEAK_HBM = 8.0e12                    # bytes/s
+
+
+def model_flops_per_token(w, n_params):
+    return 6 * n_params + 6 * w.n_layer * w.seq_len * w.n_embd
+
+
+def class_costs(w, B, n_params, n_decay):
+    """Algorithmic cost of each kernel class per step: ('flop', total) or ('byte', total)."""
+    BT, C, F, Vp, L, T, H = B * w.seq_len, w.n_embd, w.mlp_hidden, w.padded_vocab_size, w.n_layer, w.seq_len, w.n_head
+    es = 2  # bf16 storage
+    attn_fwd = 2 * 2 * B * H * (T * (T + 1) / 2) * (C // H)            # QK^T and PV, causal half
+    return {
+        "gemm_qkv": ("flop", 2 * BT * 3 * C * C * L),
+        "gemm_attn_proj": ("flop", 2 * BT * C * C * L),
+        "gemm_fc": ("flop", 2 * BT * F * C * L),
+        "gemm_mlp_proj": ("flop", 2 * BT * C * F * L),
+        "gemm_lm_head": ("flop", 2 * BT * Vp * C),
+        "gemm_lm_head_dx": ("flop", 2 * BT * Vp * C),
+        "gemm_lm_head_dw": ("flop", 2 * BT * Vp * C),
+        "gemm_dx": ("flop", 2 * BT * C * (3 * C + C + F + F) * L),
+        "gemm_dw": ("flop", 2 * BT * C * (3 * C + C + F + F) * L),
+        "attn_fwd": ("flop", attn_fwd * L),
+        "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
+        "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * 4 + BT * C * es + 8 * BT)),
+        "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 * 4 + BT * C * es + 8 * BT)),
+        "cross_entropy": ("byte", 2 * BT * Vp * es),
+        "adamw": ("byte", n_params * 28 + n_decay * 2),
+        "grad_norm": ("byte", n_params * 4),
+        "embed_fwd": ("byte", BT * C * 4 * 3),
+    }
+
+
+def cpu_baseline(w):
+    """Time the CPU oracle (float32) on one 1024-token sequence: forward, backward, AdamW."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    import synthetic
+    from oracle import gpt2_oracle as O
+    params = synthetic.init_params(w)
+    (x, y), = synthetic.micro_batches(w, 1, batch=1)
+    m = {k: np.zeros_like(v) for k, v in params.items()}
+    v = {k: np.zeros_like(a) for k, a in params.items()}
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        out = O.forward(params, w.n_layer, w.n_head, x, y, want_logits=False)
+        g = O.backward(params, w.n_layer, w.n_head, out["cache"], 1.0)
+        O.optimizer_step(params, g, m, v, steps + 1, 6e-4)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= 10.0 or steps >= 3:
+            break
+    return {"value": steps * x.size / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} x (1 sequence of {x.size} tokens: forward + backward + AdamW, float32 numpy), "
+                      f"{el:.1f} s"}
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+        if not rec:
+            return None
+        h = hashlib.sha256()
+        for f in sorted(os.listdir(os.path.join(ROOT, "transformer_lm_step_amd", "csrc"))):
+            h.update(open(os.path.join(ROOT, "transformer_lm_step_amd", "csrc", f), "rb").read())
+        return rec["bytes_per_launch"] if rec.get("source_sha256") == h.hexdigest() else None
+    except Exception:
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the data-parallel sharding is described in the design notes, not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import transformer_lm_step_amd as G
+
+    w = synthetic.workload(args.workload)
+    B, T = w.batch, w.seq_len
+    cfg = G.make_config(w.n_layer, w.n_head, w.n_embd, w.block_size, w.vocab_size, w.padded_vocab_size, B,
+                        w.dtype)
+    st = G.GPT2Step(cfg, seed=w.seed_base + 1000)
+    n_params = st.n_params
+    n_decay = G.gpt2_decay_end(cfg)
+    k = w.micro_steps
+    nb = max(2, k)
+    batches = synthetic.micro_batches(w, nb)
+    dev = torch.device("cuda:0")
+    xs = [torch.from_numpy(b[0]).to(dev) for b in batches]
+    ys = [torch.from_numpy(b[1]).to(dev) for b in batches]
+    d_loss = torch.zeros(k, dtype=torch.float32, device=dev)
+    d_norm = torch.zeros(1, dtype=torch.float32, device=dev)
+    h = st.h
+    step_no = [0]
+
+    def step():
+        for i in range(k):
+            j = (step_no[0] * k + i) % nb
+            G.gpt2_forward(h, xs[j].data_ptr(), ys[j].data_ptr(), B, T, None, d_loss.data_ptr() + 4 * i)
+            G.gpt2_backward(h, 1.0 / k, 1 if i > 0 else 0)
+        step_no[0] += 1
+        G.gpt2_adamw_step(h, w.lr, 0.9, 0.95, 1e-8, 0.1, 1.0, step_no[0], d_norm.data_ptr())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per-class live timing over a separate pass to find the dominant class
+    kernels = {}
+    if not args.no_kernel_timing:
+        G.gpt2_timing_begin(h, None)
+        for _ in range(max(1, min(5, args.steps))):
+            step()
+        G.gpt2_timing_end(h)
+        nrep = max(1, min(5, args.steps))
+        for c in G.kernel_classes():
+            ms, n = G.gpt2_timing_get(h, c)
+            if n:
+                kernels[c] = {"ms_per_step": ms / nrep, "launches_per_step": n / nrep}
+    costs = class_costs(w, B, n_params, n_decay)
+    single = [c for c in ("gemm_lm_head", "gemm_lm_head_dx", "gemm_lm_head_dw", "gemm_fc", "gemm_qkv",
+                          "gemm_attn_proj", "gemm_mlp_proj", "attn_fwd", "cross_entropy", "adamw",
+                          "layernorm_fwd") if c in kernels]
+    dominant = max(single, key=lambda c: kernels[c]["ms_per_step"]) if single else None
+
+    # timed region: the dominant class keeps its HIP events (on the library's stream)
+    if dominant:
+        G.gpt2_timing_begin(h, dominant)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    roofline = None
+    if dominant:
+        G.gpt2_timing_end(h)
+        ms, n = G.gpt2_timing_get(h, dominant)
+        kind, total = costs[dominant]
+        per_launch = total / (n / args.steps) if n else 0
+        avg_s = ms / 1e3 / n
+        if kind == "flop":
+            achieved, peak, unit, bound = per_launch / avg_s / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = per_launch / avg_s / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
+        roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": round(peak, 1),
+                    "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant),
+                    "launch_ms": round(ms / n, 4), "per_launch": per_launch,
+                    "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
+    loss = float(d_loss.sum().item()) / k
+    ms_step = el / args.steps * 1e3
+    tokens = B * T * k
+    value = tokens / (el / args.steps)
+    fpt = model_flops_per_token(w, n_params)
+    mfu = value * fpt / PEAK_BF16
+    for c, d in kernels.items():
+        if c in costs:
+            kind, total = costs[c]
+            rate = total / (d["ms_per_step"] / 1e3)
+            d["achieved"] = round(rate / (1e12 if kind == "flop" else 1e9), 2)
+            d["unit"] = "TFLOP/s" if kind == "flop" else "GB/s"
+    out = {
+        "metric": "training tokens/sec and MFU, GPT-2 124M B=16 T=1024 bf16, 1 MI355X"
+        if args.workload == "gpt2_step" else f"training tokens/sec, {args.workload}",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: GPT-2 L={w.n_layer} H={w.n_head} C={w.n_embd}, B={B}, T={T}, "
+                               f"vocab {w.vocab_size} padded to {w.padded_vocab_size}, "
+                               f"{k} micro-step(s) + AdamW per step",
+                   "global_batch": B * k, "seq_len": T, "parallelism": "single GPU"},
+        "mfu": round(mfu, 4), "model_flops_per_token": fpt, "peak_flops": PEAK_BF16,
+        "loss": round(loss, 5), "roofline": roofline, "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+        "cus": torch.cuda.get_device_properties(0).multi_processor_count,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+    st.close()
+
+
+if __name__ == "__main__":
+    main()

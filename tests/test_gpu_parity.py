@@ -37,9 +37,12 @@ def _grads_cosine(st, ref_grads, bar=0.999):
     for k in ref_grads:
         if k.endswith("attn.c_attn.bias"):
             C = ref_grads[k].shape[0] // 3
-            # the key bias has zero gradient (softmax is shift invariant per query row):
-            # compare query and value parts, check the key part is at noise level
-            assert np.abs(g[k][C:2 * C]).max() <= 1e-4 * max(np.abs(g[k]).max(), 1e-30) + 1e-7, k
+            # The key bias has zero gradient (softmax is shift invariant per query row), so
+            # its cosine compares two noise vectors. Compare the query and value parts, and
+            # bound the key part: in bf16 it is the sum over B*T positions of bf16-rounded
+            # dK rows, each off by up to 2^-8 relative, which stays below 1e-2 of the
+            # tensor's largest entry at these sizes.
+            assert np.abs(g[k][C:2 * C]).max() <= 1e-2 * max(np.abs(g[k]).max(), 1e-30), k
             for sl in (slice(0, C), slice(2 * C, 3 * C)):
                 assert cosine(g[k][sl], ref_grads[k][sl]) >= bar, k
             continue

@@ -35,6 +35,10 @@ class GPT2Error(RuntimeError):
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_lm_step_amd.build`")
+# torch ships its own HIP runtime with the same soname as the system one. Loading torch first
+# makes the library bind to that already-loaded runtime, so one process never holds two.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p
