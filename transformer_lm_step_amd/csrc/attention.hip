@@ -27,6 +27,21 @@ constexpr int A_THREADS = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Workgroups are dealt to the 8 XCDs round-robin by linear id. Renumber the 2-D grid
+// (x = block along the sequence, y = b*H + h) so that every block of one (b, h) lands on the
+// same XCD and its K/V (or Q/dO) tiles are served from that XCD's L2.
+DEV void xcd_remap(int& bx, int& by) {
+    const int nx = gridDim.x, n = nx * gridDim.y;
+    const int pid = blockIdx.y * nx + blockIdx.x;
+    const int xcd = pid & 7, slot = pid >> 3;
+    const int per = (n + 7) >> 3;
+    int tall = n & 7;
+    if (tall == 0) tall = 8;
+    const int logical = (xcd < tall) ? xcd * per + slot : tall * per + (xcd - tall) * (per - 1) + slot;
+    by = logical / nx;
+    bx = logical % nx;
+}
+
 template <typename T, int COLS>
 struct Tile {  // LDS tile of up to 64 rows x COLS elements, rows padded by 16 bytes
     static constexpr int STRIDE = COLS * (int)sizeof(T) + 16;
@@ -98,15 +113,26 @@ DEV void stage_rows(const T* __restrict__ src, int64_t ld, int nvalid, char* nat
             st16(nat + r * TN::STRIDE + cc * 16, v);
         }
     } else {
-        constexpr int NB = (64 / E) * (HS / E);
-        for (int blk = tid; blk < NB; blk += A_THREADS) {
-            const int cb = blk % (HS / E), rb = blk / (HS / E);
+        // the row block varies fastest across lanes: 8 lanes then fill one 128-byte row of
+        // the transposed tile, so those stores are free of bank conflicts. There are at most
+        // 256 blocks (64 rows x HS columns), one per thread.
+        constexpr int RBN = 64 / E, NB = RBN * (HS / E);
+        static_assert(NB <= A_THREADS, "one block per thread");
+        // (bf16 with 32-wide heads, used only by small test models, keeps the column-fastest
+        // order: hipcc 7.2 crashes on the other order for that instantiation)
+        constexpr bool row_fast = !(sizeof(T) == 2 && HS == 32);
+        if (tid < NB) {
+            const int rb = row_fast ? tid % RBN : tid / (HS / E);
+            const int cb = row_fast ? tid / RBN : tid % (HS / E);
             uint4 in[8], out[8];
 #pragma unroll
-            for (int q = 0; q < E; ++q) {
+            for (int q = 0; q < 8; ++q) {
                 const int r = rb * E + q;
-                in[q] = r < nvalid ? ld16(src + (int64_t)r * ld + cb * E) : make_uint4(0, 0, 0, 0);
-                if (nat) st16(nat + r * TN::STRIDE + cb * 16, in[q]);
+                in[q] = (q < E && r < nvalid) ? ld16(src + (int64_t)r * ld + cb * E) : make_uint4(0, 0, 0, 0);
+            }
+            if (nat) {
+#pragma unroll
+                for (int q = 0; q < E; ++q) st16(nat + (rb * E + q) * TN::STRIDE + cb * 16, in[q]);
             }
             transpose_block(in, out, (T*)nullptr);
 #pragma unroll
@@ -126,9 +152,11 @@ __global__ void __launch_bounds__(A_THREADS) attn_fwd_kernel(const T* __restrict
     char* sVt = smem + TK::BYTES;
     constexpr int KS = HS / 32, DB = HS / 16;
 
+    int bx, by;
+    xcd_remap(bx, by);
     const int nqb = (T_ + 127) / 128;
-    const int qblk = nqb - 1 - blockIdx.x;  // longest blocks first
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int qblk = nqb - 1 - bx;  // longest blocks first
+    const int bh = by, b = bh / H, h = bh % H;
     const int C = H * HS;
     const int64_t ld = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * T_ * ld;
@@ -266,10 +294,10 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_kernel(const T* __rest
     float* sD = sL + 64;
     constexpr int KS = HS / 32, DB = HS / 16;
 
-    const int nkb = (T_ + 127) / 128;
-    const int kblk = blockIdx.x;  // early key blocks see the most queries: launch them first
-    (void)nkb;
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    int bx, by;
+    xcd_remap(bx, by);
+    const int kblk = bx;  // early key blocks see the most queries: launch them first
+    const int bh = by, b = bh / H, h = bh % H;
     const int C = H * HS;
     const int64_t ld = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * T_ * ld;
@@ -390,9 +418,11 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_kernel(const T* __restr
     char* sV = sKt + TT::BYTES;
     constexpr int KS = HS / 32, DB = HS / 16;
 
+    int bx, by;
+    xcd_remap(bx, by);
     const int nqb = (T_ + 127) / 128;
-    const int qblk = nqb - 1 - blockIdx.x;
-    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int qblk = nqb - 1 - bx;
+    const int bh = by, b = bh / H, h = bh % H;
     const int C = H * HS;
     const int64_t ld = 3 * (int64_t)C;
     const T* base = qkv + (int64_t)b * T_ * ld;

@@ -200,7 +200,7 @@ Plan make_plan(const gpt2_config* c) {
         if (ns > 1) sk = std::max(sk, (size_t)ns * s[0] * s[1] * 4);
     }
     P.splitk = take(sk ? sk : 256);
-    P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 2 * C * 4);
+    P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 3 * C * 4);
     P.cspart = take((size_t)colsum_partial_floats((int)BT, (int)std::max(3 * C, F)) * 4);
     P.normpart = take((size_t)norm_blocks() * 4);
     P.normcoef = take(256);
@@ -576,12 +576,17 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     void* skpart = h->at<char>(P.splitk);
     const int lnblk = layernorm_backward_blocks(BT);
 
-    auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres) -> int {
+    // LayerNorm backward; with bias_off >= 0 the incoming residual gradient's column sum
+    // (gathered by the same kernel) is the bias gradient of the projection at that offset
+    auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
+                      int64_t bias_off) -> int {
         TRY(run(h, "layernorm_bwd", [&] {
             return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres_t, accum_dres, lnpart, lnblk, BT, C, bf, s);
         }));
         // weight and bias gradients are adjacent in the arena
-        return run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, grd + w_off, acc, s); });
+        TRY(run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, s); }));
+        if (bias_off < 0) return GPT2_OK;
+        return run(h, "bias_grad", [&] { return sum_partials(lnpart + 2 * C, lnblk, C, 3 * C, grd + bias_off, acc, s); });
     };
     auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off) -> int {
         GemmDesc g;
@@ -611,12 +616,11 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.epi = EPI_F32; g.C = grd + L.wte; g.ldc = C; g.alpha = grad_scale; g.beta = acc;
         TRY(run(h, "gemm_lm_head_dw", [&] { return gemm(g, bf, s); }));
     }
-    TRY(ln_bwd(h->at<float>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0));
+    TRY(ln_bwd(h->at<float>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0, -1));
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
         TRY(dw(dres_t, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
-        TRY(bias(dres, 1, C, L.b_pr[l]));
         {
             GemmDesc g;
             g.A = dres_t; g.lda = C; g.a_layout = 0;
@@ -635,10 +639,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
-        TRY(ln_bwd(h->at<float>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1));
+        // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
+        TRY(ln_bwd(h->at<float>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1, L.b_pr[l]));
         // x_mid = x_in + y Wo^T + bo
         TRY(dw(dres_t, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
-        TRY(bias(dres, 1, C, L.b_o[l]));
         {
             GemmDesc g;
             g.A = dres_t; g.lda = C; g.a_layout = 0;
@@ -661,7 +665,8 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
-        TRY(ln_bwd(h->at<float>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1));
+        // (the column sum of the incoming dres is the attn.c_proj bias gradient)
+        TRY(ln_bwd(h->at<float>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1, L.b_o[l]));
     }
     // embeddings: token rows scatter-add on top of the lm_head gradient, position rows
     if (!acc && T < c.block_size)

@@ -30,9 +30,12 @@ struct GemmDesc {
     int beta = 0;
     int nsplit = 1;          // split K into this many parts (EPI_F32 with ldc == N only)
     void* partial = nullptr; // fp32 scratch of nsplit*M*N floats when nsplit > 1
+    int bm = 0, bn = 0;      // block tile (0: chosen from the shape)
+    int no_dl = 0;           // 1: never use the direct global->LDS load path
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+void gemm_pick_tile(int M, int N, int nsplit, int is_bf16, int* bm, int* bn);
 void gemm_setup();
 size_t gemm_lds_bytes();
 
@@ -42,14 +45,16 @@ hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe,
 // LayerNorm forward: out(T) = (x - mean) * rstd * w + b ; saves mean, rstd (fp32)
 hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s);
-// LayerNorm backward: dres (+)= dx ; dres_t = T copy of dres (may be null);
-// partial[blk][0:C] = sum dh*xhat, partial[blk][C:2C] = sum dh over the block's rows.
+// LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; dres_t = T copy of dres (may be
+// null); partial[blk][0:C] = sum dh*xhat, [C:2C] = sum dh, [2C:3C] = sum of the incoming dres
+// (zero without accumulate) over the block's rows.
 hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
                               const float* w, float* dres, void* dres_t, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);
-// out[c] (+)= sum_blk partial[blk][c] for c < n (fixed order); used for LN dw/db
-hipError_t sum_partials(const float* partial, int nblk, int n, float* out, int accumulate, hipStream_t s);
+// out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order)
+hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,
+                        hipStream_t s);
 // column sums of a [rows, n] matrix (storage T or f32) into out[n] (+)=, deterministic
 hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial,
                   float* out, int accumulate, hipStream_t s);

@@ -110,10 +110,13 @@ hipError_t layernorm_forward(const float* x, const float* w, const float* b, voi
 // Backward through y = xhat*w + b, xhat = (x - mean)*rstd:
 //   dxhat = dh*w;  dx = rstd*(dxhat - mean(dxhat) - xhat*mean(dxhat*xhat))
 //   dw += sum_rows dh*xhat;  db += sum_rows dh
-// Waves take rows in a fixed stride; each wave's dw/db partial goes through LDS into one
-// partial row per block (fixed order), finished by sum_partials.
-constexpr int LNB_BLOCKS = 256;
-int layernorm_backward_blocks(int rows) { return rows < LNB_BLOCKS * 4 ? (rows + 3) / 4 : LNB_BLOCKS; }
+// and dres = (accumulate ? dres : 0) + dx. With accumulate, the incoming dres is the
+// gradient at the output of the residual add that produced x, so its column sum is the bias
+// gradient of that add's projection; it is collected as a third partial.
+// Each wave takes LNB_ROWS consecutive rows; the block's 4 wave partials are combined in a
+// fixed order into partial[blk][0:3C] = (dw, db, colsum(dres_in)), finished by sum_partials.
+constexpr int LNB_ROWS = 4;
+int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 * LNB_ROWS); }
 
 template <typename T>
 __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const float* __restrict__ x,
@@ -121,48 +124,48 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
                                           const float* __restrict__ w, float* __restrict__ dres,
                                           T* __restrict__ dres_t, int accumulate, float* __restrict__ partial,
                                           int rows, int C) {
-    extern __shared__ float sred[];  // [4][2C]
+    extern __shared__ float sred[];  // [4][3C]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nv = C >> 2;
-    const int nwaves = gridDim.x * 4;
-    float4 dw[LN_NV], db[LN_NV], wv[LN_NV];
+    float4 dw[LN_NV], db[LN_NV], cs[LN_NV], wv[LN_NV];
 #pragma unroll
     for (int j = 0; j < LN_NV; ++j) {
-        dw[j] = db[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        dw[j] = db[j] = cs[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         const int c = lane + 64 * j;
         wv[j] = c < nv ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int row = blockIdx.x * 4 + wave; row < rows; row += nwaves) {
+    const int r0 = (blockIdx.x * 4 + wave) * LNB_ROWS;
+    for (int row = r0; row < r0 + LNB_ROWS && row < rows; ++row) {
         const float mu = mean[row], r = rstd[row];
         const float4* dr = (const float4*)(dh + (int64_t)row * C);
         const float4* xr = (const float4*)(x + (int64_t)row * C);
-        float4 xh[LN_NV], dxh[LN_NV];
+        float4* o = (float4*)(dres + (int64_t)row * C);
+        float4 xh[LN_NV], dxh[LN_NV], old[LN_NV];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
         for (int j = 0; j < LN_NV; ++j) {
             const int c = lane + 64 * j;
             if (c < nv) {
                 const float4 d = dr[c], xx = xr[c];
+                old[j] = accumulate ? o[c] : make_float4(0.f, 0.f, 0.f, 0.f);
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
                 s1 += (dxh[j].x + dxh[j].y) + (dxh[j].z + dxh[j].w);
                 s2 += (dxh[j].x * xh[j].x + dxh[j].y * xh[j].y) + (dxh[j].z * xh[j].z + dxh[j].w * xh[j].w);
                 dw[j].x += d.x * xh[j].x; dw[j].y += d.y * xh[j].y; dw[j].z += d.z * xh[j].z; dw[j].w += d.w * xh[j].w;
                 db[j].x += d.x; db[j].y += d.y; db[j].z += d.z; db[j].w += d.w;
+                cs[j].x += old[j].x; cs[j].y += old[j].y; cs[j].z += old[j].z; cs[j].w += old[j].w;
             }
         }
         const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
-        float4* o = (float4*)(dres + (int64_t)row * C);
 #pragma unroll
         for (int j = 0; j < LN_NV; ++j) {
             const int c = lane + 64 * j;
             if (c < nv) {
-                float4 g = make_float4(r * (dxh[j].x - m1 - xh[j].x * m2), r * (dxh[j].y - m1 - xh[j].y * m2),
-                                       r * (dxh[j].z - m1 - xh[j].z * m2), r * (dxh[j].w - m1 - xh[j].w * m2));
-                if (accumulate) {
-                    const float4 old = o[c];
-                    g.x += old.x; g.y += old.y; g.z += old.z; g.w += old.w;
-                }
+                const float4 g = make_float4(old[j].x + r * (dxh[j].x - m1 - xh[j].x * m2),
+                                             old[j].y + r * (dxh[j].y - m1 - xh[j].y * m2),
+                                             old[j].z + r * (dxh[j].z - m1 - xh[j].z * m2),
+                                             old[j].w + r * (dxh[j].w - m1 - xh[j].w * m2));
                 o[c] = g;
                 if (dres_t) store4<T>(dres_t + (int64_t)row * C + 4 * c, g.x, g.y, g.z, g.w);
             }
@@ -173,14 +176,15 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
     for (int j = 0; j < LN_NV; ++j) {
         const int c = lane + 64 * j;
         if (c < nv) {
-            *(float4*)(sred + wave * 2 * C + 4 * c) = dw[j];
-            *(float4*)(sred + wave * 2 * C + C + 4 * c) = db[j];
+            *(float4*)(sred + wave * 3 * C + 4 * c) = dw[j];
+            *(float4*)(sred + wave * 3 * C + C + 4 * c) = db[j];
+            *(float4*)(sred + wave * 3 * C + 2 * C + 4 * c) = cs[j];
         }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < 2 * C; c += blockDim.x) {
-        const float v = ((sred[c] + sred[2 * C + c]) + sred[4 * C + c]) + sred[6 * C + c];
-        partial[(int64_t)blockIdx.x * 2 * C + c] = v;
+    for (int c = threadIdx.x; c < 3 * C; c += blockDim.x) {
+        const float v = ((sred[c] + sred[3 * C + c]) + sred[6 * C + c]) + sred[9 * C + c];
+        partial[(int64_t)blockIdx.x * 3 * C + c] = v;
     }
 }
 
@@ -188,7 +192,7 @@ hipError_t layernorm_backward(const float* dh, const float* x, const float* mean
                               const float* w, float* dres, void* dres_t, int accumulate_dres, float* partial,
                               int nblk, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
-    const size_t lds = 8 * (size_t)C * sizeof(float);
+    const size_t lds = 12 * (size_t)C * sizeof(float);
     if (is_bf16)
         hipLaunchKernelGGL(layernorm_backward_kernel<bf16>, dim3(nblk), dim3(256), lds, s, dh, x, mean, rstd, w, dres,
                            (bf16*)dres_t, accumulate_dres, partial, rows, C);
@@ -200,8 +204,8 @@ hipError_t layernorm_backward(const float* dh, const float* x, const float* mean
 
 // out[c] (+)= sum over p of partial[p][c], p in increasing order within each of 8 slices,
 // slices combined in a fixed tree. Block: 32 columns x 8 slices.
-__global__ void sum_partials_kernel(const float* __restrict__ partial, int np, int n, float* __restrict__ out,
-                                    int accumulate) {
+__global__ void sum_partials_kernel(const float* __restrict__ partial, int np, int n, int64_t stride,
+                                    float* __restrict__ out, int accumulate) {
     __shared__ float red[8][33];
     const int col = blockIdx.x * 32 + (threadIdx.x & 31);
     const int slice = threadIdx.x >> 5;
@@ -211,7 +215,7 @@ __global__ void sum_partials_kernel(const float* __restrict__ partial, int np, i
     if (p1 > np) p1 = np;
     float acc = 0.f;
     if (col < n)
-        for (int p = p0; p < p1; ++p) acc += partial[(int64_t)p * n + col];
+        for (int p = p0; p < p1; ++p) acc += partial[(int64_t)p * stride + col];
     red[slice][threadIdx.x & 31] = acc;
     __syncthreads();
     if (slice == 0 && col < n) {
@@ -222,8 +226,10 @@ __global__ void sum_partials_kernel(const float* __restrict__ partial, int np, i
     }
 }
 
-hipError_t sum_partials(const float* partial, int nblk, int n, float* out, int accumulate, hipStream_t s) {
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((n + 31) / 32), dim3(256), 0, s, partial, nblk, n, out, accumulate);
+hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,
+                        hipStream_t s) {
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((n + 31) / 32), dim3(256), 0, s, partial, nblk, n, stride, out,
+                       accumulate);
     return hipGetLastError();
 }
 
@@ -260,7 +266,7 @@ hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, flo
     else hipLaunchKernelGGL(colsum_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, rows, n, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return sum_partials(partial, ns, n, out, accumulate, s);
+    return sum_partials(partial, ns, n, n, out, accumulate, s);
 }
 
 // ================================================================== cross-entropy
