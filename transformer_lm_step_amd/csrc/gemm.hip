@@ -12,15 +12,15 @@
 // add, GELU derivative, gradient scaling/accumulation, split-K partials.
 //
 // Tiling: a 256-thread workgroup (4 waves in 2 x 2) owns a BM x BN output tile, each wave a
-// (BM/2) x (BN/2) sub-tile of 16x16 MFMA blocks. The block tile is 128x128, 256x128 or
-// 256x256: the larger the wave tile, the fewer LDS bytes each MFMA needs (LDS bandwidth, not
-// the matrix cores, bounds the small tile on CDNA4). K advances 128 bytes per step (64 bf16
-// / 32 fp32) through a double-buffered LDS stage whose rows are padded by 16 bytes, which
-// keeps the 16-byte fragment reads conflict-free. Operands that are not k-contiguous are
-// transposed in registers (8x8 bf16 / 4x4 fp32 blocks) on their way into LDS; the k block
-// varies fastest across lanes so 8 lanes write one whole 128-byte row. Workgroups are
-// renumbered so that each of the 8 XCDs (one L2 each) works on a contiguous, M-grouped range
-// of tiles.
+// (BM/2) x (BN/2) sub-tile of 16x16 MFMA blocks. Two paths:
+//  - LDS-streamed (bf16, whole 64-wide K tiles): both operands go from global memory straight
+//    into LDS in their stored orientation; fragments of mn-contiguous operands are read with
+//    the transposing LDS read of CDNA4. 128x128 tiles (two workgroups per CU) everywhere except
+//    the vocabulary-sized products, which take 256x256 (one per CU).
+//  - register-staged (fp32 check mode, ragged bf16 shapes): tiles pass through registers
+//    into a padded LDS stage; operands that are not k-contiguous are transposed in registers.
+// Workgroups are renumbered so that each of the 8 XCDs (one L2 each) works on a contiguous,
+// M-grouped range of tiles.
 #include <type_traits>
 
 #include "common.h"
@@ -156,6 +156,66 @@ DEV typename FragT<T>::type load_frag(const char* lds, int row, int kstep, int l
     }
 }
 
+// ---------------------------------------------------------------- epilogue
+// acc[i][j] holds, in lane l, rows mw + 16i + 4*(l>>4) + r (r = 0..3) of column
+// nw + 16j + (l & 15). CHECK = false for tiles wholly inside the matrix: straight-line code.
+template <typename T, int EPI, int FM, int FN, bool CHECK>
+DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int nw, int lane) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n = nw + j * 16 + (lane & 15);
+        const bool nok = !CHECK || n < p.N;
+        float bias = 0.f;
+        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
+            bias = (p.bias && nok) ? p.bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int mb = mw + i * 16 + (lane >> 4) * 4;
+            float extra[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = mb + r;
+                const bool ok = !CHECK || (nok && m < p.M);
+                extra[r] = 0.f;
+                if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                    if (ok) extra[r] = p.resid[(int64_t)m * p.ldr + n];
+                } else if constexpr (EPI == EPI_GELU_BWD) {
+                    if (ok) extra[r] = to_f<T>(((const T*)p.aux)[(int64_t)m * p.ldaux + n]);
+                } else if constexpr (EPI == EPI_F32) {
+                    if (ok && p.beta) extra[r] = ((const float*)p.C)[(int64_t)m * p.ldc + n];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = mb + r;
+                if (CHECK && !(nok && m < p.M)) continue;
+                const float v = acc[i][j][r];
+                const int64_t o = (int64_t)m * p.ldc + n;
+                if constexpr (EPI == EPI_BIAS_T) {
+                    ((T*)p.C)[o] = from_f<T>(p.alpha * v + bias);
+                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                    ((float*)p.C)[o] = extra[r] + v + bias;
+                } else if constexpr (EPI == EPI_BIAS_GELU) {
+                    const T u = from_f<T>(v + bias);
+                    ((T*)p.C)[o] = u;
+                    ((T*)p.C2)[o] = from_f<T>(gelu_f(to_f<T>(u)));
+                } else if constexpr (EPI == EPI_GELU_BWD) {
+                    ((T*)p.C)[o] = from_f<T>(v * gelu_grad_f(extra[r]));
+                } else if constexpr (EPI == EPI_F32) {
+                    ((float*)p.C)[o] = extra[r] + p.alpha * v;
+                } else {  // EPI_PARTIAL
+                    ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + o] = v;
+                }
+            }
+        }
+    }
+}
+template <typename T, int EPI, int FM, int FN>
+DEV void store_tile(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int nw, int lane, bool full) {
+    if (full) store_body<T, EPI, FM, FN, false>(p, acc, mw, nw, lane);
+    else store_body<T, EPI, FM, FN, true>(p, acc, mw, nw, lane);
+}
+
 template <typename T, int ALAY, int BLAY, int EPI, int BM, int BN>
 __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -228,259 +288,165 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
         __syncthreads();
     }
 
-    // ---------------------------------------------------------------- epilogue
-    // lane holds rows mb..mb+3 of column n for each (i, j) block
-    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n = n0 + wn * TN + j * 16 + (lane & 15);
-        const bool nok = full || n < p.N;
-        float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
-            bias = (p.bias && nok) ? p.bias[n] : 0.f;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int mb = m0 + wm * TM + i * 16 + (lane >> 4) * 4;
-            float extra[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb + r;
-                const bool ok = full || (nok && m < p.M);
-                extra[r] = 0.f;
-                if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    if (ok) extra[r] = p.resid[(int64_t)m * p.ldr + n];
-                } else if constexpr (EPI == EPI_GELU_BWD) {
-                    if (ok) extra[r] = to_f<T>(((const T*)p.aux)[(int64_t)m * p.ldaux + n]);
-                } else if constexpr (EPI == EPI_F32) {
-                    if (ok && p.beta) extra[r] = ((const float*)p.C)[(int64_t)m * p.ldc + n];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb + r;
-                const bool ok = full || (nok && m < p.M);
-                if (!ok) continue;
-                const float v = acc[i][j][r];
-                const int64_t o = (int64_t)m * p.ldc + n;
-                if constexpr (EPI == EPI_BIAS_T) {
-                    ((T*)p.C)[o] = from_f<T>(p.alpha * v + bias);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    ((float*)p.C)[o] = extra[r] + v + bias;
-                } else if constexpr (EPI == EPI_BIAS_GELU) {
-                    const T u = from_f<T>(v + bias);
-                    ((T*)p.C)[o] = u;
-                    ((T*)p.C2)[o] = from_f<T>(gelu_f(to_f<T>(u)));
-                } else if constexpr (EPI == EPI_GELU_BWD) {
-                    ((T*)p.C)[o] = from_f<T>(v * gelu_grad_f(extra[r]));
-                } else if constexpr (EPI == EPI_F32) {
-                    ((float*)p.C)[o] = extra[r] + p.alpha * v;
-                } else {  // EPI_PARTIAL
-                    ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + o] = v;
-                }
-            }
-        }
-    }
+    store_tile<T, EPI, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane, m0 + BM <= p.M && n0 + BN <= p.N);
 }
 
-// ====================================================================== direct-load path
-// bf16, A k-contiguous, K a multiple of 64. Tiles of k-contiguous operands go straight from
-// global memory into LDS with global_load_lds_dwordx4 (lane i of a wave writes LDS bytes
-// base + 16*i), so they cost no registers and no LDS-store instructions. The rows of such a
-// tile are 128 bytes, unpadded; the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7),
-// which keeps the 16-lane fragment reads free of bank conflicts. A transposed B operand
-// (the input-gradient products) still goes through registers into a padded [n][k] tile.
+// ====================================================================== LDS-streamed bf16 path
+// bf16 operands in either orientation, K a multiple of 64 per split. Each 64-k tile of an
+// operand goes straight from global memory into LDS with global_load_lds_dwordx4 (lane i of
+// a wave writes LDS bytes base + 16*i), in the orientation it has in global memory, so the
+// loads cost no registers, no LDS-store instructions and no transposes:
+//   k-contiguous operand, R rows:   LDS [R][64 k], 128-byte rows; the 16-byte chunk c of row
+//                                   r sits in slot c ^ ((r >> 1) & 7)
+//   mn-contiguous operand, R cols:  LDS [64 k][R], 2R-byte rows; the 16-byte chunk c of k-row
+//                                   k sits in slot c ^ (2 * ((k & 3) | ((k >> 3) & 1) << 2))
+// Each lane picks its global chunk so that the slot it writes holds the chunk the swizzle
+// puts there; a row is still read whole by 8 (or R/8) consecutive lanes. Fragments
+// (8 consecutive k of one row/column per lane) are read with ds_read_b128 from k-contiguous
+// tiles and with two ds_read_b64_tr_b16 from mn-contiguous tiles: within each 16-lane group
+// that instruction hands lane i element (i % 4) of the 8 bytes addressed by lane 4j + i/4 as
+// its j-th value, so when the group addresses 4 k-rows x 16 columns every lane receives 4
+// consecutive k of one column. Both swizzles make those reads free of bank conflicts.
 // Two stages: the loads of tile kt+1 are issued right after the barrier that opens the
-// multiplication of tile kt, and waited for before the next barrier; 68 KB of LDS per
-// workgroup leaves room for two workgroups per CU.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+// multiplication of tile kt and are waited for (vmcnt) before the next barrier.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_t;
+typedef __attribute__((address_space(3))) char* lds_char_t;
 
-constexpr int DL_BK = 64;                       // bf16 elements per K step (128 bytes)
-constexpr int DL_TILE = 128 * 128;              // bytes of a 128-row swizzled tile
-constexpr int DL_TILE_PAD = 128 * ROWB;         // bytes of a 128-row padded tile
+constexpr int MM_BK = 64;   // bf16 elements of K per tile (128 bytes)
 
 // s_waitcnt immediate waiting for vmcnt == 0 only (expcnt, lgkmcnt at their maxima)
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
-DEV int swz(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+DEV int swz_k(int r) { return (r >> 1) & 7; }
+DEV int swz_mn(int k) { return ((k & 3) | ((k >> 1) & 4)) << 1; }
 
-// One direct load: this wave's 64 lanes each move 16 bytes from their global address to
-// LDS address lds + 16 * lane. Written as inline asm (M0 and the load in one block, no
-// register results): the compiler then does not make every later LDS read wait for it; the
-// kernel orders the loads with explicit vmcnt waits and barriers instead. Loads the compiler
-// does not know about only make its own vmcnt waits stricter (the counter drains in order).
-DEV void dma16(const void* gaddr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gaddr) : "memory");
+// One direct load: the wave's 64 lanes each move 16 bytes from base + voff to LDS address
+// lds + 16 * lane. Inline asm (M0 and the load in one block, no register results), so the
+// compiler does not make later LDS reads wait for it; the kernel orders these loads with
+// explicit vmcnt waits and barriers. Loads the compiler does not track only make its own
+// vmcnt waits stricter (the counter drains in order).
+DEV void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 
-// issue the direct loads of one 128-row x 64-k tile: 4 wave-instructions per wave, each
-// covering 8 rows; lane l loads logical chunk (l & 7) ^ f(row) of row 8*(4w+i) + (l >> 3)
-DEV void dl_issue(const bf16* __restrict__ tile, const int (&off)[4], char* lds, int wave) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)(lds + wave * 4096));
+// byte offsets (from the tile's base address) of the R/32 direct loads one wave issues per
+// tile; rows/columns past the matrix edge are clamped (valid memory, outputs discarded)
+template <int LAY, int R>
+DEV void mm_offsets(uint32_t (&off)[R / 32], int64_t ld, int row0, int dim, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(tile + off[i], base + i * 1024);
+    for (int i = 0; i < R / 32; ++i) {
+        const int o = (wave * (R / 32) + i) * 64 + lane;   // 16-byte unit of the LDS tile
+        if constexpr (LAY == 0) {
+            const int r = o >> 3, c = (o & 7) ^ swz_k(r);
+            const int rr = min(row0 + r, dim - 1) - row0;
+            off[i] = (uint32_t)(rr * ld * 2 + c * 16);
+        } else {
+            constexpr int CPR = R / 8;
+            const int k = o / CPR, c = (o % CPR) ^ swz_mn(k);
+            const int col = min(row0 + c * 8, dim - 8) - row0;
+            off[i] = (uint32_t)(k * ld * 2 + col * 2);
+        }
+    }
 }
-DEV void dl_offsets(int (&off)[4], int64_t ld, int row0, int nrows, int wave, int lane) {
+template <int R>
+DEV void mm_issue(const void* base, const uint32_t (&off)[R / 32], uint32_t lds, int wave) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (4 * wave + i) + (lane >> 3);
-        int gr = row0 + r;
-        if (gr >= nrows) gr = nrows - 1;   // clamped rows: valid memory, outputs discarded
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        off[i] = (int)((gr - row0) * ld) + c * 8;
+    for (int i = 0; i < R / 32; ++i) dma16(base, off[i], lds + (wave * (R / 32) + i) * 1024);
+}
+// fragment of rows/columns rb..rb+15 with k = ks*32 + 8*(lane>>4) + 0..7
+template <int LAY, int R>
+DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
+    if constexpr (LAY == 0) {
+        const int r = rb + (lane & 15), c = ks * 4 + (lane >> 4);
+        return __builtin_bit_cast(bf16x8, ld16(t + r * 128 + ((c ^ swz_k(r)) << 4)));
+    } else {
+        const int g = lane >> 4, q = lane & 15;
+        const int col = rb + 4 * (q & 3), ch = col >> 3, within = (col & 7) * 2;
+        v4s h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int k = ks * 32 + 8 * g + 4 * hh + (q >> 2);
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4s_t)(lds_char_t)(t + k * (2 * R) + ((ch ^ swz_mn(k)) << 4) + within));
+        }
+        const v8s v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
     }
 }
 
-template <int BLAY, int EPI>
-__global__ void __launch_bounds__(GTHREADS, 2) gemm_dl_kernel(GemmArgs p, const bf16* __restrict__ Ap,
-                                                              const bf16* __restrict__ Bp) {
+template <int ALAY, int BLAY, int EPI, int BM, int BN>
+__global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_mm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    constexpr int BT = BLAY == 0 ? DL_TILE : DL_TILE_PAD;
-    constexpr int STAGE = DL_TILE + BT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int num_m = (p.M + 127) / 128, num_n = (p.N + 127) / 128;
+    constexpr int STAGE = (BM + BN) * 128;
+    constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
+    const int num_m = (p.M + BM - 1) / BM, num_n = (p.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(blockIdx.x, gridDim.x, num_m, num_n, tm, tn);
-    const int m0 = tm * 128, n0 = tn * 128;
+    const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.y * p.ksplit_len;
-    int kend = kbeg + p.ksplit_len;
-    if (kend > p.K) kend = p.K;
-    const int ntiles = kend > kbeg ? (kend - kbeg) / DL_BK : 0;
+    const int nt = min(p.ksplit_len, p.K - kbeg) / MM_BK;
 
-    const bf16* A = Ap + (int64_t)m0 * p.lda + kbeg;
-    int offA[4];
-    dl_offsets(offA, p.lda, m0, p.M, wave, lane);
-    int offB[4];
-    const bf16* Bd = Bp + (int64_t)n0 * p.ldb + kbeg;   // BLAY 0
-    TileLoader<bf16, 1, 128> lb;                                        // BLAY 1
-    if constexpr (BLAY == 0) dl_offsets(offB, p.ldb, n0, p.N, wave, lane);
+    uint32_t offA[BM / 32], offB[BN / 32];
+    mm_offsets<ALAY, BM>(offA, p.lda, m0, p.M, wave, lane);
+    mm_offsets<BLAY, BN>(offB, p.ldb, n0, p.N, wave, lane);
+    // tile kt of each operand starts at base + kt * step (bytes)
+    const char* baseA = (const char*)p.A + 2 * (ALAY == 0 ? (int64_t)m0 * p.lda + kbeg : (int64_t)kbeg * p.lda + m0);
+    const char* baseB = (const char*)p.B + 2 * (BLAY == 0 ? (int64_t)n0 * p.ldb + kbeg : (int64_t)kbeg * p.ldb + n0);
+    const int64_t stepA = ALAY == 0 ? 2 * MM_BK : 2 * MM_BK * p.lda;
+    const int64_t stepB = BLAY == 0 ? 2 * MM_BK : 2 * MM_BK * p.ldb;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t)smem;
 
-    floatx4 acc[4][4];
+    floatx4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // issue the loads of tile kt into the stage at byte offset ST (compile-time, so the
-    // compiler sees that a stage being filled is never the one being read)
-    auto issue = [&](auto st_c, int kt) {
-        constexpr int ST = decltype(st_c)::value;
-        dl_issue(A + kt * DL_BK, offA, smem + ST, wave);
-        if constexpr (BLAY == 0) dl_issue(Bd + kt * DL_BK, offB, smem + ST + DL_TILE, wave);
-        else lb.template load<false>(Bp, p.ldb, n0, p.N, kbeg + kt * DL_BK, kend, tid);
-    };
-    // multiply the tile in stage CUR while the next tile (if any) loads into stage NXT
-    auto step = [&](auto cur_c, auto nxt_c, int kt) {
-        constexpr int CUR = decltype(cur_c)::value, NXT = decltype(nxt_c)::value;
-        // tile kt is in LDS once this wave's loads have landed and every wave has passed
-        // the barrier; a bare barrier keeps the compiler from draining later prefetches
+    if (nt > 0) {
+        mm_issue<BM>(baseA, offA, lds0, wave);
+        mm_issue<BN>(baseB, offB, lds0 + BM * 128, wave);
+    }
+    for (int kt = 0; kt < nt; ++kt) {
+        // tile kt is in LDS once this wave's loads have landed and every wave has passed the
+        // barrier, which also retires every read of the stage refilled next; a bare barrier
+        // (no fence) keeps the prefetch below in flight
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        if (kt + 1 < ntiles) issue(nxt_c, kt + 1);
-        const char* a_s = smem + CUR;
-        const char* b_s = smem + CUR + DL_TILE;
+        if (kt + 1 < nt) {
+            const uint32_t st = lds0 + ((kt + 1) & 1) * STAGE;
+            mm_issue<BM>(baseA + (kt + 1) * stepA, offA, st, wave);
+            mm_issue<BN>(baseB + (kt + 1) * stepB, offB, st + BM * 128, wave);
+        }
+        const char* As = smem + (kt & 1) * STAGE;
+        const char* Bs = As + BM * 128;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 af[4], bfr[4];
+            bf16x8 af[FM], bfr[FN];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = __builtin_bit_cast(bf16x8, ld16(a_s + swz(wm * 64 + i * 16 + (lane & 15), ks * 4 + (lane >> 4))));
+            for (int i = 0; i < FM; ++i) af[i] = mm_frag<ALAY, BM>(As, wm * TM + 16 * i, ks, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn * 64 + j * 16 + (lane & 15);
-                if constexpr (BLAY == 0) bfr[j] = __builtin_bit_cast(bf16x8, ld16(b_s + swz(r, ks * 4 + (lane >> 4))));
-                else bfr[j] = load_frag<bf16>(b_s, r, ks, lane);
-            }
+            for (int j = 0; j < FN; ++j) bfr[j] = mm_frag<BLAY, BN>(Bs, wn * TN + 16 * j, ks, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mma8(acc[i][j], af[i], bfr[j]);
-        }
-        if constexpr (BLAY == 1) {
-            if (kt + 1 < ntiles) {
-                // the transposed B tile of kt+1 goes through registers into the other stage,
-                // which no wave reads before the next barrier
-                __builtin_amdgcn_s_waitcnt(kWaitVm0);
-                lb.store(smem + NXT + DL_TILE, tid);
-            }
-        }
-    };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, STAGE>;
-    if (ntiles > 0) {
-        issue(S0{}, 0);
-        if constexpr (BLAY == 1) {
-            __builtin_amdgcn_s_waitcnt(kWaitVm0);
-            lb.store(smem + DL_TILE, tid);
+                for (int j = 0; j < FN; ++j) mma8(acc[i][j], af[i], bfr[j]);
         }
     }
-    for (int kt = 0; kt < ntiles; kt += 2) {
-        step(S0{}, S1{}, kt);
-        if (kt + 1 < ntiles) step(S1{}, S0{}, kt + 1);
-    }
-
-    // ---------------------------------------------------------------- epilogue
-    const bool full = m0 + 128 <= p.M && n0 + 128 <= p.N;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int n = n0 + wn * 64 + j * 16 + (lane & 15);
-        const bool nok = full || n < p.N;
-        float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
-            bias = (p.bias && nok) ? p.bias[n] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int mb = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
-            float extra[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb + r;
-                const bool ok = full || (nok && m < p.M);
-                extra[r] = 0.f;
-                if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    if (ok) extra[r] = p.resid[(int64_t)m * p.ldr + n];
-                } else if constexpr (EPI == EPI_GELU_BWD) {
-                    if (ok) extra[r] = to_f<bf16>(((const bf16*)p.aux)[(int64_t)m * p.ldaux + n]);
-                } else if constexpr (EPI == EPI_F32) {
-                    if (ok && p.beta) extra[r] = ((const float*)p.C)[(int64_t)m * p.ldc + n];
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mb + r;
-                const bool ok = full || (nok && m < p.M);
-                if (!ok) continue;
-                const float v = acc[i][j][r];
-                const int64_t o = (int64_t)m * p.ldc + n;
-                if constexpr (EPI == EPI_BIAS_T) {
-                    ((bf16*)p.C)[o] = from_f<bf16>(p.alpha * v + bias);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    ((float*)p.C)[o] = extra[r] + v + bias;
-                } else if constexpr (EPI == EPI_BIAS_GELU) {
-                    const bf16 u = from_f<bf16>(v + bias);
-                    ((bf16*)p.C)[o] = u;
-                    ((bf16*)p.C2)[o] = from_f<bf16>(gelu_f(to_f<bf16>(u)));
-                } else if constexpr (EPI == EPI_GELU_BWD) {
-                    ((bf16*)p.C)[o] = from_f<bf16>(v * gelu_grad_f(extra[r]));
-                } else if constexpr (EPI == EPI_F32) {
-                    ((float*)p.C)[o] = extra[r] + p.alpha * v;
-                } else {  // EPI_PARTIAL
-                    ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + o] = v;
-                }
-            }
-        }
-    }
+    store_tile<bf16, EPI, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane, m0 + BM <= p.M && n0 + BN <= p.N);
 }
 
-template <int BLAY>
-constexpr size_t dl_lds_bytes() { return 2 * (size_t)(DL_TILE + (BLAY == 0 ? DL_TILE : DL_TILE_PAD)); }
+template <int BM, int BN>
+constexpr size_t mm_lds_bytes() { return 2 * (size_t)(BM + BN) * 128; }
 
-template <int BLAY, int EPI>
-static hipError_t launch_dl(const GemmArgs& a, int nsplit, hipStream_t s) {
-    const int num_m = (a.M + 127) / 128, num_n = (a.N + 127) / 128;
+template <int ALAY, int BLAY, int EPI, int BM, int BN>
+static hipError_t launch_mm(const GemmArgs& a, int nsplit, hipStream_t s) {
+    const int num_m = (a.M + BM - 1) / BM, num_n = (a.N + BN - 1) / BN;
     dim3 grid(num_m * num_n, nsplit);
-    gemm_dl_kernel<BLAY, EPI><<<grid, dim3(GTHREADS), dl_lds_bytes<BLAY>(), s>>>(a, (const bf16*)a.A, (const bf16*)a.B);
+    gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN><<<grid, dim3(GTHREADS), mm_lds_bytes<BM, BN>(), s>>>(a);
     return hipGetLastError();
 }
 
@@ -504,19 +470,17 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit,
     *(float4*)(out + i4) = o;
 }
 
-size_t gemm_lds_bytes() { return lds_bytes<256, 256>(); }
+size_t gemm_lds_bytes() { return mm_lds_bytes<256, 256>(); }
 
-// Tile choice. 256x128 and 256x256 tiles (one workgroup per CU) measured slower than
-// 128x128 (two per CU) on every shape of the step, so 128x128 is the default; the larger
-// tiles stay available through GemmDesc::bm/bn.
+// Tile of the register-staged path (fp32, and bf16 shapes the LDS-streamed path does not
+// take): always 128x128.
 void gemm_pick_tile(int M, int N, int nsplit, int is_bf16, int* bm, int* bn) {
-    const long cus = 256;
-    auto tiles = [&](int tm, int tn) { return (long)((M + tm - 1) / tm) * ((N + tn - 1) / tn) * nsplit; };
+    (void)M;
+    (void)N;
+    (void)nsplit;
+    (void)is_bf16;
     *bm = 128;
     *bn = 128;
-    (void)tiles;
-    (void)cus;
-    (void)is_bf16;
 }
 
 template <typename T, int ALAY, int BLAY, int EPI, int BM, int BN>
@@ -529,11 +493,23 @@ static hipError_t launch(const GemmArgs& a, int nsplit, hipStream_t s) {
 
 template <typename T, int ALAY, int BLAY, int EPI>
 static hipError_t launch_tiled(const GemmArgs& a, int nsplit, int bm, int bn, hipStream_t s) {
-    if constexpr (sizeof(T) == 2) {
-        if (bm == 256 && bn == 256) return launch<T, ALAY, BLAY, EPI, 256, 256>(a, nsplit, s);
-        if (bm == 256 && bn == 128) return launch<T, ALAY, BLAY, EPI, 256, 128>(a, nsplit, s);
-    }
+    (void)bm;
+    (void)bn;
     return launch<T, ALAY, BLAY, EPI, 128, 128>(a, nsplit, s);
+}
+
+// Shapes the LDS-streamed path takes: whole 64-wide K tiles in every split, leading
+// dimensions and mn-contiguous extents in multiples of 8 elements, 16-byte aligned bases,
+// and per-lane tile offsets that fit in 32 bits.
+static bool mm_ok(const GemmDesc& d, int ksplit_len) {
+    if (d.K % MM_BK || ksplit_len % MM_BK || d.lda % 8 || d.ldb % 8) return false;
+    if (((uintptr_t)d.A | (uintptr_t)d.B) & 15) return false;
+    if (d.a_layout == 1 && (d.M % 8 || d.M < 8)) return false;
+    if (d.b_layout == 1 && (d.N % 8 || d.N < 8)) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    for (int64_t ld : {d.lda, d.ldb})
+        if (255 * ld * 2 + 1024 >= lim) return false;
+    return true;
 }
 
 template <typename T>
@@ -559,21 +535,33 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     int bm = d.bm, bn = d.bn;
     if (bm == 0) gemm_pick_tile(d.M, d.N, nsplit, sizeof(T) == 2, &bm, &bn);
     hipError_t e = hipSuccess;
-    // direct-load path: bf16, A k-contiguous, every split a whole number of 64-wide K steps
-    const bool dl = sizeof(T) == 2 && d.a_layout == 0 && bm == 128 && bn == 128 && d.K % DL_BK == 0 &&
-                    a.ksplit_len % DL_BK == 0 && d.lda % 8 == 0 && (d.b_layout == 1 || d.ldb % 8 == 0) && !d.no_dl;
-    if (dl) {
-#define DL_CASE(BL, EP) if (d.b_layout == BL && epi == EP) e = launch_dl<BL, EP>(a, nsplit, s); else
-        DL_CASE(0, EPI_BIAS_T)
-        DL_CASE(0, EPI_BIAS_RESID_F32)
-        DL_CASE(0, EPI_BIAS_GELU)
-        DL_CASE(1, EPI_GELU_BWD)
-        DL_CASE(1, EPI_F32)
-        DL_CASE(1, EPI_BIAS_T)
-        DL_CASE(1, EPI_PARTIAL)
-        return hipErrorInvalidValue;
-#undef DL_CASE
-        goto reduce;
+    if constexpr (sizeof(T) == 2) {
+        if (!d.no_dl && mm_ok(d, a.ksplit_len)) {
+            // 256x256 tiles (one workgroup per CU) only pay off on the vocabulary-sized
+            // products; everything else runs 128x128 tiles, two workgroups per CU
+            const bool big = d.bm ? d.bm == 256
+                                  : d.M >= 256 && d.N >= 256 &&
+                                        ((int64_t)d.M * d.N >= (1LL << 28) || (d.K >= 32768 && nsplit == 1));
+#define MM_CASE(AL, BL, EP)                                                                   \
+    if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 128>(a, nsplit, s); else
+#define MM_CASE_BIG(AL, BL, EP)                                                               \
+    if (big && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 256, 256>(a, nsplit, s); else
+            MM_CASE_BIG(0, 0, EPI_BIAS_T)
+            MM_CASE_BIG(0, 1, EPI_F32)
+            MM_CASE(0, 0, EPI_BIAS_T)
+            MM_CASE(0, 0, EPI_BIAS_RESID_F32)
+            MM_CASE(0, 0, EPI_BIAS_GELU)
+            MM_CASE(0, 1, EPI_GELU_BWD)
+            MM_CASE(0, 1, EPI_F32)
+            MM_CASE(0, 1, EPI_BIAS_T)
+            MM_CASE(0, 1, EPI_PARTIAL)
+            MM_CASE(1, 1, EPI_F32)
+            MM_CASE(1, 1, EPI_PARTIAL)
+            return hipErrorInvalidValue;
+#undef MM_CASE
+#undef MM_CASE_BIG
+            goto reduce;
+        }
     }
 #define GEMM_CASE(AL, BL, EP) \
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_tiled<T, AL, BL, EP>(a, nsplit, bm, bn, s); else
@@ -614,21 +602,21 @@ static void set_lds() {
 template <typename T, int AL, int BL, int EP>
 static void set_lds_all() {
     set_lds<T, AL, BL, EP, 128, 128>();
-    if constexpr (sizeof(T) == 2) {
-        set_lds<T, AL, BL, EP, 256, 128>();
-        set_lds<T, AL, BL, EP, 256, 256>();
-    }
 }
 
-template <int BL, int EP>
-static void set_lds_dl() {
-    (void)hipFuncSetAttribute((const void*)gemm_dl_kernel<BL, EP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)dl_lds_bytes<BL>());
+template <int AL, int BL, int EP, int BM, int BN>
+static void set_lds_mm() {
+    (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<AL, BL, EP, BM, BN>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<BM, BN>());
 }
 
 void gemm_setup() {
-    set_lds_dl<0, EPI_BIAS_T>(); set_lds_dl<0, EPI_BIAS_RESID_F32>(); set_lds_dl<0, EPI_BIAS_GELU>();
-    set_lds_dl<1, EPI_GELU_BWD>(); set_lds_dl<1, EPI_F32>(); set_lds_dl<1, EPI_BIAS_T>(); set_lds_dl<1, EPI_PARTIAL>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 256, 256>(); set_lds_mm<0, 1, EPI_F32, 256, 256>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
+    set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
+    set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();
+    set_lds_mm<0, 1, EPI_PARTIAL, 128, 128>(); set_lds_mm<1, 1, EPI_F32, 128, 128>();
+    set_lds_mm<1, 1, EPI_PARTIAL, 128, 128>();
     // allow the dynamic LDS size (above the 64 KiB default) for every instantiation
 #define SETUP_T(T)                                                                                          \
     set_lds_all<T, 0, 0, EPI_BIAS_T>(); set_lds_all<T, 0, 0, EPI_BIAS_RESID_F32>();                        \
