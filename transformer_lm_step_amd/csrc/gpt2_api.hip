@@ -147,7 +147,7 @@ struct Plan {
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
     size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dres_t, dln, datt, dqkv, du, Dbuf;
-    size_t splitk, lnpart, cspart, normpart, normcoef, ebscratch;
+    size_t splitk, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
 };
 
 Plan make_plan(const gpt2_config* c) {
@@ -203,6 +203,7 @@ Plan make_plan(const gpt2_config* c) {
     P.splitk = take(sk ? sk : 256);
     P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 3 * C * 4);
     P.cspart = take((size_t)colsum_partial_floats((int)BT, (int)std::max(3 * C, F)) * 4);
+    P.sumscr = take((size_t)sum_scratch_floats((int)std::max(3 * C, F)) * 4);
     P.normpart = take((size_t)norm_blocks() * 4);
     P.normcoef = take(256);
     P.ebscratch = take(embed_backward_scratch_bytes((int)BT, (int)C));
@@ -574,6 +575,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     float* dln = h->at<float>(P.dln);
     float* lnpart = h->at<float>(P.lnpart);
     float* cspart = h->at<float>(P.cspart);
+    float* sumscr = h->at<float>(P.sumscr);
     void* skpart = h->at<char>(P.splitk);
     const int lnblk = layernorm_backward_blocks(BT);
 
@@ -585,9 +587,9 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres_t, accum_dres, lnpart, lnblk, BT, C, bf, s);
         }));
         // weight and bias gradients are adjacent in the arena
-        TRY(run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, s); }));
+        TRY(run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, sumscr, s); }));
         if (bias_off < 0) return GPT2_OK;
-        return run(h, "bias_grad", [&] { return sum_partials(lnpart + 2 * C, lnblk, C, 3 * C, grd + bias_off, acc, s); });
+        return run(h, "bias_grad", [&] { return sum_partials(lnpart + 2 * C, lnblk, C, 3 * C, grd + bias_off, acc, sumscr, s); });
     };
     auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off) -> int {
         GemmDesc g;
@@ -599,7 +601,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         return run(h, "gemm_dw", [&] { return gemm(g, bf, s); });
     };
     auto bias = [&](const void* dy, int dy_f32, int n, int64_t off) -> int {
-        return run(h, "bias_grad", [&] { return colsum(dy, dy_f32, bf, BT, n, cspart, grd + off, acc, s); });
+        return run(h, "bias_grad", [&] { return colsum(dy, dy_f32, bf, BT, n, cspart, grd + off, acc, sumscr, s); });
     };
 
     // lm_head: dhf = s dz wte ; dwte (+)= s dz^T hf   (dz = (softmax - onehot)/BT from the forward)

@@ -52,12 +52,14 @@ hipError_t layernorm_backward(const float* dh, const float* x, const float* mean
                               const float* w, float* dres, void* dres_t, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);
-// out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order)
+// out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order); scratch holds
+// sum_scratch_floats(n) floats
 hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,
-                        hipStream_t s);
+                        float* scratch, hipStream_t s);
+int sum_scratch_floats(int n);
 // column sums of a [rows, n] matrix (storage T or f32) into out[n] (+)=, deterministic
 hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial,
-                  float* out, int accumulate, hipStream_t s);
+                  float* out, int accumulate, float* scratch, hipStream_t s);
 int colsum_partial_floats(int rows, int n);
 
 // cross-entropy over rows of logits(T) [n_rows, Vp]: loss_rows[r] = lse - z[y]; logits are

@@ -118,18 +118,18 @@ hipError_t layernorm_forward(const float* x, const float* w, const float* b, voi
 constexpr int LNB_ROWS = 4;
 int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 * LNB_ROWS); }
 
-template <typename T>
-__global__ void layernorm_backward_kernel(const float* __restrict__ dh, const float* __restrict__ x,
-                                          const float* __restrict__ mean, const float* __restrict__ rstd,
-                                          const float* __restrict__ w, float* __restrict__ dres,
-                                          T* __restrict__ dres_t, int accumulate, float* __restrict__ partial,
-                                          int rows, int C) {
+// NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers
+template <typename T, int NV>
+__global__ void __launch_bounds__(256) layernorm_backward_kernel(
+    const float* __restrict__ dh, const float* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres, T* __restrict__ dres_t,
+    int accumulate, float* __restrict__ partial, int rows, int C) {
     extern __shared__ float sred[];  // [4][3C]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nv = C >> 2;
-    float4 dw[LN_NV], db[LN_NV], cs[LN_NV], wv[LN_NV];
+    float4 dw[NV], db[NV], cs[NV], wv[NV];
 #pragma unroll
-    for (int j = 0; j < LN_NV; ++j) {
+    for (int j = 0; j < NV; ++j) {
         dw[j] = db[j] = cs[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         const int c = lane + 64 * j;
         wv[j] = c < nv ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -140,14 +140,15 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
         const float4* dr = (const float4*)(dh + (int64_t)row * C);
         const float4* xr = (const float4*)(x + (int64_t)row * C);
         float4* o = (float4*)(dres + (int64_t)row * C);
-        float4 xh[LN_NV], dxh[LN_NV], old[LN_NV];
+        float4 xh[NV], dxh[NV], old[NV];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-        for (int j = 0; j < LN_NV; ++j) {
+        for (int j = 0; j < NV; ++j) {
             const int c = lane + 64 * j;
+            xh[j] = dxh[j] = old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < nv) {
                 const float4 d = dr[c], xx = xr[c];
-                old[j] = accumulate ? o[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+                if (accumulate) old[j] = o[c];
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
                 s1 += (dxh[j].x + dxh[j].y) + (dxh[j].z + dxh[j].w);
@@ -159,7 +160,7 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
         }
         const float m1 = wave_sum(s1) / (float)C, m2 = wave_sum(s2) / (float)C;
 #pragma unroll
-        for (int j = 0; j < LN_NV; ++j) {
+        for (int j = 0; j < NV; ++j) {
             const int c = lane + 64 * j;
             if (c < nv) {
                 const float4 g = make_float4(old[j].x + r * (dxh[j].x - m1 - xh[j].x * m2),
@@ -173,7 +174,7 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
     }
     // combine the 4 waves' partials in a fixed order
 #pragma unroll
-    for (int j = 0; j < LN_NV; ++j) {
+    for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
         if (c < nv) {
             *(float4*)(sred + wave * 3 * C + 4 * c) = dw[j];
@@ -188,48 +189,82 @@ __global__ void layernorm_backward_kernel(const float* __restrict__ dh, const fl
     }
 }
 
+template <typename T>
+static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const float* dh, const float* x,
+                                const float* mean, const float* rstd, const float* w, float* dres, T* dres_t,
+                                int acc, float* partial, int rows, int C) {
+#define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<T, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
+                                   dres, dres_t, acc, partial, rows, C)
+    if (nv4 <= 64) LNB(1);
+    else if (nv4 <= 128) LNB(2);
+    else if (nv4 <= 192) LNB(3);
+    else if (nv4 <= 256) LNB(4);
+    else LNB(8);
+#undef LNB
+    return hipGetLastError();
+}
+
 hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
                               const float* w, float* dres, void* dres_t, int accumulate_dres, float* partial,
                               int nblk, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     const size_t lds = 12 * (size_t)C * sizeof(float);
     if (is_bf16)
-        hipLaunchKernelGGL(layernorm_backward_kernel<bf16>, dim3(nblk), dim3(256), lds, s, dh, x, mean, rstd, w, dres,
-                           (bf16*)dres_t, accumulate_dres, partial, rows, C);
-    else
-        hipLaunchKernelGGL(layernorm_backward_kernel<float>, dim3(nblk), dim3(256), lds, s, dh, x, mean, rstd, w, dres,
-                           (float*)dres_t, accumulate_dres, partial, rows, C);
-    return hipGetLastError();
+        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, dh, x, mean, rstd, w, dres, (bf16*)dres_t,
+                                   accumulate_dres, partial, rows, C);
+    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, dh, x, mean, rstd, w, dres, (float*)dres_t,
+                                accumulate_dres, partial, rows, C);
 }
 
-// out[c] (+)= sum over p of partial[p][c], p in increasing order within each of 8 slices,
-// slices combined in a fixed tree. Block: 32 columns x 8 slices.
-__global__ void sum_partials_kernel(const float* __restrict__ partial, int np, int n, int64_t stride,
-                                    float* __restrict__ out, int accumulate) {
-    __shared__ float red[8][33];
-    const int col = blockIdx.x * 32 + (threadIdx.x & 31);
-    const int slice = threadIdx.x >> 5;
-    const int per = (np + 7) / 8;
-    const int p0 = slice * per;
-    int p1 = p0 + per;
-    if (p1 > np) p1 = np;
-    float acc = 0.f;
-    if (col < n)
-        for (int p = p0; p < p1; ++p) acc += partial[(int64_t)p * stride + col];
-    red[slice][threadIdx.x & 31] = acc;
+// Column sums of partial [np, n] (row stride `stride`), deterministic, in two launches:
+//  1. slice z of SUM_SLICES takes partial rows [z*per, (z+1)*per); a workgroup covers 64
+//     columns, its 4 waves take every 4th row (two running sums each) and are combined in a
+//     fixed order into scratch[z][col];
+//  2. out[col] (+)= sum_z scratch[z][col], z ascending.
+constexpr int SUM_SLICES = 16;
+int sum_scratch_floats(int n) { return SUM_SLICES * n; }
+
+__global__ void __launch_bounds__(256) colred1_kernel(const float* __restrict__ partial, int np, int n,
+                                                      int64_t stride, float* __restrict__ scratch) {
+    __shared__ float red[4][64];
+    const int col = blockIdx.x * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
+    const int per = (np + SUM_SLICES - 1) / SUM_SLICES;
+    const int p0 = blockIdx.y * per;
+    const int p1 = min(p0 + per, np);
+    float a0 = 0.f, a1 = 0.f;
+    if (col < n) {
+        int p = p0 + grp;
+        for (; p + 4 < p1; p += 8) {
+            a0 += partial[(int64_t)p * stride + col];
+            a1 += partial[(int64_t)(p + 4) * stride + col];
+        }
+        if (p < p1) a0 += partial[(int64_t)p * stride + col];
+    }
+    red[grp][threadIdx.x & 63] = a0 + a1;
     __syncthreads();
-    if (slice == 0 && col < n) {
-        const int c = threadIdx.x & 31;
-        const float v = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) +
-                        ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
-        out[col] = accumulate ? out[col] + v : v;
+    if (grp == 0 && col < n) {
+        const int c = threadIdx.x & 63;
+        scratch[(int64_t)blockIdx.y * n + col] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
     }
 }
 
-hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,
-                        hipStream_t s) {
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((n + 31) / 32), dim3(256), 0, s, partial, nblk, n, stride, out,
-                       accumulate);
+__global__ void __launch_bounds__(256) colred2_kernel(const float* __restrict__ scratch, int n,
+                                                      float* __restrict__ out, int accumulate) {
+    const int col = blockIdx.x * 256 + threadIdx.x;
+    if (col >= n) return;
+    float v = 0.f;
+#pragma unroll
+    for (int z = 0; z < SUM_SLICES; ++z) v += scratch[(int64_t)z * n + col];
+    out[col] = accumulate ? out[col] + v : v;
+}
+
+hipError_t sum_partials(const float* partial, int np, int n, int64_t stride, float* out, int accumulate,
+                        float* scratch, hipStream_t s) {
+    hipLaunchKernelGGL(colred1_kernel, dim3((n + 63) / 64, SUM_SLICES), dim3(256), 0, s, partial, np, n, stride,
+                       scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(colred2_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scratch, n, out, accumulate);
     return hipGetLastError();
 }
 
@@ -259,14 +294,14 @@ __global__ void colsum_kernel(const X* __restrict__ x, int rows, int n, float* _
 }
 
 hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial, float* out,
-                  int accumulate, hipStream_t s) {
+                  int accumulate, float* scratch, hipStream_t s) {
     const int ns = (rows + CS_SLICE_ROWS - 1) / CS_SLICE_ROWS;
     dim3 g((n + 255) / 256, ns);
     if (x_is_f32 || !is_bf16) hipLaunchKernelGGL(colsum_kernel<float>, g, dim3(256), 0, s, (const float*)x, rows, n, partial);
     else hipLaunchKernelGGL(colsum_kernel<bf16>, g, dim3(256), 0, s, (const bf16*)x, rows, n, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return sum_partials(partial, ns, n, n, out, accumulate, s);
+    return sum_partials(partial, ns, n, n, out, accumulate, scratch, s);
 }
 
 // ================================================================== cross-entropy
