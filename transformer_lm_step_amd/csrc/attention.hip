@@ -511,6 +511,414 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_kernel(const T* __restr
     }
 }
 
+// ================================================================== bf16, 64-wide heads
+// Streamed tiles: each 64-row x 64-column bf16 tile (128-byte rows) of K, V, Q or dO goes
+// from its strided rows in global memory straight into LDS by direct loads, two stages
+// deep, so the next chunk's tiles are in flight while the current chunk is multiplied.
+// Fragments whose k index runs along the tile's rows (V^T, Q^T, dO^T, K^T) come from the
+// transposing LDS read; its row choice per 16-lane group also produces the key/query order
+// of a fragment built from two 16x16 accumulator blocks, so no tile is ever transposed.
+// The 16-byte chunk c of row r sits in slot c ^ ts_swz(r), which keeps both the 16-byte row
+// reads (16 rows x one chunk) and the transposing reads (8 rows x 32 bytes per half-wave)
+// free of bank conflicts.
+constexpr int TS_BYTES = 64 * 128;
+
+DEV int ts_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+
+// this wave's share (rows 16w..16w+15) of a 64-row tile whose row r starts at src + r*ld;
+// rows >= nrows repeat the last valid row (finite values, masked out by the callers)
+DEV void ts_load(const bf16* src, int64_t ld, int nrows, uint32_t lds, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ ts_swz(r);
+        const int rr = min(r, nrows - 1);
+        dma16(src, (uint32_t)(rr * ld * 2 + c * 16), lds + (2 * wave + i) * 1024);
+    }
+}
+// rows rb..rb+15 (lane & 15), k = 32ks + 8(lane >> 4) + 0..7 along the row
+DEV bf16x8 ts_nat(const char* t, int rb, int ks, int lane) {
+    const int r = rb + (lane & 15), c = ks * 4 + (lane >> 4);
+    return __builtin_bit_cast(bf16x8, ld16(t + r * 128 + ((c ^ ts_swz(r)) << 4)));
+}
+// column cb + (lane & 15); values 0..3 from rows r0 + 4(lane >> 4) + j, 4..7 from rows
+// r1 + 4(lane >> 4) + j
+DEV bf16x8 ts_tr(const char* t, int cb, int r0, int r1, int lane) {
+    const int g = lane >> 4, q = lane & 15;
+    const int colx = cb + 4 * (q & 3), ch = colx >> 3, within = (colx & 7) * 2;
+    const int ra = r0 + 4 * g + (q >> 2), rb = r1 + 4 * g + (q >> 2);
+    return read_tr_pair(t + ra * 128 + ((ch ^ ts_swz(ra)) << 4) + within,
+                        t + rb * 128 + ((ch ^ ts_swz(rb)) << 4) + within);
+}
+DEV float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32: exp2(-inf) = 0
+
+__global__ void __launch_bounds__(A_THREADS) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+                                                                float* __restrict__ lse, int T_, int H, float sc) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
+    constexpr int HS = 64, STAGE = 2 * TS_BYTES;
+    int bx, by;
+    xcd_remap(bx, by);
+    const int nqb = (T_ + 127) / 128;
+    const int qblk = nqb - 1 - bx;  // longest blocks first
+    const int bh = by, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * T_ * ld;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+    const int col = lane & 15, g = lane >> 4;
+    const uint32_t lds0 = lds_addr(smem);
+
+    bf16x8 qf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            qf[qb][ks] = q < T_ ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+    }
+    floatx4 o[4][2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+
+    const int kend = min(q0 + 128, T_);
+    const int nchunk = (kend + 63) / 64;
+    const bool wave_live = qw0 < T_;
+    auto issue = [&](int c) {
+        const int k0 = c * 64, nv = min(64, T_ - k0);
+        const uint32_t st = lds0 + (c & 1) * STAGE;
+        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, st, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, st + TS_BYTES, wave, lane);
+    };
+    if (nchunk > 0) issue(0);
+    for (int c = 0; c < nchunk; ++c) {
+        dma_wait_barrier();
+        if (c + 1 < nchunk) issue(c + 1);
+        const int k0 = c * 64;
+        if (!wave_live || k0 > qw0 + 31) continue;
+        const char* sK = smem + (c & 1) * STAGE;
+        const char* sV = sK + TS_BYTES;
+        floatx4 s[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = s[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 kf = ts_nat(sK, kb * 16, ks, lane);
+                mma8(s[kb][0], kf, qf[0][ks]);
+                mma8(s[kb][1], kf, qf[1][ks]);
+            }
+        }
+        // online softmax in the log2 domain on raw scores: max first, then one fma + exp2
+        const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int q = qw0 + qb * 16 + col;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = s[kb][qb][i];
+                    if (need_mask) {
+                        const int key = k0 + kb * 16 + g * 4 + i;
+                        if (key > q || key >= T_) v = -INFINITY;
+                    }
+                    s[kb][qb][i] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = group4_max(mx) * sc;
+            const float mnew = fmaxf(mrun[qb], mx);
+            const float msafe = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = exp2_raw(mrun[qb] - msafe);
+            float ls = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = exp2_raw(fmaf(s[kb][qb][i], sc, -msafe));
+                    s[kb][qb][i] = p;
+                    ls += p;
+                }
+            lrun[qb] = lrun[qb] * alpha + ls;
+            mrun[qb] = mnew;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[d][qb] *= alpha;
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const bf16x8 p0 = frag_from_acc<bf16>(s[2 * st][0], s[2 * st + 1][0]);
+            const bf16x8 p1 = frag_from_acc<bf16>(s[2 * st][1], s[2 * st + 1][1]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const bf16x8 vf = ts_tr(sV, d * 16, 32 * st, 32 * st + 16, lane);
+                mma8(o[d][0], vf, p0);
+                mma8(o[d][1], vf, p1);
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        const float ltot = group4_sum(lrun[qb]);
+        if (q >= T_) continue;
+        const float inv = 1.0f / ltot;
+        bf16* yr = y + ((int64_t)b * T_ + q) * C + h * HS;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) store4v<bf16>(yr + d * 16 + g * 4, o[d][qb], inv);
+        if (g == 0) lse[(int64_t)bh * T_ + q] = (mrun[qb] + log2f(ltot)) * kLn2;
+    }
+}
+
+// dK, dV for 128 keys per workgroup (32 per wave), streaming 64-query chunks of Q, dO, lse, D.
+__global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
+                                                                    const bf16* __restrict__ dy,
+                                                                    const float* __restrict__ lse,
+                                                                    const float* __restrict__ D,
+                                                                    bf16* __restrict__ dqkv, int T_, int H, float sc,
+                                                                    float scale) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][Q | dO | lse | D]
+    constexpr int HS = 64, STAGE = 2 * TS_BYTES + 512;
+    int bx, by;
+    xcd_remap(bx, by);
+    const int kblk = bx;  // early key blocks see the most queries: launch them first
+    const int bh = by, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * T_ * ld;
+    const bf16* dyb = dy + (int64_t)b * T_ * C;
+    const float* lse_bh = lse + (int64_t)bh * T_;
+    const float* D_bh = D + (int64_t)bh * T_;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int k0 = kblk * 128, kw0 = k0 + wave * 32;
+    const uint32_t lds0 = lds_addr(smem);
+
+    bf16x8 kf[2][2], vf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + kb * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int64_t off = (int64_t)key * ld + h * HS + ks * 32 + g * 8;
+            kf[kb][ks] = key < T_ ? frag_global<bf16>(base + off + C) : frag_zero<bf16>();
+            vf[kb][ks] = key < T_ ? frag_global<bf16>(base + off + 2 * C) : frag_zero<bf16>();
+        }
+    }
+    floatx4 dk[4][2], dv[4][2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dk[d][kb] = dv[d][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int qc0 = k0 / 64, nqc = (T_ + 63) / 64;
+    const bool wave_live = kw0 < T_;
+    auto issue = [&](int qc) {
+        const int q0 = qc * 64, nv = min(64, T_ - q0);
+        const uint32_t st = lds0 + ((qc - qc0) & 1) * STAGE;
+        ts_load(base + (int64_t)q0 * ld + h * HS, ld, nv, st, wave, lane);
+        ts_load(dyb + (int64_t)q0 * C + h * HS, C, nv, st + TS_BYTES, wave, lane);
+        const uint32_t voff = (uint32_t)min(lane, nv - 1) * 4;
+        if (wave == 0) dma4(lse_bh + q0, voff, st + 2 * TS_BYTES);
+        if (wave == 1) dma4(D_bh + q0, voff, st + 2 * TS_BYTES + 256);
+    };
+    if (qc0 < nqc) issue(qc0);
+    for (int qc = qc0; qc < nqc; ++qc) {
+        dma_wait_barrier();
+        if (qc + 1 < nqc) issue(qc + 1);
+        const int q0 = qc * 64;
+        if (!wave_live || q0 + 63 < kw0) continue;
+        const char* sQ = smem + ((qc - qc0) & 1) * STAGE;
+        const char* sO = sQ + TS_BYTES;
+        const float* sL = (const float*)(sQ + 2 * TS_BYTES);
+        const float* sD = sL + 64;
+        floatx4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[qb][kb] = dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 qa = ts_nat(sQ, qb * 16, ks, lane);
+                const bf16x8 oa = ts_nat(sO, qb * 16, ks, lane);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma8(s[qb][kb], qa, kf[kb][ks]);
+                    mma8(dp[qb][kb], oa, vf[kb][ks]);
+                }
+            }
+        }
+        // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col
+        const bool need_mask = (q0 < kw0 + 32) || (q0 + 64 > T_);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ql = qb * 16 + g * 4 + i;
+                const int q = q0 + ql;
+                const float L = sL[ql] * kLog2e, Dq = sD[ql];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int key = kw0 + kb * 16 + col;
+                    float p = exp2_raw(fmaf(s[qb][kb][i], sc, -L));
+                    if (need_mask && !(key <= q && q < T_)) p = 0.f;
+                    s[qb][kb][i] = p;
+                    dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
+                }
+            }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bf16x8 pf[2], df[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                pf[kb] = frag_from_acc<bf16>(s[2 * st][kb], s[2 * st + 1][kb]);
+                df[kb] = frag_from_acc<bf16>(dp[2 * st][kb], dp[2 * st + 1][kb]);
+            }
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const bf16x8 oat = ts_tr(sO, d * 16, 32 * st, 32 * st + 16, lane);
+                const bf16x8 qat = ts_tr(sQ, d * 16, 32 * st, 32 * st + 16, lane);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    mma8(dv[d][kb], oat, pf[kb]);
+                    mma8(dk[d][kb], qat, df[kb]);
+                }
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + kb * 16 + col;
+        if (key >= T_) continue;
+        bf16* r = dqkv + ((int64_t)b * T_ + key) * ld + h * HS;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            store4v<bf16>(r + C + d * 16 + g * 4, dk[d][kb], scale);
+            store4v<bf16>(r + 2 * C + d * 16 + g * 4, dv[d][kb], 1.0f);
+        }
+    }
+}
+
+// dQ for 128 queries per workgroup (32 per wave), streaming 64-key chunks of K and V.
+__global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+                                                                   const bf16* __restrict__ dy,
+                                                                   const float* __restrict__ lse,
+                                                                   const float* __restrict__ D,
+                                                                   bf16* __restrict__ dqkv, int T_, int H, float sc,
+                                                                   float scale) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
+    constexpr int HS = 64, STAGE = 2 * TS_BYTES;
+    int bx, by;
+    xcd_remap(bx, by);
+    const int nqb = (T_ + 127) / 128;
+    const int qblk = nqb - 1 - bx;
+    const int bh = by, b = bh / H, h = bh % H;
+    const int C = H * HS;
+    const int64_t ld = 3 * (int64_t)C;
+    const bf16* base = qkv + (int64_t)b * T_ * ld;
+    const bf16* dyb = dy + (int64_t)b * T_ * C;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+    const uint32_t lds0 = lds_addr(smem);
+
+    bf16x8 qf[2][2], of[2][2];
+    float L[2], Dq[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        const bool ok = q < T_;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            qf[qb][ks] = ok ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+            of[qb][ks] = ok ? frag_global<bf16>(dyb + (int64_t)q * C + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+        }
+        L[qb] = ok ? lse[(int64_t)bh * T_ + q] * kLog2e : 0.f;
+        Dq[qb] = ok ? D[(int64_t)bh * T_ + q] : 0.f;
+    }
+    floatx4 dq[4][2];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dq[d][0] = dq[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int kend = min(q0 + 128, T_);
+    const int nchunk = (kend + 63) / 64;
+    const bool wave_live = qw0 < T_;
+    auto issue = [&](int c) {
+        const int k0 = c * 64, nv = min(64, T_ - k0);
+        const uint32_t st = lds0 + (c & 1) * STAGE;
+        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, st, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, st + TS_BYTES, wave, lane);
+    };
+    if (nchunk > 0) issue(0);
+    for (int c = 0; c < nchunk; ++c) {
+        dma_wait_barrier();
+        if (c + 1 < nchunk) issue(c + 1);
+        const int k0 = c * 64;
+        if (!wave_live || k0 > qw0 + 31) continue;
+        const char* sK = smem + (c & 1) * STAGE;
+        const char* sV = sK + TS_BYTES;
+        floatx4 s[4][2], dp[4][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 ka = ts_nat(sK, kb * 16, ks, lane);
+                const bf16x8 va = ts_nat(sV, kb * 16, ks, lane);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    mma8(s[kb][qb], ka, qf[qb][ks]);
+                    mma8(dp[kb][qb], va, of[qb][ks]);
+                }
+            }
+        }
+        // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col
+        const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q = qw0 + qb * 16 + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = k0 + kb * 16 + g * 4 + i;
+                    float p = exp2_raw(fmaf(s[kb][qb][i], sc, -L[qb]));
+                    if (need_mask && !(key <= q && key < T_)) p = 0.f;
+                    dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
+                }
+            }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const bf16x8 d0 = frag_from_acc<bf16>(dp[2 * st][0], dp[2 * st + 1][0]);
+            const bf16x8 d1 = frag_from_acc<bf16>(dp[2 * st][1], dp[2 * st + 1][1]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const bf16x8 kat = ts_tr(sK, d * 16, 32 * st, 32 * st + 16, lane);
+                mma8(dq[d][0], kat, d0);
+                mma8(dq[d][1], kat, d1);
+            }
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int q = qw0 + qb * 16 + col;
+        if (q >= T_) continue;
+        bf16* r = dqkv + ((int64_t)b * T_ + q) * ld + h * HS;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) store4v<bf16>(r + d * 16 + g * 4, dq[d][qb], scale);
+    }
+}
+
+constexpr size_t ts_fwd_lds() { return 2 * 2 * TS_BYTES; }
+constexpr size_t ts_dkv_lds() { return 2 * (2 * TS_BYTES + 512); }
+
 template <typename T, int HS> constexpr size_t fwd_lds() { return Tile<T, HS>::BYTES + Tile<T, 64>::BYTES; }
 template <typename T, int HS> constexpr size_t dkv_lds() { return 2 * (Tile<T, HS>::BYTES + Tile<T, 64>::BYTES) + 128 * sizeof(float); }
 template <typename T, int HS> constexpr size_t dq_lds() { return 2 * Tile<T, HS>::BYTES + Tile<T, 64>::BYTES; }
@@ -519,7 +927,10 @@ template <typename T, int HS>
 static hipError_t fwd_launch(const void* qkv, void* y, float* lse, int B, int T_, int H, hipStream_t s) {
     const float sc = kLog2e / sqrtf((float)HS);
     dim3 grid((T_ + 127) / 128, B * H);
-    attn_fwd_kernel<T, HS><<<grid, dim3(A_THREADS), fwd_lds<T, HS>(), s>>>((const T*)qkv, (T*)y, lse, T_, H, sc);
+    if constexpr (sizeof(T) == 2 && HS == 64)
+        attn_fwd_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (bf16*)y, lse, T_, H, sc);
+    else
+        attn_fwd_kernel<T, HS><<<grid, dim3(A_THREADS), fwd_lds<T, HS>(), s>>>((const T*)qkv, (T*)y, lse, T_, H, sc);
     return hipGetLastError();
 }
 
@@ -534,6 +945,17 @@ static hipError_t bwd_launch(const void* qkv, const void* y, const void* dy, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 grid((T_ + 127) / 128, B * H);
+    if constexpr (sizeof(T) == 2 && HS == 64) {
+        attn_bwd_dkv_ts_kernel<<<grid, dim3(A_THREADS), ts_dkv_lds(), s>>>((const bf16*)qkv, (const bf16*)dy, lse,
+                                                                          (const float*)D, (bf16*)dqkv, T_, H, sc,
+                                                                          scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        attn_bwd_dq_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (const bf16*)dy, lse,
+                                                                         (const float*)D, (bf16*)dqkv, T_, H, sc,
+                                                                         scale);
+        return hipGetLastError();
+    }
     attn_bwd_dkv_kernel<T, HS><<<grid, dim3(A_THREADS), dkv_lds<T, HS>(), s>>>((const T*)qkv, (const T*)dy, lse,
                                                                               (const float*)D, (T*)dqkv, T_, H, sc, scale);
     e = hipGetLastError();
@@ -568,6 +990,9 @@ void attention_setup() {
     (void)hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<T, HS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds<T, HS>());
     ASET(bf16, 64) ASET(bf16, 32) ASET(float, 64) ASET(float, 32)
 #undef ASET
+    (void)hipFuncSetAttribute((const void*)attn_fwd_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dq_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dkv_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_dkv_lds());
 }
 
 }  // namespace gpt2k

@@ -145,3 +145,46 @@ DEV float gelu_grad_f(float u) {
     const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
     return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluC * (1.0f + 3.0f * kGeluA * u * u);
 }
+
+// ------------------------------------------------------------------ direct global->LDS loads
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_t;
+typedef __attribute__((address_space(3))) char* lds_char_t;
+
+// s_waitcnt immediate waiting for vmcnt == 0 only (expcnt, lgkmcnt at their maxima)
+constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+
+// LDS byte address of a shared-memory pointer
+DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_char_t)(p); }
+
+// One direct load: the wave's 64 lanes each move 16 bytes from base + voff to LDS address
+// lds + 16 * lane (global_load_lds_dwordx4; base and lds wave-uniform). Inline asm (M0 and
+// the load in one block, no register results), so the compiler does not make later LDS reads
+// wait for it; kernels order these loads with explicit vmcnt waits and barriers. Loads the
+// compiler does not track only make its own vmcnt waits stricter (the counter drains in order).
+DEV void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+// the same with 4 bytes per lane (LDS address lds + 4 * lane)
+DEV void dma4(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+}
+// wait for this wave's direct loads, then a bare barrier (no fence: a fence would also drain
+// loads issued for later tiles). Afterwards every wave's loads issued before it have landed
+// and every wave's earlier LDS reads have completed.
+DEV void dma_wait_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Two transposing LDS reads (ds_read_b64_tr_b16) joined into one 8-value fragment. Within
+// each 16-lane group the instruction gives lane i, as its j-th value, element (i % 4) of the
+// 8 bytes addressed by lane 4j + i/4 of the group. When the group's lanes address 4 rows
+// (lane >> 2) x 4 consecutive 4-element column pieces (lane & 3) of a row-major tile, lane i
+// receives column i of those 4 rows: the first read gives values 0..3, the second 4..7.
+DEV bf16x8 read_tr_pair(const char* p0, const char* p1) {
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(lds_char_t)p0);
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t)(lds_char_t)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}

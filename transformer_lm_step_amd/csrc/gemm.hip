@@ -309,27 +309,10 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
 // consecutive k of one column. Both swizzles make those reads free of bank conflicts.
 // Two stages: the loads of tile kt+1 are issued right after the barrier that opens the
 // multiplication of tile kt and are waited for (vmcnt) before the next barrier.
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4s* lds_v4s_t;
-typedef __attribute__((address_space(3))) char* lds_char_t;
-
 constexpr int MM_BK = 64;   // bf16 elements of K per tile (128 bytes)
-
-// s_waitcnt immediate waiting for vmcnt == 0 only (expcnt, lgkmcnt at their maxima)
-constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 
 DEV int swz_k(int r) { return (r >> 1) & 7; }
 DEV int swz_mn(int k) { return ((k & 3) | ((k >> 1) & 4)) << 1; }
-
-// One direct load: the wave's 64 lanes each move 16 bytes from base + voff to LDS address
-// lds + 16 * lane. Inline asm (M0 and the load in one block, no register results), so the
-// compiler does not make later LDS reads wait for it; the kernel orders these loads with
-// explicit vmcnt waits and barriers. Loads the compiler does not track only make its own
-// vmcnt waits stricter (the counter drains in order).
-DEV void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
-}
 
 // byte offsets (from the tile's base address) of the R/32 direct loads one wave issues per
 // tile; rows/columns past the matrix edge are clamped (valid memory, outputs discarded)
@@ -364,15 +347,9 @@ DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
     } else {
         const int g = lane >> 4, q = lane & 15;
         const int col = rb + 4 * (q & 3), ch = col >> 3, within = (col & 7) * 2;
-        v4s h[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int k = ks * 32 + 8 * g + 4 * hh + (q >> 2);
-            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4s_t)(lds_char_t)(t + k * (2 * R) + ((ch ^ swz_mn(k)) << 4) + within));
-        }
-        const v8s v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, v);
+        const int k0 = ks * 32 + 8 * g + (q >> 2), k1 = k0 + 4;
+        return read_tr_pair(t + k0 * (2 * R) + ((ch ^ swz_mn(k0)) << 4) + within,
+                            t + k1 * (2 * R) + ((ch ^ swz_mn(k1)) << 4) + within);
     }
 }
 
@@ -398,7 +375,7 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
     const char* baseB = (const char*)p.B + 2 * (BLAY == 0 ? (int64_t)n0 * p.ldb + kbeg : (int64_t)kbeg * p.ldb + n0);
     const int64_t stepA = ALAY == 0 ? 2 * MM_BK : 2 * MM_BK * p.lda;
     const int64_t stepB = BLAY == 0 ? 2 * MM_BK : 2 * MM_BK * p.ldb;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t)smem;
+    const uint32_t lds0 = lds_addr(smem);
 
     floatx4 acc[FM][FN];
 #pragma unroll
@@ -414,8 +391,7 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
         // tile kt is in LDS once this wave's loads have landed and every wave has passed the
         // barrier, which also retires every read of the stage refilled next; a bare barrier
         // (no fence) keeps the prefetch below in flight
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        dma_wait_barrier();
         if (kt + 1 < nt) {
             const uint32_t st = lds0 + ((kt + 1) & 1) * STAGE;
             mm_issue<BM>(baseA + (kt + 1) * stepA, offA, st, wave);
