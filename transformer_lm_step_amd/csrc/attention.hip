@@ -552,7 +552,7 @@ DEV bf16x8 ts_tr(const char* t, int cb, int r0, int r1, int lane) {
 }
 DEV float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32: exp2(-inf) = 0
 
-__global__ void __launch_bounds__(A_THREADS) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+__global__ void __launch_bounds__(A_THREADS, 2) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
                                                                 float* __restrict__ lse, int T_, int H, float sc) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
     constexpr int HS = 64, STAGE = 2 * TS_BYTES;
@@ -674,7 +674,7 @@ __global__ void __launch_bounds__(A_THREADS) attn_fwd_ts_kernel(const bf16* __re
 }
 
 // dK, dV for 128 keys per workgroup (32 per wave), streaming 64-query chunks of Q, dO, lse, D.
-__global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
+__global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
                                                                     const bf16* __restrict__ dy,
                                                                     const float* __restrict__ lse,
                                                                     const float* __restrict__ D,
@@ -805,7 +805,7 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_ts_kernel(const bf16* 
 }
 
 // dQ for 128 queries per workgroup (32 per wave), streaming 64-key chunks of K and V.
-__global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+__global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
                                                                    const float* __restrict__ D,

@@ -132,18 +132,18 @@ DEV void st16(void* p, const uint4& v) { *(uint4*)p = v; }
 // 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) and its derivative.
 constexpr float kGeluC = 0.7978845608028654f;  // sqrt(2/pi)
 constexpr float kGeluA = 0.044715f;
-DEV float tanh_fast(float w) {
-    // tanh(w) = 1 - 2/(exp(2w)+1), exact enough in fp32 and saturating for large |w|
-    const float e = __expf(2.0f * w);
-    return 1.0f - 2.0f / (e + 1.0f);
+// GELU-tanh through the logistic function: with w = c (u + a u^3) and s = 1 / (1 + e^{-2w}),
+//   0.5 (1 + tanh w) = s   and   1 - tanh^2 w = 4 s (1 - s), so
+//   gelu(u) = u s,   gelu'(u) = s + 2 u s (1 - s) c (1 + 3 a u^2).
+// One v_exp_f32 and one v_rcp_f32 (about 1 ulp each); saturates cleanly for large |u|.
+DEV float gelu_sigmoid(float u) {
+    const float w2 = -2.0f * 1.4426950408889634f * kGeluC * (u + kGeluA * u * u * u);   // -2w log2(e)
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w2));
 }
-DEV float gelu_f(float u) {
-    const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
-    return 0.5f * u * (1.0f + t);
-}
+DEV float gelu_f(float u) { return u * gelu_sigmoid(u); }
 DEV float gelu_grad_f(float u) {
-    const float t = tanh_fast(kGeluC * (u + kGeluA * u * u * u));
-    return 0.5f * (1.0f + t) + 0.5f * u * (1.0f - t * t) * kGeluC * (1.0f + 3.0f * kGeluA * u * u);
+    const float sg = gelu_sigmoid(u);
+    return sg + 2.0f * u * sg * (1.0f - sg) * kGeluC * (1.0f + 3.0f * kGeluA * u * u);
 }
 
 // ------------------------------------------------------------------ direct global->LDS loads

@@ -15,8 +15,7 @@
 // (BM/2) x (BN/2) sub-tile of 16x16 MFMA blocks. Two paths:
 //  - LDS-streamed (bf16, whole 64-wide K tiles): both operands go from global memory straight
 //    into LDS in their stored orientation; fragments of mn-contiguous operands are read with
-//    the transposing LDS read of CDNA4. 128x128 tiles (two workgroups per CU) everywhere except
-//    the vocabulary-sized products, which take 256x256 (one per CU).
+//    the transposing LDS read of CDNA4. 128x128 or 128x192 tiles, two workgroups per CU.
 //  - register-staged (fp32 check mode, ragged bf16 shapes): tiles pass through registers
 //    into a padded LDS stage; operands that are not k-contiguous are transposed in registers.
 // Workgroups are renumbered so that each of the 8 XCDs (one L2 each) works on a contiguous,
@@ -44,6 +43,7 @@ struct GemmArgs {
     float alpha;
     int beta;                   // 1: add into the fp32 output
     int64_t part_stride;        // split-K partial stride (elements)
+    int vec;                    // 1: full tiles may use 8/16-byte epilogue accesses
 };
 
 template <int BM, int BN>
@@ -313,6 +313,19 @@ constexpr int MM_BK = 64;   // bf16 elements of K per tile (128 bytes)
 
 DEV int swz_k(int r) { return (r >> 1) & 7; }
 DEV int swz_mn(int k) { return ((k & 3) | ((k >> 1) & 4)) << 1; }
+// slot of 16-byte chunk ch in k-row k of an mn-contiguous tile with R columns (R/8 chunks):
+// the XOR stays inside aligned groups of 16 chunks; a trailing group of 8 (R = 192) uses
+// the low 3 bits of the swizzle only
+template <int R>
+DEV int mn_slot(int ch, int k) {
+    constexpr int CPR = R / 8;
+    if constexpr (CPR % 16 == 0) {
+        return ch ^ swz_mn(k);
+    } else {
+        const int base = ch & ~15;
+        return base + ((ch & 15) ^ (swz_mn(k) & (base + 16 <= CPR ? 15 : 7)));
+    }
+}
 
 // byte offsets (from the tile's base address) of the R/32 direct loads one wave issues per
 // tile; rows/columns past the matrix edge are clamped (valid memory, outputs discarded)
@@ -327,7 +340,7 @@ DEV void mm_offsets(uint32_t (&off)[R / 32], int64_t ld, int row0, int dim, int 
             off[i] = (uint32_t)(rr * ld * 2 + c * 16);
         } else {
             constexpr int CPR = R / 8;
-            const int k = o / CPR, c = (o % CPR) ^ swz_mn(k);
+            const int k = o / CPR, c = mn_slot<R>(o % CPR, k);   // mn_slot is an involution
             const int col = min(row0 + c * 8, dim - 8) - row0;
             off[i] = (uint32_t)(k * ld * 2 + col * 2);
         }
@@ -348,13 +361,101 @@ DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
         const int g = lane >> 4, q = lane & 15;
         const int col = rb + 4 * (q & 3), ch = col >> 3, within = (col & 7) * 2;
         const int k0 = ks * 32 + 8 * g + (q >> 2), k1 = k0 + 4;
-        return read_tr_pair(t + k0 * (2 * R) + ((ch ^ swz_mn(k0)) << 4) + within,
-                            t + k1 * (2 * R) + ((ch ^ swz_mn(k1)) << 4) + within);
+        return read_tr_pair(t + k0 * (2 * R) + (mn_slot<R>(ch, k0) << 4) + within,
+                            t + k1 * (2 * R) + (mn_slot<R>(ch, k1) << 4) + within);
+    }
+}
+
+// Epilogue of the LDS-streamed path. Its MFMAs take B as the first operand, so acc[i][j] is a
+// block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
+// n = nw + 16j + 4(l >> 4) + r, r = 0..3 -- one 16-byte (fp32) or 8-byte (bf16) access per
+// block and lane on full tiles.
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    bf16x4 o;
+    o[0] = (bf16)a; o[1] = (bf16)b; o[2] = (bf16)c; o[3] = (bf16)d;
+    return o;
+}
+template <int EPI, int FM, int FN, bool CHECK>
+DEV void store_t_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int nw, int lane) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int n0 = nw + 16 * j + 4 * (lane >> 4);
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU) {
+            if (p.bias) {
+                if constexpr (!CHECK) {
+                    const float4 b4 = *(const float4*)(p.bias + n0);
+                    bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bias[r] = n0 + r < p.N ? p.bias[n0 + r] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = mw + 16 * i + (lane & 15);
+            const floatx4 v = acc[i][j];
+            const int64_t o = (int64_t)m * p.ldc + n0;
+            if constexpr (!CHECK) {
+                if constexpr (EPI == EPI_BIAS_T) {
+                    *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(p.alpha * v[0] + bias[0], p.alpha * v[1] + bias[1],
+                                                           p.alpha * v[2] + bias[2], p.alpha * v[3] + bias[3]);
+                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                    const float4 rr = *(const float4*)(p.resid + (int64_t)m * p.ldr + n0);
+                    *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0] + bias[0], rr.y + v[1] + bias[1],
+                                                              rr.z + v[2] + bias[2], rr.w + v[3] + bias[3]);
+                } else if constexpr (EPI == EPI_BIAS_GELU) {
+                    const bf16x4 u = to_bf16x4(v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]);
+                    *(bf16x4*)((bf16*)p.C + o) = u;
+                    *(bf16x4*)((bf16*)p.C2 + o) = to_bf16x4(gelu_f((float)u[0]), gelu_f((float)u[1]),
+                                                            gelu_f((float)u[2]), gelu_f((float)u[3]));
+                } else if constexpr (EPI == EPI_GELU_BWD) {
+                    const bf16x4 a = *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n0);
+                    *(bf16x4*)((bf16*)p.C + o) =
+                        to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
+                                  v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
+                } else if constexpr (EPI == EPI_F32) {
+                    float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (p.beta) old = *(const float4*)((const float*)p.C + o);
+                    *(float4*)((float*)p.C + o) = make_float4(old.x + p.alpha * v[0], old.y + p.alpha * v[1],
+                                                              old.z + p.alpha * v[2], old.w + p.alpha * v[3]);
+                } else {  // EPI_PARTIAL
+                    *(float4*)((float*)p.C + (int64_t)blockIdx.y * p.part_stride + o) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                if (m >= p.M) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = n0 + r;
+                    if (n >= p.N) continue;
+                    const int64_t e = o + r;
+                    if constexpr (EPI == EPI_BIAS_T) {
+                        ((bf16*)p.C)[e] = (bf16)(p.alpha * v[r] + bias[r]);
+                    } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                        ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + n] + v[r] + bias[r];
+                    } else if constexpr (EPI == EPI_BIAS_GELU) {
+                        const bf16 u = (bf16)(v[r] + bias[r]);
+                        ((bf16*)p.C)[e] = u;
+                        ((bf16*)p.C2)[e] = (bf16)gelu_f((float)u);
+                    } else if constexpr (EPI == EPI_GELU_BWD) {
+                        const float a = (float)((const bf16*)p.aux)[(int64_t)m * p.ldaux + n];
+                        ((bf16*)p.C)[e] = (bf16)(v[r] * gelu_grad_f(a));
+                    } else if constexpr (EPI == EPI_F32) {
+                        const float old = p.beta ? ((const float*)p.C)[e] : 0.f;
+                        ((float*)p.C)[e] = old + p.alpha * v[r];
+                    } else {  // EPI_PARTIAL
+                        ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + e] = v[r];
+                    }
+                }
+            }
+        }
     }
 }
 
 template <int ALAY, int BLAY, int EPI, int BM, int BN>
-__global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_mm_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(GTHREADS, (BM * BN >= 256 * 128) ? 1 : 2) gemm_mm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
@@ -409,10 +510,13 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) mma8(acc[i][j], af[i], bfr[j]);
+                for (int j = 0; j < FN; ++j) mma8(acc[i][j], bfr[j], af[i]);
         }
     }
-    store_tile<bf16, EPI, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane, m0 + BM <= p.M && n0 + BN <= p.N);
+    if (p.vec && m0 + BM <= p.M && n0 + BN <= p.N)
+        store_t_body<EPI, FM, FN, false>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
+    else
+        store_t_body<EPI, FM, FN, true>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
 }
 
 template <int BM, int BN>
@@ -446,7 +550,7 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit,
     *(float4*)(out + i4) = o;
 }
 
-size_t gemm_lds_bytes() { return mm_lds_bytes<256, 256>(); }
+size_t gemm_lds_bytes() { return mm_lds_bytes<128, 192>(); }
 
 // Tile of the register-staged path (fp32, and bf16 shapes the LDS-streamed path does not
 // take): always 128x128.
@@ -502,6 +606,12 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     const int per = (ktiles + nsplit - 1) / nsplit;
     nsplit = (ktiles + per - 1) / per;
     a.ksplit_len = per * BK;
+    {
+        // vector epilogue accesses need 4-element-aligned rows and 16-byte aligned bases
+        auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+        a.vec = d.ldc % 4 == 0 && d.ldr % 4 == 0 && d.ldaux % 4 == 0 && al(d.C) && al(d.C2) && al(d.bias) &&
+                al(d.resid) && al(d.aux) && al(d.partial);
+    }
     int epi = d.epi;
     if (nsplit > 1) {
         // partials, then a fixed-order reduce into the fp32 output
@@ -513,17 +623,31 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     hipError_t e = hipSuccess;
     if constexpr (sizeof(T) == 2) {
         if (!d.no_dl && mm_ok(d, a.ksplit_len)) {
-            // 256x256 tiles (one workgroup per CU) only pay off on the vocabulary-sized
-            // products; everything else runs 128x128 tiles, two workgroups per CU
-            const bool big = d.bm ? d.bm == 256
-                                  : d.M >= 256 && d.N >= 256 &&
-                                        ((int64_t)d.M * d.N >= (1LL << 28) || (d.K >= 32768 && nsplit == 1));
+            // 128x192 tiles (wave tile 64x96: fewer LDS bytes per MFMA) whenever N is a multiple
+            // of 192 and they fill whole rounds of 512 workgroups (two per CU) about as well as
+            // 128x128 tiles: N = 768 gives 512 tiles instead of 768, N = 2304 three rounds
+            // instead of 4.5, N = 50304 = 262 x 192. 256x256 tiles measured slower everywhere.
+            bool wide = false;
+            if (d.bn) {
+                wide = d.bn == 192;
+            } else if (nsplit == 1 && d.N % 192 == 0) {
+                auto fill = [&](int bn) {
+                    const int64_t blocks = (int64_t)((d.M + 127) / 128) * ((d.N + bn - 1) / bn);
+                    const int64_t rounds = (blocks + 511) / 512;
+                    return (double)blocks / (double)(rounds * 512);
+                };
+                wide = fill(192) >= fill(128) - 0.02;
+            }
 #define MM_CASE(AL, BL, EP)                                                                   \
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 128>(a, nsplit, s); else
-#define MM_CASE_BIG(AL, BL, EP)                                                               \
-    if (big && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 256, 256>(a, nsplit, s); else
-            MM_CASE_BIG(0, 0, EPI_BIAS_T)
-            MM_CASE_BIG(0, 1, EPI_F32)
+#define MM_CASE_WIDE(AL, BL, EP)                                                              \
+    if (wide && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 192>(a, nsplit, s); else
+            MM_CASE_WIDE(0, 0, EPI_BIAS_T)
+            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID_F32)
+            MM_CASE_WIDE(0, 1, EPI_F32)
+            MM_CASE_WIDE(0, 1, EPI_BIAS_T)
+            MM_CASE_WIDE(0, 0, EPI_BIAS_GELU)
+            MM_CASE_WIDE(0, 1, EPI_GELU_BWD)
             MM_CASE(0, 0, EPI_BIAS_T)
             MM_CASE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE(0, 0, EPI_BIAS_GELU)
@@ -535,7 +659,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE(1, 1, EPI_PARTIAL)
             return hipErrorInvalidValue;
 #undef MM_CASE
-#undef MM_CASE_BIG
+#undef MM_CASE_WIDE
             goto reduce;
         }
     }
@@ -587,7 +711,9 @@ static void set_lds_mm() {
 }
 
 void gemm_setup() {
-    set_lds_mm<0, 0, EPI_BIAS_T, 256, 256>(); set_lds_mm<0, 1, EPI_F32, 256, 256>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 192>();
+    set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
+    set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();

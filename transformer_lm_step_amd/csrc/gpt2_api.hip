@@ -127,14 +127,14 @@ bool tensor_info(const gpt2_config* c, int i, std::string* name, int64_t* off, i
     return false;
 }
 
-// split-K factor of a weight-gradient product: about two 128x128 workgroups per CU (every
-// extra split adds M*N*4 bytes of partials to write and reduce), at least 4 K-tiles per
-// split, at most 16 splits
+// split-K factor of a weight-gradient product: as many splits as fit in one round of two
+// 128x128 workgroups per CU (a partial second round would take as long as the first; every
+// split also adds M*N*4 bytes of partials), at least 4 K-tiles per split, at most 16 splits
 int choose_split(int M, int N, int K, bool bf16) {
     const int BK = bf16 ? 64 : 32;
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int ktiles = (K + BK - 1) / BK;
-    int s = (512 + tiles - 1) / tiles;
+    int s = 512 / tiles;
     if (s > 16) s = 16;
     if (s > ktiles / 4) s = ktiles / 4;
     if (s < 1) s = 1;
