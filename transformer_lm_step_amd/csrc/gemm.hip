@@ -651,6 +651,8 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(0, 1, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_BIAS_GELU)
             MM_CASE_WIDE(0, 1, EPI_GELU_BWD)
+            MM_CASE_WIDE(1, 1, EPI_PARTIAL)
+            MM_CASE_WIDE(1, 1, EPI_F32)
             MM_CASE(0, 0, EPI_BIAS_T)
             MM_CASE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE(0, 0, EPI_BIAS_GELU)
@@ -717,6 +719,7 @@ void gemm_setup() {
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
+    set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();

@@ -127,18 +127,37 @@ bool tensor_info(const gpt2_config* c, int i, std::string* name, int64_t* off, i
     return false;
 }
 
-// split-K factor of a weight-gradient product: as many splits as fit in one round of two
-// 128x128 workgroups per CU (a partial second round would take as long as the first; every
-// split also adds M*N*4 bytes of partials), at least 4 K-tiles per split, at most 16 splits
-int choose_split(int M, int N, int K, bool bf16) {
+// Split-K factor and tile width of a weight-gradient product (M x N, K = tokens): as many
+// splits as fit in one round of 512 workgroups (two per CU; a partial second round would take
+// as long as the first, and every split adds M*N*4 bytes of partials), at least 4 K-tiles per
+// split, at most 16 splits. 128x192 tiles are taken when they fill the round better.
+struct Split {
+    int ns = 1, bn = 128;
+};
+Split choose_split(int M, int N, int K, bool bf16) {
     const int BK = bf16 ? 64 : 32;
-    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     const int ktiles = (K + BK - 1) / BK;
-    int s = 512 / tiles;
-    if (s > 16) s = 16;
-    if (s > ktiles / 4) s = ktiles / 4;
-    if (s < 1) s = 1;
-    return s;
+    auto pick = [&](int bn, double* fill) {
+        const int tiles = ((M + 127) / 128) * ((N + bn - 1) / bn);
+        int s = 512 / tiles;
+        if (s > 16) s = 16;
+        if (s > ktiles / 4) s = ktiles / 4;
+        if (s < 1) s = 1;
+        const int64_t blocks = (int64_t)tiles * s, rounds = (blocks + 511) / 512;
+        *fill = (double)blocks / (double)(rounds * 512);
+        return s;
+    };
+    Split r;
+    double f128 = 0.0, f192 = 0.0;
+    r.ns = pick(128, &f128);
+    if (bf16 && N % 192 == 0) {
+        const int s192 = pick(192, &f192);
+        if (f192 > f128 + 0.01) {
+            r.ns = s192;
+            r.bn = 192;
+        }
+    }
+    return r;
 }
 
 struct Plan {
@@ -197,7 +216,7 @@ Plan make_plan(const gpt2_config* c) {
     size_t sk = 0;
     const int shapes[4][2] = {{(int)(3 * C), (int)C}, {(int)C, (int)C}, {(int)F, (int)C}, {(int)C, (int)F}};
     for (auto& s : shapes) {
-        const int ns = choose_split(s[0], s[1], (int)BT, bf);
+        const int ns = choose_split(s[0], s[1], (int)BT, bf).ns;
         if (ns > 1) sk = std::max(sk, (size_t)ns * s[0] * s[1] * 4);
     }
     P.splitk = take(sk ? sk : 256);
@@ -586,10 +605,13 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         TRY(run(h, "layernorm_bwd", [&] {
             return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres_t, accum_dres, lnpart, lnblk, BT, C, bf, s);
         }));
-        // weight and bias gradients are adjacent in the arena
-        TRY(run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, sumscr, s); }));
-        if (bias_off < 0) return GPT2_OK;
-        return run(h, "bias_grad", [&] { return sum_partials(lnpart + 2 * C, lnblk, C, 3 * C, grd + bias_off, acc, sumscr, s); });
+        // LayerNorm weight and bias gradients are adjacent in the arena; the third partial
+        // (column sums of the incoming residual gradient) is the projection bias gradient
+        if (bias_off < 0)
+            return run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, sumscr, s); });
+        return run(h, "ln_param_grad", [&] {
+            return sum_partials2(lnpart, lnblk, 3 * C, 3 * C, grd + w_off, 2 * C, grd + bias_off, acc, sumscr, s);
+        });
     };
     auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off) -> int {
         GemmDesc g;
@@ -597,7 +619,8 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.B = x; g.ldb = ldx; g.b_layout = 1;
         g.M = M; g.N = N; g.K = BT;
         g.epi = EPI_F32; g.C = grd + off; g.ldc = N; g.alpha = 1.f; g.beta = acc;
-        g.nsplit = choose_split(M, N, BT, bf); g.partial = skpart;
+        const Split sp = choose_split(M, N, BT, bf);
+        g.nsplit = sp.ns; g.bn = sp.bn; g.partial = skpart;
         return run(h, "gemm_dw", [&] { return gemm(g, bf, s); });
     };
     auto bias = [&](const void* dy, int dy_f32, int n, int64_t off) -> int {

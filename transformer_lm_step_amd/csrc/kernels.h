@@ -57,6 +57,9 @@ int layernorm_backward_blocks(int rows);
 hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,
                         float* scratch, hipStream_t s);
 int sum_scratch_floats(int n);
+// the same with two destinations: columns [0, n1) into out1, [n1, n) into out2
+hipError_t sum_partials2(const float* partial, int nblk, int n, int64_t stride, float* out1, int n1, float* out2,
+                         int accumulate, float* scratch, hipStream_t s);
 // column sums of a [rows, n] matrix (storage T or f32) into out[n] (+)=, deterministic
 hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial,
                   float* out, int accumulate, float* scratch, hipStream_t s);

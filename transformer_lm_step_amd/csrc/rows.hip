@@ -248,24 +248,31 @@ __global__ void __launch_bounds__(256) colred1_kernel(const float* __restrict__ 
     }
 }
 
-__global__ void __launch_bounds__(256) colred2_kernel(const float* __restrict__ scratch, int n,
-                                                      float* __restrict__ out, int accumulate) {
+// columns [0, n1) go to out1[col], columns [n1, n) to out2[col - n1]
+__global__ void __launch_bounds__(256) colred2_kernel(const float* __restrict__ scratch, int n, float* __restrict__ out1,
+                                                      int n1, float* __restrict__ out2, int accumulate) {
     const int col = blockIdx.x * 256 + threadIdx.x;
     if (col >= n) return;
     float v = 0.f;
 #pragma unroll
     for (int z = 0; z < SUM_SLICES; ++z) v += scratch[(int64_t)z * n + col];
-    out[col] = accumulate ? out[col] + v : v;
+    float* o = col < n1 ? out1 + col : out2 + (col - n1);
+    *o = accumulate ? *o + v : v;
 }
 
-hipError_t sum_partials(const float* partial, int np, int n, int64_t stride, float* out, int accumulate,
-                        float* scratch, hipStream_t s) {
+hipError_t sum_partials2(const float* partial, int np, int n, int64_t stride, float* out1, int n1, float* out2,
+                         int accumulate, float* scratch, hipStream_t s) {
     hipLaunchKernelGGL(colred1_kernel, dim3((n + 63) / 64, SUM_SLICES), dim3(256), 0, s, partial, np, n, stride,
                        scratch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(colred2_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scratch, n, out, accumulate);
+    hipLaunchKernelGGL(colred2_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scratch, n, out1, n1, out2, accumulate);
     return hipGetLastError();
+}
+
+hipError_t sum_partials(const float* partial, int np, int n, int64_t stride, float* out, int accumulate,
+                        float* scratch, hipStream_t s) {
+    return sum_partials2(partial, np, n, stride, out, n, nullptr, accumulate, scratch, s);
 }
 
 // column sums of x [rows, n]: stage 1 writes one partial row per row-slice, stage 2 is
@@ -646,40 +653,54 @@ hipError_t grad_norm(const float* g, int64_t n, float* partial, float* d_norm_co
 // the 2-D tensors, chapter 2:25:57-2:34:49): p *= 1 - lr*wd; m = b1 m + (1-b1) g;
 // v = b2 v + (1-b2) g^2; p -= (lr/bc1) * m / (sqrt(v)/sqrt(bc2) + eps), g = c * grad.
 // The bf16 copy of the 2-D weights used by the products is refreshed in the same pass.
-__global__ void adamw_kernel(float* __restrict__ p, const float* __restrict__ g, float* __restrict__ m,
-                             float* __restrict__ v, bf16* __restrict__ shadow, int64_t n4, int64_t n_decay4,
-                             const float* __restrict__ norm_coef, float lr, float beta1, float beta2, float eps,
-                             float wd, float bc1, float bc2_sqrt) {
-    const float c = norm_coef[1];
-    const float step = lr / bc1;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-        float4 pp = ((float4*)p)[i];
-        const float4 gg = ((const float4*)g)[i];
-        float4 mm = ((float4*)m)[i];
-        float4 vv = ((float4*)v)[i];
-        const bool dec = i < n_decay4;
-        const float keep = dec ? 1.0f - lr * wd : 1.0f;
-        float* pa = (float*)&pp;
-        const float* ga = (const float*)&gg;
-        float* ma = (float*)&mm;
-        float* va = (float*)&vv;
+DEV void adamw4(float4& pp, const float4& gg, float4& mm, float4& vv, float keep, float c, float beta1,
+                float beta2, float eps, float step, float inv_bc2_sqrt) {
+    float* pa = (float*)&pp;
+    const float* ga = (const float*)&gg;
+    float* ma = (float*)&mm;
+    float* va = (float*)&vv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float gq = c * ga[q];
-            pa[q] *= keep;
-            ma[q] = beta1 * ma[q] + (1.0f - beta1) * gq;
-            va[q] = beta2 * va[q] + (1.0f - beta2) * gq * gq;
-            const float den = sqrtf(va[q]) / bc2_sqrt + eps;
-            pa[q] -= step * (ma[q] / den);
+    for (int q = 0; q < 4; ++q) {
+        const float gq = c * ga[q];
+        pa[q] *= keep;
+        ma[q] = beta1 * ma[q] + (1.0f - beta1) * gq;
+        va[q] = beta2 * va[q] + (1.0f - beta2) * gq * gq;
+        const float den = sqrtf(va[q]) * inv_bc2_sqrt + eps;
+        pa[q] -= step * (ma[q] / den);
+    }
+}
+DEV void store_shadow4(bf16* sh, int64_t i, const float4& pp) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 b;
+    b[0] = (bf16)pp.x; b[1] = (bf16)pp.y; b[2] = (bf16)pp.z; b[3] = (bf16)pp.w;
+    ((bf16x4*)sh)[i] = b;
+}
+// Each thread updates float4 groups i and i + stride per iteration, all eight loads issued
+// before any arithmetic so two groups' memory latency overlaps.
+__global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    bf16* __restrict__ shadow, int64_t n4, int64_t n_decay4,
+                                                    const float* __restrict__ norm_coef, float lr, float beta1,
+                                                    float beta2, float eps, float wd, float bc1, float bc2_sqrt) {
+    const float c = norm_coef[1];
+    const float step = lr / bc1, inv_bc2_sqrt = 1.0f / bc2_sqrt, kd = 1.0f - lr * wd;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += 2 * stride) {
+        const int64_t j = i + stride;
+        const bool two = j < n4;
+        float4 p0 = ((float4*)p)[i], m0 = ((float4*)m)[i], v0 = ((float4*)v)[i];
+        const float4 g0 = ((const float4*)g)[i];
+        float4 p1, m1, v1, g1;
+        if (two) {
+            p1 = ((float4*)p)[j]; m1 = ((float4*)m)[j]; v1 = ((float4*)v)[j]; g1 = ((const float4*)g)[j];
         }
-        ((float4*)p)[i] = pp;
-        ((float4*)m)[i] = mm;
-        ((float4*)v)[i] = vv;
-        if (shadow && dec) {
-            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-            bf16x4 b;
-            b[0] = (bf16)pa[0]; b[1] = (bf16)pa[1]; b[2] = (bf16)pa[2]; b[3] = (bf16)pa[3];
-            ((bf16x4*)shadow)[i] = b;
+        adamw4(p0, g0, m0, v0, i < n_decay4 ? kd : 1.0f, c, beta1, beta2, eps, step, inv_bc2_sqrt);
+        ((float4*)p)[i] = p0; ((float4*)m)[i] = m0; ((float4*)v)[i] = v0;
+        if (shadow && i < n_decay4) store_shadow4(shadow, i, p0);
+        if (two) {
+            adamw4(p1, g1, m1, v1, j < n_decay4 ? kd : 1.0f, c, beta1, beta2, eps, step, inv_bc2_sqrt);
+            ((float4*)p)[j] = p1; ((float4*)m)[j] = m1; ((float4*)v)[j] = v1;
+            if (shadow && j < n_decay4) store_shadow4(shadow, j, p1);
         }
     }
 }
