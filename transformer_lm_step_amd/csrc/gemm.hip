@@ -366,8 +366,8 @@ DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
     }
 }
 
-// Epilogue of the LDS-streamed path. Its MFMAs take B as the first operand, so acc[i][j] is a
-// block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
+// Transposed epilogue of the LDS-streamed path. With B as the first MFMA operand, acc[i][j]
+// is a block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
 // n = nw + 16j + 4(l >> 4) + r, r = 0..3 -- one 16-byte (fp32) or 8-byte (bf16) access per
 // block and lane on full tiles.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -462,6 +462,11 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
+    // Epilogues that read a second operand or do per-element math (residual add, GELU, GELU
+    // derivative) take the transposed accumulator layout and 8/16-byte accesses; plain stores
+    // keep the natural layout, whose store instructions cover 4 rows x 16 columns (measured
+    // faster for write-only epilogues, slower for the others).
+    constexpr bool TRANS_EPI = EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
     const int num_m = (p.M + BM - 1) / BM, num_n = (p.N + BN - 1) / BN;
@@ -513,13 +518,19 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) mma8(acc[i][j], bfr[j], af[i]);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (TRANS_EPI) mma8(acc[i][j], bfr[j], af[i]);
+                    else mma8(acc[i][j], af[i], bfr[j]);
+                }
         }
     }
-    if (p.vec && m0 + BM <= p.M && n0 + BN <= p.N)
-        store_t_body<EPI, FM, FN, false>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
-    else
-        store_t_body<EPI, FM, FN, true>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
+    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
+    if constexpr (TRANS_EPI) {
+        if (p.vec && full) store_t_body<EPI, FM, FN, false>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        else store_t_body<EPI, FM, FN, true>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
+    } else {
+        store_tile<bf16, EPI, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane, full);
+    }
 }
 
 template <int BM, int BN>
