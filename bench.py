@@ -90,21 +90,99 @@ def cpu_baseline(w):
                       f"{el:.1f} s"}
 
 
-def traffic_for(kernel):
+def sources_sha256():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "transformer_lm_step_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel_class):
     """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel)
-        if not rec:
+        rec = json.load(open(path))
+        if rec.get("source_sha256") != sources_sha256():
             return None
-        h = hashlib.sha256()
-        for f in sorted(os.listdir(os.path.join(ROOT, "transformer_lm_step_amd", "csrc"))):
-            h.update(open(os.path.join(ROOT, "transformer_lm_step_amd", "csrc", f), "rb").read())
-        return rec["bytes_per_launch"] if rec.get("source_sha256") == h.hexdigest() else None
+        c = rec["classes"].get(kernel_class)
+        return c["bytes_per_launch"] if c else None
     except Exception:
         return None
+
+
+# Kernel classes whose kernel can be told apart in a counter trace by name (and, for the
+# kernel shared by the qkv and lm_head products, by grid size).
+TRAFFIC_CLASSES = {
+    "gemm_fc": ("gemm_mm_kernel<0, 0, 2,", None),
+    "gemm_lm_head": ("gemm_mm_kernel<0, 0, 0,", "max"),
+    "gemm_qkv": ("gemm_mm_kernel<0, 0, 0,", "min"),
+    "gemm_lm_head_dw": ("gemm_mm_kernel<1, 1, 4,", None),
+    "cross_entropy": ("cross_entropy_kernel", None),
+    "adamw": ("adamw_kernel", None),
+    "attn_fwd": ("attn_fwd_ts_kernel", None),
+    "layernorm_fwd": ("layernorm_forward_kernel", None),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into HBM bytes
+    per launch for the classes above. Each counter is scaled by what it reads for the device
+    copy of copy_bytes bytes (which reads and writes exactly copy_bytes)."""
+    import csv
+    from collections import defaultdict
+
+    def load(path, counter):
+        per = defaultdict(float)
+        meta = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            per[d] += float(r["Counter_Value"])
+            meta[d] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        return per, meta
+
+    fetch, fmeta = load(fetch_csv, "FETCH_SIZE")
+    write, wmeta = load(write_csv, "WRITE_SIZE")
+
+    def copies(per, meta):
+        v = [per[d] for d in per if COPY_KERNEL in meta[d][0]]
+        v.sort()
+        return v[-1] if v else None  # the calibration copies are the largest copy dispatches
+
+    cf, cw = copies(fetch, fmeta), copies(write, wmeta)
+    if not cf or not cw:
+        raise SystemExit("no calibration copy found in the counter traces")
+    sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+
+    def select(per, meta, name, grid_rule):
+        ds = [d for d in per if name in meta[d][0]]
+        if grid_rule and ds:
+            grids = sorted({meta[d][1] for d in ds})
+            g = grids[-1] if grid_rule == "max" else grids[0]
+            ds = [d for d in ds if meta[d][1] == g]
+        return ds
+
+    classes = {}
+    for cls, (name, rule) in TRAFFIC_CLASSES.items():
+        fd, wd = select(fetch, fmeta, name, rule), select(write, wmeta, name, rule)
+        if not fd or not wd:
+            continue
+        fb = sum(fetch[d] for d in fd) / len(fd) * 1024.0 * sf
+        wb = sum(write[d] for d in wd) / len(wd) * 1024.0 * sw
+        classes[cls] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                        "dispatches": len(fd)}
+    rec = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                     "scaled by the ratio of a device copy's known bytes to what the counter read for it",
+           "source_sha256": sources_sha256(), "copy_bytes": copy_bytes,
+           "copy_scale": {"fetch": round(sf, 4), "write": round(sw, 4)}, "classes": classes}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def main():
@@ -115,7 +193,16 @@ def main():
     ap.add_argument("--workload", default="gpt2_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
+                    help="after timing, run device copies of BYTES bytes (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="build profiles/traffic.json from two rocprofv3 --pmc counter traces and exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_bytes,
+                     os.path.join(ROOT, "profiles", "traffic.json"))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the data-parallel sharding is described in the design notes, not implemented)", file=sys.stderr)
@@ -226,6 +313,13 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    if args.copy_calib:
+        src = torch.empty(args.copy_calib, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
