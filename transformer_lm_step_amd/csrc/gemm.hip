@@ -60,6 +60,13 @@ DEV void tile_coords(int pid, int nwg, int num_m, int num_n, int& tm, int& tn) {
     int tall = nwg & 7;
     if (tall == 0) tall = 8;
     int logical = (xcd < tall) ? xcd * per + slot : tall * per + (xcd - tall) * (per - 1) + slot;
+    if (num_n <= 8) {
+        // few column tiles: the tiles of one row panel are consecutive, so the blocks that share
+        // an A panel start (and stream its K tiles) together
+        tm = logical / num_n;
+        tn = logical - tm * num_n;
+        return;
+    }
     const int GROUP_M = 8;
     const int in_group = GROUP_M * num_n;
     const int gid = logical / in_group;
@@ -366,91 +373,109 @@ DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
     }
 }
 
-// Transposed epilogue of the LDS-streamed path. With B as the first MFMA operand, acc[i][j]
-// is a block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
-// n = nw + 16j + 4(l >> 4) + r, r = 0..3 -- one 16-byte (fp32) or 8-byte (bf16) access per
-// block and lane on full tiles.
+// Epilogue of the LDS-streamed path. Its MFMAs take B as the first operand, so acc[i][j] is a
+// block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
+// n = nw + 16j + 4(l >> 4) + r, r = 0..3.
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
     bf16x4 o;
     o[0] = (bf16)a; o[1] = (bf16)b; o[2] = (bf16)c; o[3] = (bf16)d;
     return o;
 }
-template <int EPI, int FM, int FN, bool CHECK>
-DEV void store_t_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int nw, int lane) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int n0 = nw + 16 * j + 4 * (lane >> 4);
+// Epilogue on 4 consecutive columns n..n+3 of row m (v = accumulators): vector accesses when
+// the 4 columns are inside the matrix and the rows are 16-byte friendly, else per element.
+template <int EPI>
+DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4) {
+    if (m >= p.M) return;
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    const int64_t o = (int64_t)m * p.ldc + n;
+    if (p.vec && n + 3 < p.N) {
         float bias[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU) {
             if (p.bias) {
-                if constexpr (!CHECK) {
-                    const float4 b4 = *(const float4*)(p.bias + n0);
-                    bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) bias[r] = n0 + r < p.N ? p.bias[n0 + r] : 0.f;
-                }
+                const float4 b4 = *(const float4*)(p.bias + n);
+                bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
             }
         }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int m = mw + 16 * i + (lane & 15);
-            const floatx4 v = acc[i][j];
-            const int64_t o = (int64_t)m * p.ldc + n0;
-            if constexpr (!CHECK) {
-                if constexpr (EPI == EPI_BIAS_T) {
-                    *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(p.alpha * v[0] + bias[0], p.alpha * v[1] + bias[1],
-                                                           p.alpha * v[2] + bias[2], p.alpha * v[3] + bias[3]);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    const float4 rr = *(const float4*)(p.resid + (int64_t)m * p.ldr + n0);
-                    *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0] + bias[0], rr.y + v[1] + bias[1],
-                                                              rr.z + v[2] + bias[2], rr.w + v[3] + bias[3]);
-                } else if constexpr (EPI == EPI_BIAS_GELU) {
-                    const bf16x4 u = to_bf16x4(v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]);
-                    *(bf16x4*)((bf16*)p.C + o) = u;
-                    *(bf16x4*)((bf16*)p.C2 + o) = to_bf16x4(gelu_f((float)u[0]), gelu_f((float)u[1]),
-                                                            gelu_f((float)u[2]), gelu_f((float)u[3]));
-                } else if constexpr (EPI == EPI_GELU_BWD) {
-                    const bf16x4 a = *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n0);
-                    *(bf16x4*)((bf16*)p.C + o) =
-                        to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
-                                  v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
-                } else if constexpr (EPI == EPI_F32) {
-                    float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (p.beta) old = *(const float4*)((const float*)p.C + o);
-                    *(float4*)((float*)p.C + o) = make_float4(old.x + p.alpha * v[0], old.y + p.alpha * v[1],
-                                                              old.z + p.alpha * v[2], old.w + p.alpha * v[3]);
-                } else {  // EPI_PARTIAL
-                    *(float4*)((float*)p.C + (int64_t)blockIdx.y * p.part_stride + o) = make_float4(v[0], v[1], v[2], v[3]);
-                }
-            } else {
-                if (m >= p.M) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = n0 + r;
-                    if (n >= p.N) continue;
-                    const int64_t e = o + r;
-                    if constexpr (EPI == EPI_BIAS_T) {
-                        ((bf16*)p.C)[e] = (bf16)(p.alpha * v[r] + bias[r]);
-                    } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                        ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + n] + v[r] + bias[r];
-                    } else if constexpr (EPI == EPI_BIAS_GELU) {
-                        const bf16 u = (bf16)(v[r] + bias[r]);
-                        ((bf16*)p.C)[e] = u;
-                        ((bf16*)p.C2)[e] = (bf16)gelu_f((float)u);
-                    } else if constexpr (EPI == EPI_GELU_BWD) {
-                        const float a = (float)((const bf16*)p.aux)[(int64_t)m * p.ldaux + n];
-                        ((bf16*)p.C)[e] = (bf16)(v[r] * gelu_grad_f(a));
-                    } else if constexpr (EPI == EPI_F32) {
-                        const float old = p.beta ? ((const float*)p.C)[e] : 0.f;
-                        ((float*)p.C)[e] = old + p.alpha * v[r];
-                    } else {  // EPI_PARTIAL
-                        ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + e] = v[r];
-                    }
-                }
-            }
+        if constexpr (EPI == EPI_BIAS_T) {
+            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(p.alpha * v[0] + bias[0], p.alpha * v[1] + bias[1],
+                                                   p.alpha * v[2] + bias[2], p.alpha * v[3] + bias[3]);
+        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+            const float4 rr = *(const float4*)(p.resid + (int64_t)m * p.ldr + n);
+            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0] + bias[0], rr.y + v[1] + bias[1],
+                                                      rr.z + v[2] + bias[2], rr.w + v[3] + bias[3]);
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+            const bf16x4 u = to_bf16x4(v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]);
+            *(bf16x4*)((bf16*)p.C + o) = u;
+            *(bf16x4*)((bf16*)p.C2 + o) = to_bf16x4(gelu_f((float)u[0]), gelu_f((float)u[1]), gelu_f((float)u[2]),
+                                                    gelu_f((float)u[3]));
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+            const bf16x4 a = *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
+                                                   v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
+        } else if constexpr (EPI == EPI_F32) {
+            float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p.beta) old = *(const float4*)((const float*)p.C + o);
+            *(float4*)((float*)p.C + o) = make_float4(old.x + p.alpha * v[0], old.y + p.alpha * v[1],
+                                                      old.z + p.alpha * v[2], old.w + p.alpha * v[3]);
+        } else {  // EPI_PARTIAL
+            *(float4*)((float*)p.C + (int64_t)blockIdx.y * p.part_stride + o) = v4;
         }
+        return;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int nn = n + r;
+        if (nn >= p.N) continue;
+        const int64_t e = o + r;
+        const float b = (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU) && p.bias ? p.bias[nn] : 0.f;
+        if constexpr (EPI == EPI_BIAS_T) {
+            ((bf16*)p.C)[e] = (bf16)(p.alpha * v[r] + b);
+        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+            ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + nn] + v[r] + b;
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+            const bf16 u = (bf16)(v[r] + b);
+            ((bf16*)p.C)[e] = u;
+            ((bf16*)p.C2)[e] = (bf16)gelu_f((float)u);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+            ((bf16*)p.C)[e] = (bf16)(v[r] * gelu_grad_f((float)((const bf16*)p.aux)[(int64_t)m * p.ldaux + nn]));
+        } else if constexpr (EPI == EPI_F32) {
+            const float old = p.beta ? ((const float*)p.C)[e] : 0.f;
+            ((float*)p.C)[e] = old + p.alpha * v[r];
+        } else {  // EPI_PARTIAL
+            ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + e] = v[r];
+        }
+    }
+}
+
+// LDS-staged epilogue: the fp32 tile passes through LDS in two halves of 64 rows (the waves
+// with wm == h write half h with 16-byte stores, conflict-free with rows padded by 16 bytes),
+// then all threads apply the epilogue to 4-column chunks along the rows, so every global load
+// and store of the epilogue covers whole row segments.
+template <int EPI, int FM, int FN, int BN>
+DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm, int wn,
+                      int lane, int tid) {
+    constexpr int LDW = BN + 4;            // floats per staged row
+    constexpr int CPR = BN / 4;            // 4-column chunks per row
+    float* st = (float*)smem;
+    __syncthreads();                       // every wave is done reading the last K tile
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (wm == h) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    *(float4*)(st + (16 * i + (lane & 15)) * LDW + wn * (BN / 2) + 16 * j + 4 * (lane >> 4)) =
+                        make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int k = tid; k < 64 * CPR; k += GTHREADS) {
+            const int r = k / CPR, c4 = k - r * CPR;
+            epi4<EPI>(p, m0 + 64 * h + r, n0 + 4 * c4, *(const float4*)(st + r * LDW + 4 * c4));
+        }
+        __syncthreads();
     }
 }
 
@@ -462,11 +487,6 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
-    // Epilogues that read a second operand or do per-element math (residual add, GELU, GELU
-    // derivative) take the transposed accumulator layout and 8/16-byte accesses; plain stores
-    // keep the natural layout, whose store instructions cover 4 rows x 16 columns (measured
-    // faster for write-only epilogues, slower for the others).
-    constexpr bool TRANS_EPI = EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
     const int num_m = (p.M + BM - 1) / BM, num_n = (p.N + BN - 1) / BN;
@@ -518,19 +538,10 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    if constexpr (TRANS_EPI) mma8(acc[i][j], bfr[j], af[i]);
-                    else mma8(acc[i][j], af[i], bfr[j]);
-                }
+                for (int j = 0; j < FN; ++j) mma8(acc[i][j], bfr[j], af[i]);
         }
     }
-    const bool full = m0 + BM <= p.M && n0 + BN <= p.N;
-    if constexpr (TRANS_EPI) {
-        if (p.vec && full) store_t_body<EPI, FM, FN, false>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
-        else store_t_body<EPI, FM, FN, true>(p, acc, m0 + wm * TM, n0 + wn * TN, lane);
-    } else {
-        store_tile<bf16, EPI, FM, FN>(p, acc, m0 + wm * TM, n0 + wn * TN, lane, full);
-    }
+    store_staged<EPI, FM, FN, BN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
 
 template <int BM, int BN>
