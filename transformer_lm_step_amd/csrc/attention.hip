@@ -525,16 +525,31 @@ constexpr int TS_BYTES = 64 * 128;
 
 DEV int ts_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
 
-// this wave's share (rows 16w..16w+15) of a 64-row tile whose row r starts at src + r*ld;
-// rows >= nrows repeat the last valid row (finite values, masked out by the callers)
-DEV void ts_load(const bf16* src, int64_t ld, int nrows, uint32_t lds, int wave, int lane) {
+// Byte offsets of this wave's share (rows 16w..16w+15) of a 64-row tile whose row r starts at
+// src + r*ld; rows >= nrows repeat the last valid row (finite values, masked out by the
+// callers). They depend only on nrows, so kernels compute the full-tile set once.
+struct TsOff {
+    uint32_t o[2];
+};
+DEV TsOff ts_offsets(int64_t ld, int nrows, int wave, int lane) {
+    TsOff t;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = 16 * wave + 8 * i + (lane >> 3);
         const int c = (lane & 7) ^ ts_swz(r);
         const int rr = min(r, nrows - 1);
-        dma16(src, (uint32_t)(rr * ld * 2 + c * 16), lds + (2 * wave + i) * 1024);
+        t.o[i] = (uint32_t)(rr * ld * 2 + c * 16);
     }
+    return t;
+}
+DEV void ts_issue(const bf16* src, const TsOff& off, uint32_t lds, int wave) {
+    dma16(src, off.o[0], lds + (2 * wave) * 1024);
+    dma16(src, off.o[1], lds + (2 * wave + 1) * 1024);
+}
+// the tile of nrows valid rows: the precomputed full-tile offsets unless the tile is ragged
+DEV void ts_load(const bf16* src, int64_t ld, int nrows, const TsOff& full, uint32_t lds, int wave, int lane) {
+    if (nrows == 64) ts_issue(src, full, lds, wave);
+    else ts_issue(src, ts_offsets(ld, nrows, wave, lane), lds, wave);
 }
 // rows rb..rb+15 (lane & 15), k = 32ks + 8(lane >> 4) + 0..7 along the row
 DEV bf16x8 ts_nat(const char* t, int rb, int ks, int lane) {
@@ -552,7 +567,7 @@ DEV bf16x8 ts_tr(const char* t, int cb, int r0, int r1, int lane) {
 }
 DEV float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32: exp2(-inf) = 0
 
-__global__ void __launch_bounds__(A_THREADS, 2) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
+__global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
                                                                 float* __restrict__ lse, int T_, int H, float sc) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
     constexpr int HS = 64, STAGE = 2 * TS_BYTES;
@@ -586,11 +601,12 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_fwd_ts_kernel(const bf16* _
     const int kend = min(q0 + 128, T_);
     const int nchunk = (kend + 63) / 64;
     const bool wave_live = qw0 < T_;
+    const TsOff offkv = ts_offsets(ld, 64, wave, lane);
     auto issue = [&](int c) {
         const int k0 = c * 64, nv = min(64, T_ - k0);
         const uint32_t st = lds0 + (c & 1) * STAGE;
-        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, st, wave, lane);
-        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, st + TS_BYTES, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, offkv, st, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, offkv, st + TS_BYTES, wave, lane);
     };
     if (nchunk > 0) issue(0);
     for (int c = 0; c < nchunk; ++c) {
@@ -717,11 +733,12 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
 
     const int qc0 = k0 / 64, nqc = (T_ + 63) / 64;
     const bool wave_live = kw0 < T_;
+    const TsOff offq = ts_offsets(ld, 64, wave, lane), offo = ts_offsets(C, 64, wave, lane);
     auto issue = [&](int qc) {
         const int q0 = qc * 64, nv = min(64, T_ - q0);
         const uint32_t st = lds0 + ((qc - qc0) & 1) * STAGE;
-        ts_load(base + (int64_t)q0 * ld + h * HS, ld, nv, st, wave, lane);
-        ts_load(dyb + (int64_t)q0 * C + h * HS, C, nv, st + TS_BYTES, wave, lane);
+        ts_load(base + (int64_t)q0 * ld + h * HS, ld, nv, offq, st, wave, lane);
+        ts_load(dyb + (int64_t)q0 * C + h * HS, C, nv, offo, st + TS_BYTES, wave, lane);
         const uint32_t voff = (uint32_t)min(lane, nv - 1) * 4;
         if (wave == 0) dma4(lse_bh + q0, voff, st + 2 * TS_BYTES);
         if (wave == 1) dma4(D_bh + q0, voff, st + 2 * TS_BYTES + 256);
@@ -849,11 +866,12 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
     const int kend = min(q0 + 128, T_);
     const int nchunk = (kend + 63) / 64;
     const bool wave_live = qw0 < T_;
+    const TsOff offkv = ts_offsets(ld, 64, wave, lane);
     auto issue = [&](int c) {
         const int k0 = c * 64, nv = min(64, T_ - k0);
         const uint32_t st = lds0 + (c & 1) * STAGE;
-        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, st, wave, lane);
-        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, st + TS_BYTES, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + C + h * HS, ld, nv, offkv, st, wave, lane);
+        ts_load(base + (int64_t)k0 * ld + 2 * C + h * HS, ld, nv, offkv, st + TS_BYTES, wave, lane);
     };
     if (nchunk > 0) issue(0);
     for (int c = 0; c < nchunk; ++c) {
