@@ -389,6 +389,7 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dkv_kernel(const T* __rest
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll
@@ -617,6 +618,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
         floatx4 s[4][2];
+        __builtin_amdgcn_s_setprio(1);  // MFMA phase first; other waves run their softmax meanwhile
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             s[kb][0] = s[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -627,6 +629,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
                 mma8(s[kb][1], kf, qf[1][ks]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // online softmax in the log2 domain on raw scores: max first, then one fma + exp2
         const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
 #pragma unroll
@@ -663,6 +666,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
 #pragma unroll
             for (int d = 0; d < 4; ++d) o[d][qb] *= alpha;
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const bf16x8 p0 = frag_from_acc<bf16>(s[2 * st][0], s[2 * st + 1][0]);
@@ -674,6 +678,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
                 mma8(o[d][1], vf, p1);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll
@@ -754,6 +759,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
         const float* sL = (const float*)(sQ + 2 * TS_BYTES);
         const float* sD = sL + 64;
         floatx4 s[4][2], dp[4][2];
+        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
 #pragma unroll
@@ -769,6 +775,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col
         const bool need_mask = (q0 < kw0 + 32) || (q0 + 64 > T_);
 #pragma unroll
@@ -787,6 +794,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                     dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
                 }
             }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             bf16x8 pf[2], df[2];
@@ -806,6 +814,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll
@@ -882,6 +891,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
         floatx4 s[4][2], dp[4][2];
+        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -896,6 +906,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col
         const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
 #pragma unroll
@@ -911,6 +922,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
                     dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
                 }
             }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const bf16x8 d0 = frag_from_acc<bf16>(dp[2 * st][0], dp[2 * st + 1][0]);
@@ -922,6 +934,7 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
                 mma8(dq[d][1], kat, d1);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll

@@ -528,6 +528,9 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
         }
         const char* As = smem + (kt & 1) * STAGE;
         const char* Bs = As + BM * 128;
+        // raised priority while this wave multiplies: the other wave on the SIMD (from the other
+        // workgroup) issues its loads in the gaps instead of interleaving its own MFMA chain
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 af[FM], bfr[FN];
@@ -540,6 +543,7 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j) mma8(acc[i][j], bfr[j], af[i]);
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     store_staged<EPI, FM, FN, BN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
