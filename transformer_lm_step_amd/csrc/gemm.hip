@@ -43,6 +43,7 @@ struct GemmArgs {
     float alpha;
     int beta;                   // 1: add into the fp32 output
     int64_t part_stride;        // split-K partial stride (elements)
+    float* rowsum_part;         // [nsplit][M] row sums of A (a_layout 1), or null
     int vec;                    // 1: full tiles may use 8/16-byte epilogue accesses
 };
 
@@ -479,11 +480,12 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
     }
 }
 
-template <int ALAY, int BLAY, int EPI, int BM, int BN>
+template <int ALAY, int BLAY, int EPI, int BM, int BN, bool ROWSUM = false>
 // Bounds of one workgroup per CU: the compiler then keeps the accumulators in AGPRs and uses the
 // VGPRs for deeper load scheduling (measured 10-15% faster than a two-workgroup bound). Every
 // instantiation stays at or below 256 registers in total, so two workgroups still share a CU.
-__global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
+// (The row-sum variant needs the explicit two-workgroup bound to stay within 256 registers.)
+__global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmArgs p) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
@@ -511,6 +513,12 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // row sums of A: the waves of the first column tile with wn == 0 add up the A fragments
+    // they read anyway (lane group g holds 8 of each 32 k for row 16i + (lane & 15))
+    float rs[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) rs[i] = 0.f;
+    const bool do_rs = ROWSUM && tn == 0 && wn == 0;
 
     if (nt > 0) {
         mm_issue<BM>(baseA, offA, lds0, wave);
@@ -536,6 +544,20 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
             bf16x8 af[FM], bfr[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) af[i] = mm_frag<ALAY, BM>(As, wm * TM + 16 * i, ks, lane);
+            if constexpr (ROWSUM) {
+                if (do_rs) {
+                    // each 32-bit word holds two bf16: their fp32 values are (w << 16) and
+                    // (w & 0xffff0000)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const uint4 w = __builtin_bit_cast(uint4, af[i]);
+                        rs[i] += ((__uint_as_float(w.x << 16) + __uint_as_float(w.x & 0xffff0000u)) +
+                                  (__uint_as_float(w.y << 16) + __uint_as_float(w.y & 0xffff0000u))) +
+                                 ((__uint_as_float(w.z << 16) + __uint_as_float(w.z & 0xffff0000u)) +
+                                  (__uint_as_float(w.w << 16) + __uint_as_float(w.w & 0xffff0000u)));
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < FN; ++j) bfr[j] = mm_frag<BLAY, BN>(Bs, wn * TN + 16 * j, ks, lane);
 #pragma unroll
@@ -544,6 +566,18 @@ __global__ void __launch_bounds__(GTHREADS, 1) gemm_mm_kernel(GemmArgs p) {
                 for (int j = 0; j < FN; ++j) mma8(acc[i][j], bfr[j], af[i]);
         }
         __builtin_amdgcn_s_setprio(0);
+    }
+    if constexpr (ROWSUM) {
+        if (do_rs) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                float v = rs[i];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                const int m = m0 + wm * TM + 16 * i + (lane & 15);
+                if (lane < 16 && m < p.M) p.rowsum_part[(int64_t)blockIdx.y * p.M + m] = v;
+            }
+        }
     }
     store_staged<EPI, FM, FN, BN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
 }
@@ -555,13 +589,31 @@ template <int ALAY, int BLAY, int EPI, int BM, int BN>
 static hipError_t launch_mm(const GemmArgs& a, int nsplit, hipStream_t s) {
     const int num_m = (a.M + BM - 1) / BM, num_n = (a.N + BN - 1) / BN;
     dim3 grid(num_m * num_n, nsplit);
+    if constexpr (ALAY == 1) {
+        if (a.rowsum_part) {
+            gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN, true><<<grid, dim3(GTHREADS), mm_lds_bytes<BM, BN>(), s>>>(a);
+            return hipGetLastError();
+        }
+    }
     gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN><<<grid, dim3(GTHREADS), mm_lds_bytes<BM, BN>(), s>>>(a);
     return hipGetLastError();
 }
 
-// out[m][n] = (beta ? out : 0) + alpha * sum_z part[z][m][n], z in order (deterministic)
+
+// out[m][n] = (beta ? out : 0) + alpha * sum_z part[z][m][n], z in order (deterministic).
+// Workgroups past the matrix (when rs_out is set) reduce the row-sum partials the same way:
+// rs_out[m] = (beta ? rs_out[m] : 0) + sum_z rs_part[z][m].
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t stride,
-                                     float* __restrict__ out, int64_t n_elem, float alpha, int beta) {
+                                     float* __restrict__ out, int64_t n_elem, float alpha, int beta, int mat_blocks,
+                                     const float* __restrict__ rs_part, int rs_m, float* __restrict__ rs_out) {
+    if ((int)blockIdx.x >= mat_blocks) {
+        const int m = ((int)blockIdx.x - mat_blocks) * blockDim.x + threadIdx.x;
+        if (m >= rs_m) return;
+        float v = 0.f;
+        for (int z = 0; z < nsplit; ++z) v += rs_part[(int64_t)z * rs_m + m];
+        rs_out[m] = beta ? rs_out[m] + v : v;
+        return;
+    }
     const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i4 >= n_elem) return;
     float4 s = *(const float4*)(part + i4);
@@ -628,6 +680,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     a.M = d.M; a.N = d.N; a.K = d.K;
     a.C = d.C; a.ldc = d.ldc; a.C2 = d.C2; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
     a.aux = d.aux; a.ldaux = d.ldaux; a.alpha = d.alpha; a.beta = d.beta;
+    a.rowsum_part = nullptr;
     constexpr int BK = 128 / sizeof(T);
     int nsplit = d.nsplit < 1 ? 1 : d.nsplit;
     const int ktiles = (d.K + BK - 1) / BK;
@@ -652,6 +705,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     hipError_t e = hipSuccess;
     if constexpr (sizeof(T) == 2) {
         if (!d.no_dl && mm_ok(d, a.ksplit_len)) {
+            if (d.rowsum && d.a_layout == 1) a.rowsum_part = d.rowsum_part;
             // 128x192 tiles (wave tile 64x96: fewer LDS bytes per MFMA) whenever N is a multiple
             // of 192 and they fill whole rounds of 512 workgroups (two per CU) about as well as
             // 128x128 tiles: N = 768 gives 512 tiles instead of 768, N = 2304 three rounds
@@ -709,16 +763,29 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 #undef GEMM_CASE
 reduce:
     if (e != hipSuccess) return e;
-    if (nsplit > 1) {
-        if (d.epi != EPI_F32 || d.ldc != d.N) return hipErrorInvalidValue;
-        const int64_t n = (int64_t)d.M * d.N;
+    if (nsplit > 1 || a.rowsum_part) {
+        // one launch: the split-K partials (if split) and the row-sum partials (if requested)
+        if (nsplit > 1 && (d.epi != EPI_F32 || d.ldc != d.N)) return hipErrorInvalidValue;
+        const int64_t n = nsplit > 1 ? (int64_t)d.M * d.N : 0;
         const int threads = 256;
-        const int64_t blocks = (n / 4 + threads - 1) / threads;
-        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(threads), 0, s,
-                           (const float*)d.partial, nsplit, (int64_t)d.M * d.N, (float*)d.C, n, d.alpha, d.beta);
+        const int mat_blocks = (int)((n / 4 + threads - 1) / threads);
+        const int rs_blocks = a.rowsum_part ? (d.M + threads - 1) / threads : 0;
+        hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)(mat_blocks + rs_blocks)), dim3(threads), 0, s,
+                           (const float*)d.partial, nsplit, (int64_t)d.M * d.N, (float*)d.C, n, d.alpha, d.beta,
+                           mat_blocks, (const float*)a.rowsum_part, d.M, d.rowsum);
         e = hipGetLastError();
     }
     return e;
+}
+
+int gemm_fuses_rowsum(const GemmDesc& d, int is_bf16) {
+    if (!is_bf16 || d.no_dl || d.a_layout != 1) return 0;
+    // the same split and tile-K rules dispatch applies
+    int nsplit = d.nsplit < 1 ? 1 : d.nsplit;
+    const int ktiles = (d.K + MM_BK - 1) / MM_BK;
+    if (nsplit > ktiles) nsplit = ktiles;
+    const int per = (ktiles + nsplit - 1) / nsplit;
+    return mm_ok(d, per * MM_BK) ? 1 : 0;
 }
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s) {
@@ -746,6 +813,14 @@ void gemm_setup() {
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();
+    (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_PARTIAL, 128, 192, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 192>());
+    (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_F32, 128, 192, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 192>());
+    (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_PARTIAL, 128, 128, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
+    (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_F32, 128, 128, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();

@@ -166,7 +166,7 @@ struct Plan {
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
     size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dres_t, dln, datt, dqkv, du, Dbuf;
-    size_t splitk, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
+    size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
 };
 
 Plan make_plan(const gpt2_config* c) {
@@ -220,6 +220,7 @@ Plan make_plan(const gpt2_config* c) {
         if (ns > 1) sk = std::max(sk, (size_t)ns * s[0] * s[1] * 4);
     }
     P.splitk = take(sk ? sk : 256);
+    P.rspart = take((size_t)16 * std::max(3 * C, F) * 4);   // <= 16 splits x the widest bias
     P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 3 * C * 4);
     P.cspart = take((size_t)colsum_partial_floats((int)BT, (int)std::max(3 * C, F)) * 4);
     P.sumscr = take((size_t)sum_scratch_floats((int)std::max(3 * C, F)) * 4);
@@ -613,7 +614,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             return sum_partials2(lnpart, lnblk, 3 * C, 3 * C, grd + w_off, 2 * C, grd + bias_off, acc, sumscr, s);
         });
     };
-    auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off) -> int {
+    // weight gradient dW (+)= dy^T x; with bias_off >= 0 also the bias gradient db (+)= colsum(dy),
+    // fused into the product when the LDS-streamed path runs it
+    auto dw = [&](const void* dy, int ldy, const void* x, int ldx, int M, int N, int64_t off,
+                  int64_t bias_off = -1) -> int {
         GemmDesc g;
         g.A = dy; g.lda = ldy; g.a_layout = 1;
         g.B = x; g.ldb = ldx; g.b_layout = 1;
@@ -621,12 +625,13 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.epi = EPI_F32; g.C = grd + off; g.ldc = N; g.alpha = 1.f; g.beta = acc;
         const Split sp = choose_split(M, N, BT, bf);
         g.nsplit = sp.ns; g.bn = sp.bn; g.partial = skpart;
-        return run(h, "gemm_dw", [&] { return gemm(g, bf, s); });
+        const bool fused = bias_off >= 0 && gemm_fuses_rowsum(g, bf);
+        if (fused) { g.rowsum = grd + bias_off; g.rowsum_part = h->at<float>(P.rspart); }
+        TRY(run(h, "gemm_dw", [&] { return gemm(g, bf, s); }));
+        if (bias_off >= 0 && !fused)
+            return run(h, "bias_grad", [&] { return colsum(dy, 0, bf, BT, M, cspart, grd + bias_off, acc, sumscr, s); });
+        return GPT2_OK;
     };
-    auto bias = [&](const void* dy, int dy_f32, int n, int64_t off) -> int {
-        return run(h, "bias_grad", [&] { return colsum(dy, dy_f32, bf, BT, n, cspart, grd + off, acc, sumscr, s); });
-    };
-
     // lm_head: dhf = s dz wte ; dwte (+)= s dz^T hf   (dz = (softmax - onehot)/BT from the forward)
     {
         GemmDesc g;
@@ -655,8 +660,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             g.epi = EPI_GELU_BWD; g.C = h->at<char>(P.du); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
-        TRY(dw(h->at<char>(P.du), F, h->at<char>(P.h2[l]), C, F, C, L.w_fc[l]));
-        TRY(bias(h->at<char>(P.du), 0, F, L.b_fc[l]));
+        TRY(dw(h->at<char>(P.du), F, h->at<char>(P.h2[l]), C, F, C, L.w_fc[l], L.b_fc[l]));
         {
             GemmDesc g;
             g.A = h->at<char>(P.du); g.lda = F; g.a_layout = 0;
@@ -681,8 +685,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             return attention_backward(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), h->at<char>(P.datt),
                                       h->at<float>(P.lse[l]), h->at<float>(P.Dbuf), h->at<char>(P.dqkv), B, T, H, hs, bf, s);
         }));
-        TRY(dw(h->at<char>(P.dqkv), 3 * C, h->at<char>(P.h1[l]), C, 3 * C, C, L.w_qkv[l]));
-        TRY(bias(h->at<char>(P.dqkv), 0, 3 * C, L.b_qkv[l]));
+        TRY(dw(h->at<char>(P.dqkv), 3 * C, h->at<char>(P.h1[l]), C, 3 * C, C, L.w_qkv[l], L.b_qkv[l]));
         {
             GemmDesc g;
             g.A = h->at<char>(P.dqkv); g.lda = 3 * C; g.a_layout = 0;

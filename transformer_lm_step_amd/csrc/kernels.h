@@ -32,9 +32,15 @@ struct GemmDesc {
     void* partial = nullptr; // fp32 scratch of nsplit*M*N floats when nsplit > 1
     int bm = 0, bn = 0;      // block tile (0: chosen from the shape)
     int no_dl = 0;           // 1: never use the direct global->LDS load path
+    // optional with a_layout 1 (A[k*lda + m]): rowsum[m] (+= if beta) sum_k A(m, k), i.e. the
+    // bias gradient of a weight-gradient product; rowsum_part holds nsplit*M floats
+    float* rowsum = nullptr;
+    float* rowsum_part = nullptr;
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+// 1 if gemm() computes d.rowsum itself (LDS-streamed bf16 path), 0 if the caller must
+int gemm_fuses_rowsum(const GemmDesc& d, int is_bf16);
 void gemm_pick_tile(int M, int N, int nsplit, int is_bf16, int* bm, int* bn);
 void gemm_setup();
 size_t gemm_lds_bytes();
