@@ -57,19 +57,21 @@ template <> DEV float4 load4<bf16>(const bf16* p) {
     return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
 }
 
-template <typename T>
-__global__ void layernorm_forward_kernel(const float* __restrict__ x, const float* __restrict__ w,
-                                         const float* __restrict__ b, T* __restrict__ out,
-                                         float* __restrict__ mean, float* __restrict__ rstd, int rows, int C) {
+// NV = float4 per lane needed for C (C <= 256 * NV): the row is held in registers sized to C
+template <typename T, int NV>
+__global__ void __launch_bounds__(256) layernorm_forward_kernel(const float* __restrict__ x, const float* __restrict__ w,
+                                                                const float* __restrict__ b, T* __restrict__ out,
+                                                                float* __restrict__ mean, float* __restrict__ rstd,
+                                                                int rows, int C) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int nv = C >> 2;
     const float4* xr = (const float4*)(x + (int64_t)row * C);
-    float4 v[LN_NV];
+    float4 v[NV];
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < LN_NV; ++j) {
+    for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
         v[j] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
@@ -77,7 +79,7 @@ __global__ void layernorm_forward_kernel(const float* __restrict__ x, const floa
     const float mu = wave_sum(s) / (float)C;
     float s2 = 0.f;
 #pragma unroll
-    for (int j = 0; j < LN_NV; ++j) {
+    for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
         if (c < nv) {
             const float a = v[j].x - mu, bb = v[j].y - mu, cc = v[j].z - mu, d = v[j].w - mu;
@@ -87,7 +89,7 @@ __global__ void layernorm_forward_kernel(const float* __restrict__ x, const floa
     const float var = wave_sum(s2) / (float)C;
     const float r = 1.0f / sqrtf(var + LN_EPS);
 #pragma unroll
-    for (int j = 0; j < LN_NV; ++j) {
+    for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
         if (c < nv) {
             const float4 ww = ((const float4*)w)[c], bb = ((const float4*)b)[c];
@@ -98,13 +100,25 @@ __global__ void layernorm_forward_kernel(const float* __restrict__ x, const floa
     if (lane == 0) { mean[row] = mu; rstd[row] = r; }
 }
 
+template <typename T>
+static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const float* x, const float* w, const float* b, T* out,
+                                float* mean, float* rstd, int rows, int C) {
+#define LNF(NV) hipLaunchKernelGGL((layernorm_forward_kernel<T, NV>), g, dim3(256), 0, s, x, w, b, out, mean, rstd, rows, C)
+    if (nv4 <= 64) LNF(1);
+    else if (nv4 <= 128) LNF(2);
+    else if (nv4 <= 192) LNF(3);
+    else if (nv4 <= 256) LNF(4);
+    else LNF(8);
+#undef LNF
+    return hipGetLastError();
+}
+
 hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     dim3 g((rows + 3) / 4);
-    if (is_bf16) hipLaunchKernelGGL(layernorm_forward_kernel<bf16>, g, dim3(256), 0, s, x, w, b, (bf16*)out, mean, rstd, rows, C);
-    else hipLaunchKernelGGL(layernorm_forward_kernel<float>, g, dim3(256), 0, s, x, w, b, (float*)out, mean, rstd, rows, C);
-    return hipGetLastError();
+    if (is_bf16) return ln_fwd_launch<bf16>(C / 4, g, s, x, w, b, (bf16*)out, mean, rstd, rows, C);
+    return ln_fwd_launch<float>(C / 4, g, s, x, w, b, (float*)out, mean, rstd, rows, C);
 }
 
 // Backward through y = xhat*w + b, xhat = (x - mean)*rstd:
