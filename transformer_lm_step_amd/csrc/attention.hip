@@ -568,13 +568,18 @@ DEV bf16x8 ts_tr(const char* t, int cb, int r0, int r1, int lane) {
 }
 DEV float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32: exp2(-inf) = 0
 
-__global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* __restrict__ qkv, bf16* __restrict__ y,
-                                                                float* __restrict__ lse, int T_, int H, float sc) {
+// QB blocks of 16 queries per wave: 4 waves cover 64 * QB queries of one (batch, head)
+template <int QB>
+__global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel(const bf16* __restrict__ qkv,
+                                                                                 bf16* __restrict__ y,
+                                                                                 float* __restrict__ lse, int T_, int H,
+                                                                                 float sc) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
     constexpr int HS = 64, STAGE = 2 * TS_BYTES;
     int bx, by;
     xcd_remap(bx, by);
-    const int nqb = (T_ + 127) / 128;
+    constexpr int QW = 16 * QB, QBLK = 4 * QW;  // queries per wave, per workgroup
+    const int nqb = (T_ + QBLK - 1) / QBLK;
     const int qblk = nqb - 1 - bx;  // longest blocks first
     const int bh = by, b = bh / H, h = bh % H;
     const int C = H * HS;
@@ -582,24 +587,29 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
     const bf16* base = qkv + (int64_t)b * T_ * ld;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+    const int q0 = qblk * QBLK, qw0 = q0 + wave * QW;
     const int col = lane & 15, g = lane >> 4;
     const uint32_t lds0 = lds_addr(smem);
 
-    bf16x8 qf[2][2];
+    bf16x8 qf[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 16 + col;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             qf[qb][ks] = q < T_ ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
     }
-    floatx4 o[4][2];
+    floatx4 o[4][QB];
+    float mrun[QB], lrun[QB];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) o[d][0] = o[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        mrun[qb] = -INFINITY;
+        lrun[qb] = 0.f;
+    }
 
-    const int kend = min(q0 + 128, T_);
+    const int kend = min(q0 + QBLK, T_);
     const int nchunk = (kend + 63) / 64;
     const bool wave_live = qw0 < T_;
     const TsOff offkv = ts_offsets(ld, 64, wave, lane);
@@ -614,26 +624,27 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
         dma_wait_barrier();
         if (c + 1 < nchunk) issue(c + 1);
         const int k0 = c * 64;
-        if (!wave_live || k0 > qw0 + 31) continue;
+        if (!wave_live || k0 > qw0 + QW - 1) continue;
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
-        floatx4 s[4][2];
+        floatx4 s[4][QB];
         __builtin_amdgcn_s_setprio(1);  // MFMA phase first; other waves run their softmax meanwhile
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            s[kb][0] = s[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8 kf = ts_nat(sK, kb * 16, ks, lane);
-                mma8(s[kb][0], kf, qf[0][ks]);
-                mma8(s[kb][1], kf, qf[1][ks]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) mma8(s[kb][qb], kf, qf[qb][ks]);
             }
         }
         __builtin_amdgcn_s_setprio(0);
         // online softmax in the log2 domain on raw scores: max first, then one fma + exp2
         const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             const int q = qw0 + qb * 16 + col;
             float mx = -INFINITY;
 #pragma unroll
@@ -669,20 +680,21 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_fwd_ts_kernel(const bf16* _
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const bf16x8 p0 = frag_from_acc<bf16>(s[2 * st][0], s[2 * st + 1][0]);
-            const bf16x8 p1 = frag_from_acc<bf16>(s[2 * st][1], s[2 * st + 1][1]);
+            bf16x8 pf[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) pf[qb] = frag_from_acc<bf16>(s[2 * st][qb], s[2 * st + 1][qb]);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const bf16x8 vf = ts_tr(sV, d * 16, 32 * st, 32 * st + 16, lane);
-                mma8(o[d][0], vf, p0);
-                mma8(o[d][1], vf, p1);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) mma8(o[d][qb], vf, pf[qb]);
             }
         }
         __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 16 + col;
         const float ltot = group4_sum(lrun[qb]);
         if (q >= T_) continue;
@@ -948,6 +960,9 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
 }
 
 constexpr size_t ts_fwd_lds() { return 2 * 2 * TS_BYTES; }
+#ifndef ATT_FWD_QB
+#define ATT_FWD_QB 2
+#endif
 constexpr size_t ts_dkv_lds() { return 2 * (2 * TS_BYTES + 512); }
 
 template <typename T, int HS> constexpr size_t fwd_lds() { return Tile<T, HS>::BYTES + Tile<T, 64>::BYTES; }
@@ -958,10 +973,12 @@ template <typename T, int HS>
 static hipError_t fwd_launch(const void* qkv, void* y, float* lse, int B, int T_, int H, hipStream_t s) {
     const float sc = kLog2e / sqrtf((float)HS);
     dim3 grid((T_ + 127) / 128, B * H);
-    if constexpr (sizeof(T) == 2 && HS == 64)
-        attn_fwd_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (bf16*)y, lse, T_, H, sc);
-    else
+    if constexpr (sizeof(T) == 2 && HS == 64) {
+        dim3 g4((T_ + 4 * 16 * ATT_FWD_QB - 1) / (4 * 16 * ATT_FWD_QB), B * H);
+        attn_fwd_ts_kernel<ATT_FWD_QB><<<g4, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (bf16*)y, lse, T_, H, sc);
+    } else {
         attn_fwd_kernel<T, HS><<<grid, dim3(A_THREADS), fwd_lds<T, HS>(), s>>>((const T*)qkv, (T*)y, lse, T_, H, sc);
+    }
     return hipGetLastError();
 }
 
@@ -1021,7 +1038,7 @@ void attention_setup() {
     (void)hipFuncSetAttribute((const void*)attn_bwd_dq_kernel<T, HS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds<T, HS>());
     ASET(bf16, 64) ASET(bf16, 32) ASET(float, 64) ASET(float, 32)
 #undef ASET
-    (void)hipFuncSetAttribute((const void*)attn_fwd_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
+    (void)hipFuncSetAttribute((const void*)attn_fwd_ts_kernel<ATT_FWD_QB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
     (void)hipFuncSetAttribute((const void*)attn_bwd_dq_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
     (void)hipFuncSetAttribute((const void*)attn_bwd_dkv_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_dkv_lds());
 }
