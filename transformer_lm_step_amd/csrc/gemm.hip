@@ -383,10 +383,29 @@ DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
     o[0] = (bf16)a; o[1] = (bf16)b; o[2] = (bf16)c; o[3] = (bf16)d;
     return o;
 }
+// Epilogues that read a second matrix (the residual, the saved pre-activation, or the output
+// itself when accumulating) get that input as a value loaded ahead of time, so that a thread's
+// loads of a whole staged half are in flight together instead of one after each store.
+template <int EPI> struct EpiIn { typedef float4 T; };
+template <> struct EpiIn<EPI_GELU_BWD> { typedef bf16x4 T; };
+template <int EPI>
+DEV bool epi_reads(const GemmArgs& p) {
+    return EPI == EPI_BIAS_RESID_F32 || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
+}
+// 1 if the 4 columns n..n+3 of row m take the vector path
+DEV bool epi_vec(const GemmArgs& p, int m, int n) { return m < p.M && p.vec && n + 3 < p.N; }
+template <int EPI>
+DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
+    if constexpr (EPI == EPI_BIAS_RESID_F32) return *(const float4*)(p.resid + (int64_t)m * p.ldr + n);
+    else if constexpr (EPI == EPI_GELU_BWD) return *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+    else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
+}
+
 // Epilogue on 4 consecutive columns n..n+3 of row m (v = accumulators): vector accesses when
 // the 4 columns are inside the matrix and the rows are 16-byte friendly, else per element.
+// `in` is epi_load(p, m, n) on the vector path of an epilogue that reads (unused otherwise).
 template <int EPI>
-DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4) {
+DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename EpiIn<EPI>::T& in) {
     if (m >= p.M) return;
     const float v[4] = {v4.x, v4.y, v4.z, v4.w};
     const int64_t o = (int64_t)m * p.ldc + n;
@@ -402,7 +421,7 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4) {
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(p.alpha * v[0] + bias[0], p.alpha * v[1] + bias[1],
                                                    p.alpha * v[2] + bias[2], p.alpha * v[3] + bias[3]);
         } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            const float4 rr = *(const float4*)(p.resid + (int64_t)m * p.ldr + n);
+            const float4 rr = in;
             *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0] + bias[0], rr.y + v[1] + bias[1],
                                                       rr.z + v[2] + bias[2], rr.w + v[3] + bias[3]);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
@@ -411,12 +430,12 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4) {
             *(bf16x4*)((bf16*)p.C2 + o) = to_bf16x4(gelu_f((float)u[0]), gelu_f((float)u[1]), gelu_f((float)u[2]),
                                                     gelu_f((float)u[3]));
         } else if constexpr (EPI == EPI_GELU_BWD) {
-            const bf16x4 a = *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+            const bf16x4 a = in;
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
                                                    v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
         } else if constexpr (EPI == EPI_F32) {
             float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (p.beta) old = *(const float4*)((const float*)p.C + o);
+            if (p.beta) old = in;
             *(float4*)((float*)p.C + o) = make_float4(old.x + p.alpha * v[0], old.y + p.alpha * v[1],
                                                       old.z + p.alpha * v[2], old.w + p.alpha * v[3]);
         } else {  // EPI_PARTIAL
@@ -458,10 +477,23 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
                       int lane, int tid) {
     constexpr int LDW = BN + 4;            // floats per staged row
     constexpr int CPR = BN / 4;            // 4-column chunks per row
+    constexpr int NIT = 64 * CPR / GTHREADS;  // chunks per thread and half
+    static_assert(64 * CPR % GTHREADS == 0, "whole chunks per thread");
+    typedef typename EpiIn<EPI>::T In;
     float* st = (float*)smem;
+    const bool reads = epi_reads<EPI>(p);
     __syncthreads();                       // every wave is done reading the last K tile
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        In in[NIT];
+        if (reads) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int k = tid + it * GTHREADS, r = k / CPR, c4 = k - r * CPR;
+                const int m = m0 + 64 * h + r, n = n0 + 4 * c4;
+                if (epi_vec(p, m, n)) in[it] = epi_load<EPI>(p, m, n);
+            }
+        }
         if (wm == h) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
@@ -471,10 +503,10 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
                         make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
         __syncthreads();
-#pragma unroll 4
-        for (int k = tid; k < 64 * CPR; k += GTHREADS) {
-            const int r = k / CPR, c4 = k - r * CPR;
-            epi4<EPI>(p, m0 + 64 * h + r, n0 + 4 * c4, *(const float4*)(st + r * LDW + 4 * c4));
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int k = tid + it * GTHREADS, r = k / CPR, c4 = k - r * CPR;
+            epi4<EPI>(p, m0 + 64 * h + r, n0 + 4 * c4, *(const float4*)(st + r * LDW + 4 * c4), in[it]);
         }
         __syncthreads();
     }
