@@ -436,7 +436,7 @@ hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s) {
 // dwte[idx[r]] += dx[r] summed in ascending r per id, dwpe[t] (+)= sum_b dx[b,t].
 // The gradients of repeated ids add ("Code you'll write" ties wte to lm_head; chapter
 // 1:06:18-1:13:27: the two uses' gradients add up on the one tensor).
-// 1) one workgroup sorts the (id, row) keys of a chunk of <= 16384 rows in LDS (bitonic),
+// 1) one workgroup sorts the (id, row) keys of a chunk of <= 16384 rows (bitonic),
 //    cuts the sorted list into segments (same id, <= SEG rows, aligned to SEG) and runs
 //    (same id), 2) every segment's rows are summed in order into a partial row,
 // 3) every run adds its segments' partials in order to its wte row.
@@ -461,70 +461,130 @@ size_t embed_backward_scratch_bytes(int rows, int C) {
     return b;
 }
 
+constexpr int EB_PER = EB_CHUNK / EB_THREADS;  // keys per thread (16)
+
+// Exclusive prefix sums of two per-thread counts over the workgroup; also returns the totals.
+DEV void eb_block_scan(int& a, int& b, int& ta, int& tb, int* wa, int* wb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int ia = a, ib = b;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int xa = __shfl_up(ia, o), xb = __shfl_up(ib, o);
+        if (lane >= o) { ia += xa; ib += xb; }
+    }
+    if (lane == 63) { wa[wave] = ia; wb[wave] = ib; }
+    __syncthreads();
+    int pa = 0, pb = 0;
+    ta = 0; tb = 0;
+    for (int w = 0; w < EB_THREADS / 64; ++w) {
+        if (w < wave) { pa += wa[w]; pb += wb[w]; }
+        ta += wa[w]; tb += wb[w];
+    }
+    a = pa + ia - a;
+    b = pb + ib - b;
+}
+
+// Bitonic sort of EB_CHUNK keys (id << 14 | row; padding keys are all ones) held 16 per
+// thread in registers: partners closer than 16 positions are in the same thread, closer than
+// 1024 in the same wave (exchanged with lane shuffles); only the passes with partners in other
+// waves go through LDS (double-buffered, one barrier each).
 __global__ void __launch_bounds__(EB_THREADS) eb_sort_kernel(const int32_t* __restrict__ idx, int n,
                                                              EbMeta* meta, int32_t* __restrict__ srow,
                                                              int32_t* __restrict__ seg_begin, int32_t* __restrict__ run_id,
                                                              int32_t* __restrict__ run_seg) {
-    extern __shared__ uint32_t keys[];  // [np2]
-    __shared__ int cnt_s[EB_THREADS], cnt_r[EB_THREADS];
-    int np2 = 1;
-    while (np2 < n) np2 <<= 1;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < np2; i += EB_THREADS)
-        keys[i] = i < n ? ((uint32_t)idx[i] << 14) | (uint32_t)i : 0xFFFFFFFFu;
-    __syncthreads();
-    for (int k = 2; k <= np2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < np2; i += EB_THREADS) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t a = keys[i], b = keys[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+    extern __shared__ uint32_t keys[];  // [2][EB_CHUNK]
+    __shared__ int wa[EB_THREADS / 64], wb[EB_THREADS / 64];
+    const int tid = threadIdx.x, base = tid * EB_PER;
+    uint32_t v[EB_PER];
+#pragma unroll
+    for (int e = 0; e < EB_PER; ++e) {
+        const int i = base + e;
+        v[e] = i < n ? ((uint32_t)idx[i] << 14) | (uint32_t)i : 0xFFFFFFFFu;
+    }
+    int buf = 0;
+    for (int k = 2; k <= EB_CHUNK; k <<= 1) {
+        // partners 16 or more positions away: the thread's 16 keys move as one block
+        const bool up = (base & k) == 0;
+        for (int j = k >> 1; j >= EB_PER; j >>= 1) {
+            const bool keep_min = ((base & j) == 0) == up;
+            uint32_t w[EB_PER];
+            if (j < EB_PER * 64) {
+                const int lm = j / EB_PER;
+#pragma unroll
+                for (int e = 0; e < EB_PER; ++e) w[e] = (uint32_t)__shfl_xor((int)v[e], lm);
+            } else {
+                uint32_t* kb = keys + buf * EB_CHUNK;
+#pragma unroll
+                for (int e = 0; e < EB_PER; e += 4)
+                    *(uint4*)(kb + base + e) = make_uint4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+                __syncthreads();
+                const int pb = base ^ j;
+#pragma unroll
+                for (int e = 0; e < EB_PER; e += 4) {
+                    const uint4 q = *(const uint4*)(kb + pb + e);
+                    w[e] = q.x; w[e + 1] = q.y; w[e + 2] = q.z; w[e + 3] = q.w;
+                }
+                buf ^= 1;
+            }
+#pragma unroll
+            for (int e = 0; e < EB_PER; ++e) v[e] = keep_min ? min(v[e], w[e]) : max(v[e], w[e]);
+        }
+        // partners inside the thread (distances 8, 4, 2, 1, those below k)
+#pragma unroll
+        for (int j = EB_PER / 2; j > 0; j >>= 1) {
+            if (j < k) {
+#pragma unroll
+                for (int e = 0; e < EB_PER; ++e) {
+                    if ((e & j) == 0) {
+                        const bool asc = ((base + e) & k) == 0;
+                        const uint32_t a = v[e], b = v[e | j];
+                        if ((a > b) == asc) { v[e] = b; v[e | j] = a; }
+                    }
                 }
             }
-            __syncthreads();
         }
     }
-    // each thread owns a contiguous range of sorted positions
-    const int per = (n + EB_THREADS - 1) / EB_THREADS;
-    const int i0 = tid * per;
-    int i1 = i0 + per;
-    if (i1 > n) i1 = n;
+    // the key before this thread's first position (the sorted order is now v of thread t at
+    // positions 16t + e)
+    uint32_t* kb = keys + buf * EB_CHUNK;
+    kb[base + EB_PER - 1] = v[EB_PER - 1];
+    __syncthreads();
+    const uint32_t before = tid > 0 ? kb[base - 1] : 0xFFFFFFFFu;
     int cs = 0, cr = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t id = keys[i] >> 14;
-        const bool run = i == 0 || (keys[i - 1] >> 14) != id;
-        const bool seg = run || (i % EB_SEG) == 0;
-        cs += seg;
-        cr += run;
-    }
-    cnt_s[tid] = cs;
-    cnt_r[tid] = cr;
-    __syncthreads();
-    // exclusive scans (thread 0, sequential over 1024 entries: cheap next to the sort)
-    if (tid == 0) {
-        int a = 0, b = 0;
-        for (int t = 0; t < EB_THREADS; ++t) {
-            const int x = cnt_s[t], y = cnt_r[t];
-            cnt_s[t] = a; cnt_r[t] = b;
-            a += x; b += y;
+    uint32_t prev = before;
+#pragma unroll
+    for (int e = 0; e < EB_PER; ++e) {
+        const int i = base + e;
+        if (i < n) {
+            const bool run = i == 0 || (prev >> 14) != (v[e] >> 14);
+            const bool seg = run || (i % EB_SEG) == 0;
+            cs += seg;
+            cr += run;
         }
-        meta->nseg = a;
-        meta->nrun = b;
-        seg_begin[a] = n;
-        run_seg[b] = a;
+        prev = v[e];
     }
-    __syncthreads();
-    int s = cnt_s[tid] - 1, r = cnt_r[tid] - 1;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = keys[i];
-        const uint32_t id = key >> 14;
-        const bool run = i == 0 || (keys[i - 1] >> 14) != id;
-        const bool seg = run || (i % EB_SEG) == 0;
-        if (seg) { ++s; seg_begin[s] = i; }
-        if (run) { ++r; run_id[r] = (int32_t)id; run_seg[r] = s; }
-        srow[i] = (int32_t)(key & 0x3FFF);
+    int ts, tr;
+    eb_block_scan(cs, cr, ts, tr, wa, wb);
+    if (tid == 0) {
+        meta->nseg = ts;
+        meta->nrun = tr;
+        seg_begin[ts] = n;
+        run_seg[tr] = ts;
+    }
+    int sg = cs - 1, r = cr - 1;
+    prev = before;
+#pragma unroll
+    for (int e = 0; e < EB_PER; ++e) {
+        const int i = base + e;
+        if (i < n) {
+            const uint32_t id = v[e] >> 14;
+            const bool run = i == 0 || (prev >> 14) != id;
+            const bool seg = run || (i % EB_SEG) == 0;
+            if (seg) { ++sg; seg_begin[sg] = i; }
+            if (run) { ++r; run_id[r] = (int32_t)id; run_seg[r] = sg; }
+            srow[i] = (int32_t)(v[e] & 0x3FFF);
+        }
+        prev = v[e];
     }
 }
 
@@ -589,9 +649,7 @@ hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, floa
     float* part = (float*)((char*)scratch + off);
     for (int r0 = 0; r0 < rows; r0 += EB_CHUNK) {
         const int n = rows - r0 < EB_CHUNK ? rows - r0 : EB_CHUNK;
-        int np2 = 1;
-        while (np2 < n) np2 <<= 1;
-        hipLaunchKernelGGL(eb_sort_kernel, dim3(1), dim3(EB_THREADS), (size_t)np2 * 4, s, idx + r0, n, meta, srow,
+        hipLaunchKernelGGL(eb_sort_kernel, dim3(1), dim3(EB_THREADS), (size_t)2 * EB_CHUNK * 4, s, idx + r0, n, meta, srow,
                            seg_begin, run_id, run_seg);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -610,8 +668,9 @@ hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, floa
 }
 
 void rows_setup() {
-    // the id sort keeps up to EB_CHUNK 4-byte keys in LDS next to its static scan arrays
-    (void)hipFuncSetAttribute((const void*)eb_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, EB_CHUNK * 4);
+    // the id sort exchanges keys through two LDS buffers of EB_CHUNK 4-byte keys
+    (void)hipFuncSetAttribute((const void*)eb_sort_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              2 * EB_CHUNK * 4);
 }
 
 // ================================================================== gradient norm + AdamW
