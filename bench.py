@@ -11,7 +11,7 @@ GPT-2 initialization. Prints one JSON line.
               events on the library's stream during the timed steps: algorithmic FLOPs or
               bytes per launch / mean launch time, against the MI355X peak
   kernels     ms per step of every kernel class (same live timing)
-  cpu_baseline  the CPU oracle (float32 numpy) on one 1024-token sequence of the same
+  cpu_baseline  the CPU oracle (float32 numpy) on one sequence of the same
               model, forward + backward + AdamW, on this host's cores
 """
 from __future__ import annotations
@@ -36,11 +36,13 @@ def model_flops_per_token(w, n_params):
 
 
 def class_costs(w, B, n_params, n_decay):
-    """Algorithmic cost of each kernel class per step: ('flop', total) or ('byte', total)."""
+    """Algorithmic cost of each kernel class per step: ('flop', total) or ('byte', total).
+    A step is w.micro_steps forward/backward passes of B sequences and one optimizer update."""
     BT, C, F, Vp, L, T, H = B * w.seq_len, w.n_embd, w.mlp_hidden, w.padded_vocab_size, w.n_layer, w.seq_len, w.n_head
     es = 2  # bf16 storage
+    k = w.micro_steps
     attn_fwd = 2 * 2 * B * H * (T * (T + 1) / 2) * (C // H)            # QK^T and PV, causal half
-    return {
+    per_micro = {
         "gemm_qkv": ("flop", 2 * BT * 3 * C * C * L),
         "gemm_attn_proj": ("flop", 2 * BT * C * C * L),
         "gemm_fc": ("flop", 2 * BT * F * C * L),
@@ -55,14 +57,16 @@ def class_costs(w, B, n_params, n_decay):
         "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * 4 + BT * C * es + 8 * BT)),
         "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 * 4 + BT * C * es + 8 * BT)),
         "cross_entropy": ("byte", 2 * BT * Vp * es),
-        "adamw": ("byte", n_params * 28 + n_decay * 2),
-        "grad_norm": ("byte", n_params * 4),
         "embed_fwd": ("byte", BT * C * 4 * 3),
     }
+    costs = {c: (kind, total * k) for c, (kind, total) in per_micro.items()}
+    costs["adamw"] = ("byte", n_params * 28 + n_decay * 2)
+    costs["grad_norm"] = ("byte", n_params * 4)
+    return costs
 
 
 def cpu_baseline(w):
-    """Time the CPU oracle (float32) on one 1024-token sequence: forward, backward, AdamW."""
+    """Time the CPU oracle (float32) on one sequence of the workload: forward, backward, AdamW."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info

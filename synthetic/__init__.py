@@ -16,6 +16,10 @@ chapter 2:06:39):
 * ``gpt2_step``   L=12, H=12, C=768,  T=1024, B=16, V=50257, Vp=50304, full step
 * ``gpt2_accum``  as gpt2_step, 32 micro-steps per optimizer step (2**19 tokens)
 * ``gpt2_xl``     L=48, H=25, C=1600, T=1024, B=4,  V=50257, Vp=50304, full step
+* ``gpt2_ctx2048`` the 124M widths at GPT-3's context: block_size = T = 2048, B=32 per
+  micro-step, 8 micro-steps per optimizer step (2**19 tokens, about half a million), the
+  setting chapter 3:43:45-3:59:10 names for matching GPT-3 (and chapter 2:14:58: GPT-3 mainly
+  doubles GPT-2's context)
 
 Token streams: the lecture's data (Tiny Shakespeare, FineWeb-Edu) is not available, so a
 seeded finite Zipf(1.1) law over the real vocabulary stands in for natural-language token
@@ -85,6 +89,8 @@ WORKLOADS: Dict[str, Workload] = {
                            micro_steps=32, lr=6e-4 * 101 / 715, seed_base=4),
     "gpt2_xl": Workload("gpt2_xl", 48, 25, 1600, 1024, 50257, 50304, 4, 1024, "bf16", "zipf",
                         seed_base=5),
+    "gpt2_ctx2048": Workload("gpt2_ctx2048", 12, 12, 768, 2048, 50257, 50304, 32, 2048, "bf16", "zipf",
+                             micro_steps=8, lr=6e-4 * 101 / 715, seed_base=6),
 }
 
 

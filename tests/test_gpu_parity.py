@@ -223,6 +223,60 @@ def test_full_step_b16_invariants():
     assert torch.equal(logits[:b], logits2[:b])
 
 
+def test_ctx2048_two_layers_bf16():
+    """GPT-3's context (block_size = T = 2048) at the 124M widths, 2 layers, one sequence:
+    loss and every gradient against the oracle."""
+    note("ctx2048 L=2 bf16 B=1")
+    params, batches, ref_loss, ref_g, _ = oracle_step("gpt2_ctx2048", (("n_layer", 2),), 1, 1, True, False)
+    w = synthetic.workload("gpt2_ctx2048", n_layer=2)
+    st = make_step(w, "bf16", max_batch=1)
+    st.set_params(params)
+    loss, _ = st.forward(*batches[0])
+    assert abs(loss - ref_loss) <= 2e-2
+    st.backward(1.0, False)
+    _grads_cosine(st, ref_g)
+
+
+def test_full_ctx2048_b32_invariants():
+    """The 2048-context micro-step at its real size (B=32, T=2048: 65,536 rows, so the logits
+    hold more than 2^31 elements): a sampled sequence's logits against the oracle, the
+    initial-loss closed form, bitwise determinism of backward, bitwise causality at t=1500."""
+    note("124M bf16 ctx2048 full B=32")
+    w = synthetic.workload("gpt2_ctx2048")
+    params = synthetic.init_params(w)
+    (x, y), = synthetic.micro_batches(w, 1)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    loss, logits = st.forward(x, y, want_logits=True)
+    assert math.isfinite(loss)
+    b = 29
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x[b:b + 1], y[b:b + 1], want_cache=False)
+    assert cosine(logits[b].cpu().numpy(), ref["logits"][0]) >= 0.999
+    z = ref["logits"][0]
+    closed = math.log(w.padded_vocab_size) + z.var(axis=-1).mean() / 2
+    assert abs(loss - closed) <= 0.05
+    st.backward(1.0, False)
+    g1 = torch.empty(st.n_params, dtype=torch.float32, device="cuda")
+    G.gpt2_get_grads(st.h, g1.data_ptr(), 1)
+    assert torch.isfinite(g1).all()
+    st.forward(x, y)
+    st.backward(1.0, False)
+    g2 = torch.empty_like(g1)
+    G.gpt2_get_grads(st.h, g2.data_ptr(), 1)
+    assert torch.equal(g1, g2), "backward is not bitwise deterministic"
+    del g1, g2
+    x2 = x.copy()
+    t = 1500
+    x2[b, t + 1] = (x2[b, t + 1] + 7) % w.vocab_size
+    lb = logits[b].clone()
+    lrest = logits[b + 1:].clone()
+    del logits
+    _, logits2 = st.forward(x2, y, want_logits=True, want_loss=False)
+    assert torch.equal(lb[:t + 1], logits2[b, :t + 1])
+    assert not torch.equal(lb[t + 1:], logits2[b, t + 1:])
+    assert torch.equal(lrest, logits2[b + 1:])
+
+
 def test_zero_wte_exact_cross_entropy():
     """wte = 0: every logit is 0, so the loss is ln(50304) up to fp32 rounding."""
     note("zero wte exact CE")
