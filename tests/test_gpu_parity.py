@@ -277,6 +277,74 @@ def test_full_ctx2048_b32_invariants():
     assert torch.equal(lrest, logits2[b + 1:])
 
 
+def _state(st):
+    p = torch.empty(st.n_params, dtype=torch.float32, device="cuda")
+    m, v = torch.empty_like(p), torch.empty_like(p)
+    G.gpt2_get_params(st.h, p.data_ptr(), 1)
+    G.gpt2_get_moments(st.h, m.data_ptr(), v.data_ptr(), 1)
+    torch.cuda.synchronize()
+    return p, m, v
+
+
+def test_checkpoint_resume_bitwise(tmp_path):
+    """Full-state checkpoint and resume: 4 optimizer steps of 2 micro-steps each without a
+    break, against 2 steps, a saved state, the handle destroyed, a fresh handle with another
+    device initialization, the state loaded and the last 2 steps: parameters and both AdamW
+    moments bitwise equal. Restoring the parameters without the moments must not match (the
+    check has teeth), and a state does not load into a handle of another model shape."""
+    from transformer_lm_step_amd import checkpoint as ck
+    note("checkpoint resume 124M widths L=4 B=2")
+    w = synthetic.workload("gpt2_step", n_layer=4, batch=2)
+    params = synthetic.init_params(w, randomize_affine=True)
+    batches = synthetic.micro_batches(w, 8)
+
+    def run(st, s0, s1, pos):
+        for s in range(s0, s1):
+            for i in range(2):
+                x, y = batches[pos]
+                pos += 1
+                st.forward(x, y)
+                st.backward(0.5, i > 0)
+            st.adamw_step(G.gpt2_cosine_lr(s, 6e-4, 6e-5, 2, 10), t=s + 1)
+        return pos
+
+    a = make_step(w, "bf16")
+    a.set_params(params)
+    run(a, 0, 4, 0)
+    pa, ma, va = _state(a)
+    a.close()
+
+    b = make_step(w, "bf16")
+    b.set_params(params)
+    pos = run(b, 0, 2, 0)
+    p2, _, _ = _state(b)
+    path = str(tmp_path / "state.npz")
+    ck.save(b, path, adam_t=2, data_pos=pos, extra={"note": "after 2 steps"})
+    b.close()
+    del b
+
+    c = make_step(w, "bf16", seed=77)
+    got = ck.load(c, path)
+    assert got == {"adam_t": 2, "data_pos": 4, "extra": {"note": "after 2 steps"}}
+    run(c, got["adam_t"], 4, got["data_pos"])
+    pc, mc, vc = _state(c)
+    assert not torch.equal(pc, p2), "the last two steps changed nothing"
+    assert torch.equal(pa, pc) and torch.equal(ma, mc) and torch.equal(va, vc)
+    c.close()
+
+    d = make_step(w, "bf16", seed=78)
+    d.set_params(d.unpack(ck.read_state(path)["params"]))
+    run(d, 2, 4, 4)
+    pd, _, _ = _state(d)
+    assert not torch.equal(pa, pd), "moments made no difference to the resumed steps"
+    d.close()
+
+    e = make_step(synthetic.workload("tiny"), "fp32")
+    with pytest.raises(ValueError):
+        ck.load(e, path)
+    e.close()
+
+
 def test_zero_wte_exact_cross_entropy():
     """wte = 0: every logit is 0, so the loss is ln(50304) up to fp32 rounding."""
     note("zero wte exact CE")
