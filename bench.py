@@ -31,13 +31,15 @@ PEAK_FP32 = 157.3e12
 PEAK_HBM = 8.0e12                    # bytes/s
 
 
-def model_flops_per_token(w, n_params):
-    return 6 * n_params + 6 * w.n_layer * w.seq_len * w.n_embd
+def model_flops_per_token(w, n_params, mode="train"):
+    f = 6 * n_params + 6 * w.n_layer * w.seq_len * w.n_embd
+    return f // 3 if mode == "eval" else f     # forward only: 2N + 2LTC
 
 
-def class_costs(w, B, n_params, n_decay):
+def class_costs(w, B, n_params, n_decay, mode="train"):
     """Algorithmic cost of each kernel class per step: ('flop', total) or ('byte', total).
-    A step is w.micro_steps forward/backward passes of B sequences and one optimizer update."""
+    A step is w.micro_steps forward/backward passes of B sequences and one optimizer update
+    (mode "eval": one forward-only scoring pass, whose cross-entropy reads the logits once)."""
     BT, C, F, Vp, L, T, H = B * w.seq_len, w.n_embd, w.mlp_hidden, w.padded_vocab_size, w.n_layer, w.seq_len, w.n_head
     es = 2  # bf16 storage
     k = w.micro_steps
@@ -56,17 +58,20 @@ def class_costs(w, B, n_params, n_decay):
         "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
         "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * 4 + BT * C * es + 8 * BT)),
         "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 * 4 + BT * C * es + 8 * BT)),
-        "cross_entropy": ("byte", 2 * BT * Vp * es),
+        "cross_entropy": ("byte", (1 if mode == "eval" else 2) * BT * Vp * es),
         "embed_fwd": ("byte", BT * C * 4 * 3),
     }
+    if mode == "eval":
+        k = 1
     costs = {c: (kind, total * k) for c, (kind, total) in per_micro.items()}
     costs["adamw"] = ("byte", n_params * 28 + n_decay * 2)
     costs["grad_norm"] = ("byte", n_params * 4)
     return costs
 
 
-def cpu_baseline(w):
-    """Time the CPU oracle (float32) on one sequence of the workload: forward, backward, AdamW."""
+def cpu_baseline(w, mode="train"):
+    """Time the CPU oracle (float32) on one sequence of the workload: forward, backward, AdamW
+    (mode "eval": the forward with its per-position losses only)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -82,16 +87,20 @@ def cpu_baseline(w):
     t0 = time.perf_counter()
     steps = 0
     while True:
-        out = O.forward(params, w.n_layer, w.n_head, x, y, want_logits=False)
-        g = O.backward(params, w.n_layer, w.n_head, out["cache"], 1.0)
-        O.optimizer_step(params, g, m, v, steps + 1, 6e-4)
+        if mode == "eval":
+            O.forward(params, w.n_layer, w.n_head, x, y, want_logits=False, want_cache=False)
+        else:
+            out = O.forward(params, w.n_layer, w.n_head, x, y, want_logits=False)
+            g = O.backward(params, w.n_layer, w.n_head, out["cache"], 1.0)
+            O.optimizer_step(params, g, m, v, steps + 1, 6e-4)
         steps += 1
         el = time.perf_counter() - t0
         if el >= 10.0 or steps >= 3:
             break
     return {"value": steps * x.size / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{steps} x (1 sequence of {x.size} tokens: forward + backward + AdamW, float32 numpy), "
-                      f"{el:.1f} s"}
+            "sample": f"{steps} x (1 sequence of {x.size} tokens: "
+                      + ("forward with per-position losses" if mode == "eval" else "forward + backward + AdamW")
+                      + f", float32 numpy), {el:.1f} s"}
 
 
 def sources_sha256():
@@ -195,6 +204,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_step")
+    ap.add_argument("--mode", choices=("train", "eval"), default="train",
+                    help="eval: time forward-only scoring (gpt2_evaluate, the validation-loss form) of "
+                         "one micro-batch instead of the training step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
@@ -237,6 +249,11 @@ def main():
     step_no = [0]
 
     def step():
+        if args.mode == "eval":
+            j = step_no[0] % nb
+            G.gpt2_evaluate(h, xs[j].data_ptr(), ys[j].data_ptr(), None, B, T, None, None, d_loss.data_ptr())
+            step_no[0] += 1
+            return
         for i in range(k):
             j = (step_no[0] * k + i) % nb
             G.gpt2_forward(h, xs[j].data_ptr(), ys[j].data_ptr(), B, T, None, d_loss.data_ptr() + 4 * i)
@@ -260,7 +277,7 @@ def main():
             ms, n = G.gpt2_timing_get(h, c)
             if n:
                 kernels[c] = {"ms_per_step": ms / nrep, "launches_per_step": n / nrep}
-    costs = class_costs(w, B, n_params, n_decay)
+    costs = class_costs(w, B, n_params, n_decay, args.mode)
     single = [c for c in ("gemm_lm_head", "gemm_lm_head_dx", "gemm_lm_head_dw", "gemm_fc", "gemm_qkv",
                           "gemm_attn_proj", "gemm_mlp_proj", "attn_fwd", "cross_entropy", "adamw",
                           "layernorm_fwd") if c in kernels]
@@ -290,11 +307,13 @@ def main():
                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant),
                     "launch_ms": round(ms / n, 4), "per_launch": per_launch,
                     "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
-    loss = float(d_loss.sum().item()) / k
+    if args.mode == "eval":
+        k = 1
+    loss = float(d_loss[:k].sum().item()) / k
     ms_step = el / args.steps * 1e3
     tokens = B * T * k
     value = tokens / (el / args.steps)
-    fpt = model_flops_per_token(w, n_params)
+    fpt = model_flops_per_token(w, n_params, args.mode)
     mfu = value * fpt / PEAK_BF16
     for c, d in kernels.items():
         if c in costs:
@@ -303,14 +322,16 @@ def main():
             d["achieved"] = round(rate / (1e12 if kind == "flop" else 1e9), 2)
             d["unit"] = "TFLOP/s" if kind == "flop" else "GB/s"
     out = {
-        "metric": "training tokens/sec and MFU, GPT-2 124M B=16 T=1024 bf16, 1 MI355X"
-        if args.workload == "gpt2_step" else f"training tokens/sec, {args.workload}",
+        "metric": ("training tokens/sec and MFU, GPT-2 124M B=16 T=1024 bf16, 1 MI355X"
+                   if args.workload == "gpt2_step" else f"training tokens/sec, {args.workload}")
+        if args.mode == "train" else f"evaluation tokens/sec (forward-only scoring), {args.workload}",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: GPT-2 L={w.n_layer} H={w.n_head} C={w.n_embd}, B={B}, T={T}, "
                                f"vocab {w.vocab_size} padded to {w.padded_vocab_size}, "
-                               f"{k} micro-step(s) + AdamW per step",
+                               + (f"{k} micro-step(s) + AdamW per step" if args.mode == "train"
+                                  else "one forward-only scoring pass (no backward, no update) per step"),
                    "global_batch": B * k, "seq_len": T, "parallelism": "single GPU"},
         "mfu": round(mfu, 4), "model_flops_per_token": fpt, "peak_flops": PEAK_BF16,
         "loss": round(loss, 5), "roofline": roofline, "kernels": kernels,
@@ -325,7 +346,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, args.mode)
     print(json.dumps(out))
     st.close()
 

@@ -145,6 +145,27 @@ float* gpt2_grads_device(gpt2_t* h);
 int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T,
                  float* d_logits, float* d_loss, float* h_loss);
 
+/* Forward-only evaluation: the validation loss and completion scoring of the lecture notes
+ * (chapter 3:22:33-3:28:16: the loss averaged over validation batches with no backward pass;
+ * chapter 3:28:16-3:41:50: each candidate row is the shared context followed by one ending,
+ * padded to a common length, and the row whose ending tokens have the lowest mean
+ * cross-entropy is the prediction). Runs the forward over B sequences of T tokens and the
+ * per-position cross-entropy of the targets (as gpt2_forward, without forming its gradient),
+ * then reduces it per sequence over the positions the mask selects.
+ *   d_idx, d_targets  int32 [B, T] device; the target of position t is the token that
+ *              follows it, as in gpt2_forward (copied into the workspace; reusable at return)
+ *   d_mask     uint8 [B, T] device or NULL: nonzero selects a position; NULL selects all
+ *   d_row_sum  float [B] device or NULL: sum of the selected positions' losses per sequence
+ *   d_row_mean float [B] device or NULL: that sum over the number of selected positions
+ *              (0 for a sequence with none selected)
+ *   d_loss     float device scalar or NULL: mean loss over every selected position of the
+ *              batch (without a mask, exactly the loss gpt2_forward reports for these inputs)
+ * Sums are formed in double in a fixed order (deterministic). Nothing synchronizes. The call
+ * overwrites the saved activations: a following gpt2_backward fails with GPT2_ESTATE until
+ * gpt2_forward runs again. Gradients and optimizer state are untouched. */
+int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask, int32_t B,
+                  int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss);
+
 /* Backward pass of the last forward (which must have had targets):
  *   grads = (accumulate ? grads : 0) + grad_scale * d loss / d params
  * grad_scale is the 1/micro_steps factor of gradient accumulation (chapter 2:34:49-2:46:43:

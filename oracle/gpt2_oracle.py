@@ -218,9 +218,27 @@ def forward(params: Dict[str, np.ndarray], n_layer: int, n_head: int,
         if want_cache:
             cache["probs"] = probs
     out = {"loss": loss, "cache": cache if want_cache else None}
+    if targets is not None:
+        out["losses"] = losses.reshape(B, T)
     if want_logits:
         out["logits"] = logits.reshape(B, T, -1)
     return out
+
+
+def masked_row_losses(losses: np.ndarray, mask: Optional[np.ndarray] = None):
+    """Forward-only scores ([LVN] chapter 3:22:33-3:28:16, the validation loss: the mean loss
+    with no backward pass; chapter 3:28:16-3:41:50, completion scoring: a row's score is the
+    mean cross-entropy over the tokens its mask marks, the lowest score wins).
+
+    losses: per-position cross-entropy [B, T] (``forward(...)["losses"]``); mask: [B, T],
+    nonzero selects (None: all). Returns (row_sum [B], row_mean [B], mean over every selected
+    position of the batch); a row with nothing selected has mean 0, as does an empty batch."""
+    sel = np.ones(losses.shape, dtype=bool) if mask is None else np.asarray(mask) != 0
+    row_sum = np.where(sel, losses, 0.0).sum(axis=-1)
+    count = sel.sum(axis=-1)
+    row_mean = np.where(count > 0, row_sum / np.maximum(count, 1), 0.0)
+    total = row_sum.sum() / count.sum() if count.sum() > 0 else 0.0
+    return row_sum, row_mean, total
 
 
 def backward(params: Dict[str, np.ndarray], n_layer: int, n_head: int, cache, grad_scale: float = 1.0):

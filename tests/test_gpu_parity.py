@@ -345,6 +345,92 @@ def test_checkpoint_resume_bitwise(tmp_path):
     e.close()
 
 
+def test_evaluate_tiny_fp32_matches_oracle():
+    """Forward-only scores in fp32 check mode: per-row sums and means over a ragged mask (one
+    row selects nothing, one row everything) and the masked batch mean against the oracle
+    (1e-4 relative); without a mask the batch mean is bitwise the loss gpt2_forward reports."""
+    note("evaluate tiny fp32")
+    w = synthetic.workload("tiny")
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    B, T = x.shape
+    mask = (np.random.default_rng(11).random((B, T)) < 0.3).astype(np.uint8)
+    mask[1] = 0
+    mask[2] = 1
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x, y, want_cache=False)
+    r_sum, r_mean, r_tot = O.masked_row_losses(ref["losses"], mask)
+    st = make_step(w, "fp32")
+    st.set_params(params)
+    s, m, tot = st.evaluate(x, y, mask)
+    assert rel_max(s, r_sum) <= 1e-4 and rel_max(m, r_mean) <= 1e-4
+    assert s[1] == 0.0 and m[1] == 0.0
+    assert abs(tot - r_tot) <= 1e-4 * abs(r_tot)
+    _, _, tot_all = st.evaluate(x, y)
+    loss, _ = st.forward(x, y)
+    assert tot_all == loss
+
+
+def test_evaluate_completion_rows_bf16():
+    """Completion-style scoring at the 124M widths (2 layers, bf16): four rows share a 60-token
+    context and end in 5 to 20 different tokens, zero-padded to T = 96, the mask on the
+    positions whose targets are the ending's tokens. Row means against the oracle within the
+    bf16 loss bar, and the same lowest row wherever the oracle's margin exceeds twice that bar.
+    Gradients are untouched and a backward after the call is refused."""
+    note("evaluate completion rows bf16")
+    w = synthetic.workload("gpt2_step", n_layer=2, batch=4, seq_len=96)
+    params = synthetic.init_params(w, randomize_affine=True)
+    rng = np.random.default_rng(5)
+    ctx = rng.integers(0, w.vocab_size, 60)
+    rows = np.zeros((4, 97), dtype=np.int64)
+    mask = np.zeros((4, 96), dtype=np.uint8)
+    for r, n_end in enumerate((5, 12, 20, 9)):
+        toks = np.concatenate([ctx, rng.integers(0, w.vocab_size, n_end)])
+        rows[r, :toks.size] = toks
+        mask[r, ctx.size - 1:toks.size - 1] = 1
+    x, y = rows[:, :96].astype(np.int32), rows[:, 1:].astype(np.int32)
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x, y, want_cache=False)
+    _, r_mean, r_tot = O.masked_row_losses(ref["losses"], mask)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    st.forward(x, y)
+    st.backward(1.0, False)
+    g0 = torch.empty(st.n_params, dtype=torch.float32, device="cuda")
+    G.gpt2_get_grads(st.h, g0.data_ptr(), 1)
+    _, m, tot = st.evaluate(x, y, mask)
+    assert np.abs(m - r_mean).max() <= 2e-2, (m, r_mean)
+    assert abs(tot - r_tot) <= 2e-2
+    order = np.sort(r_mean)
+    if order[1] - order[0] > 4e-2:
+        assert int(np.argmin(m)) == int(np.argmin(r_mean))
+    g1 = torch.empty_like(g0)
+    G.gpt2_get_grads(st.h, g1.data_ptr(), 1)
+    assert torch.equal(g0, g1)
+    with pytest.raises(G.GPT2Error):
+        st.backward(1.0, False)
+
+
+def test_evaluate_full_b16():
+    """Forward-only scoring at the benchmarked size (B=16, T=1024, bf16), half the positions
+    masked at random: a sampled sequence's masked mean against the oracle; without a mask the
+    batch mean is bitwise the loss of the training forward."""
+    note("evaluate 124M bf16 full B=16")
+    w = synthetic.workload("gpt2_step")
+    params = synthetic.init_params(w)
+    (x, y), = synthetic.micro_batches(w, 1)
+    mask = (np.random.default_rng(3).random(x.shape) < 0.5).astype(np.uint8)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    s, m, _ = st.evaluate(x, y, mask)
+    b = 11
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x[b:b + 1], y[b:b + 1], want_cache=False)
+    _, r_mean, _ = O.masked_row_losses(ref["losses"], mask[b:b + 1])
+    assert abs(m[b] - r_mean[0]) <= 2e-2
+    assert np.all(np.isfinite(s)) and np.all(s > 0)
+    _, _, tot_all = st.evaluate(x, y)
+    loss, _ = st.forward(x, y)
+    assert tot_all == loss
+
+
 def test_zero_wte_exact_cross_entropy():
     """wte = 0: every logit is 0, so the loss is ln(50304) up to fp32 rounding."""
     note("zero wte exact CE")

@@ -219,6 +219,52 @@ def test_exact_cross_entropy_at_zero_wte():
     np.testing.assert_allclose(pad_rows, np.broadcast_to(hf.sum(0) / (50304 * n), pad_rows.shape), atol=1e-15)
 
 
+def test_masked_row_losses_hand_values():
+    """Completion scores on a hand-checked case: row 0 selects positions 1 and 2 (losses 2, 3:
+    sum 5, mean 2.5), row 1 selects nothing (0, 0), row 2 everything (sum 26, mean 6.5); the
+    batch mean is over the 6 selected positions: 31 / 6."""
+    losses = np.array([[1.0, 2.0, 3.0, 4.0], [5.0, 6.0, 7.0, 8.0], [5.0, 6.0, 7.0, 8.0]])
+    mask = np.array([[0, 1, 1, 0], [0, 0, 0, 0], [1, 1, 1, 1]], dtype=np.uint8)
+    row_sum, row_mean, total = O.masked_row_losses(losses, mask)
+    assert row_sum.tolist() == [5.0, 0.0, 26.0]
+    assert row_mean.tolist() == [2.5, 0.0, 6.5]
+    assert total == 31.0 / 6.0
+    assert int(np.argmin(row_mean[[0, 2]])) == 0
+    _, row_mean, total = O.masked_row_losses(losses)
+    assert row_mean.tolist() == [2.5, 6.5, 6.5] and total == losses.mean()
+    assert O.masked_row_losses(losses, np.zeros_like(mask))[2] == 0.0
+
+
+def test_eval_losses_zero_wte_and_no_mask():
+    """wte = 0: every position's loss is ln 50304, so every non-empty row mean is exactly that
+    and a row sum is its count times it; without a mask the batch mean is the forward's loss."""
+    w = synthetic.workload("gpt2_step", n_layer=1, batch=2, seq_len=16)
+    params = _f64(synthetic.init_params(w, randomize_affine=True))
+    (x, y), = synthetic.micro_batches(w, 1)
+    p0 = dict(params, wte=np.zeros_like(params["wte"]))
+    out = O.forward(p0, w.n_layer, w.n_head, x, y, want_cache=False)
+    mask = np.zeros((2, 16), dtype=np.uint8)
+    mask[0, 3:9] = 1
+    row_sum, row_mean, total = O.masked_row_losses(out["losses"], mask)
+    assert abs(row_mean[0] - math.log(50304)) <= 1e-12 and row_mean[1] == 0.0
+    assert abs(row_sum[0] - 6 * math.log(50304)) <= 1e-11 and abs(total - math.log(50304)) <= 1e-12
+    out = O.forward(params, w.n_layer, w.n_head, x, y, want_cache=False)
+    assert abs(O.masked_row_losses(out["losses"])[2] - out["loss"]) <= 1e-12 * out["loss"]
+
+
+def test_eval_losses_equal_prefix_forwards():
+    """Brute force: the loss at position t of a row equals the loss of a forward over that
+    row's first t + 1 tokens alone, scored at its last position (only the prefix matters)."""
+    w = _tiny()
+    params = _f64(synthetic.init_params(w, randomize_affine=True))
+    (x, y), = synthetic.micro_batches(w, 1)
+    full = O.forward(params, w.n_layer, w.n_head, x, y, want_cache=False)["losses"]
+    b = 2
+    for t in range(0, x.shape[1], 7):
+        one = O.forward(params, w.n_layer, w.n_head, x[b:b + 1, :t + 1], y[b:b + 1, :t + 1], want_cache=False)
+        assert abs(one["losses"][0, t] - full[b, t]) <= 1e-12
+
+
 def test_initial_loss_tiny_and_124m():
     for name, lo, hi in (("tiny", None, None), ("gpt2_step", None, None)):
         w = synthetic.workload(name, batch=1, seq_len=64) if name != "tiny" else _tiny()
@@ -365,3 +411,23 @@ def test_pins_catch_planted_mistakes(mistake, monkeypatch):
     except AssertionError:
         caught = True
     assert caught, mistake
+
+
+@pytest.mark.parametrize("mistake", ["count_all_positions", "mask_shifted"])
+def test_eval_pins_catch_planted_mistakes(mistake, monkeypatch):
+    """Plant a plausible mistake in the completion scores and check the hand-checked pin
+    rejects it: dividing by every position instead of the selected ones, or a mask applied one
+    position late (the shift between a token and the logits that predict it done twice)."""
+    good = O.masked_row_losses
+
+    def bad(losses, mask=None):
+        if mask is None:
+            return good(losses)
+        if mistake == "mask_shifted":
+            return good(losses, np.roll(np.asarray(mask), 1, axis=-1))
+        row_sum, _, _ = good(losses, mask)
+        return row_sum, row_sum / losses.shape[-1], row_sum.sum() / losses.size
+
+    monkeypatch.setattr(O, "masked_row_losses", bad)
+    with pytest.raises(AssertionError):
+        test_masked_row_losses_hand_values()

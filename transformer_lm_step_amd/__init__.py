@@ -59,6 +59,7 @@ _SIGS = {
     "gpt2_get_grads": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "gpt2_set_grads": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "gpt2_get_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
+    "gpt2_evaluate": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_set_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     "gpt2_params_device": (_P, [_P]),
     "gpt2_grads_device": (_P, [_P]),
@@ -192,6 +193,10 @@ def gpt2_forward(h, d_idx, d_targets, B, T, d_logits=None, d_loss=None, want_hos
     return hl.value if want_host_loss else None
 
 
+def gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum=None, d_row_mean=None, d_loss=None) -> None:
+    _check(_lib.gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss))
+
+
 def gpt2_backward(h, grad_scale: float, accumulate: int) -> None:
     _check(_lib.gpt2_backward(h, grad_scale, accumulate))
 
@@ -320,6 +325,25 @@ class GPT2Step:
                             want_host_loss=(targets is not None and want_loss))
         self._keep = (idx_d, tgt_d)
         return loss, logits
+
+    def evaluate(self, idx, targets, mask=None):
+        """Forward-only scoring: (row_sum [B], row_mean [B], loss) as host numpy values, with
+        the mask (bool/uint8 [B, T]) selecting the scored positions (None: all)."""
+        torch = self.torch
+        B, T = idx.shape
+
+        def dev(a, dt):
+            t = a if isinstance(a, torch.Tensor) else torch.from_numpy(a)
+            return t.to(self.device, dt).contiguous()
+
+        idx_d, tgt_d = dev(idx, torch.int32), dev(targets, torch.int32)
+        mask_d = dev(mask, torch.uint8) if mask is not None else None
+        out = torch.empty(2 * B + 1, dtype=torch.float32, device=self.device)
+        p = out.data_ptr()
+        gpt2_evaluate(self.h, idx_d.data_ptr(), tgt_d.data_ptr(), mask_d.data_ptr() if mask_d is not None else None,
+                      B, T, p, p + 4 * B, p + 8 * B)
+        o = out.cpu().numpy()
+        return o[:B].copy(), o[B:2 * B].copy(), float(o[2 * B])
 
     def backward(self, grad_scale=1.0, accumulate=False):
         gpt2_backward(self.h, grad_scale, 1 if accumulate else 0)

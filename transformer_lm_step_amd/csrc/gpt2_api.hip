@@ -167,6 +167,7 @@ struct Plan {
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
     size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dres_t, dln, datt, dqkv, du, Dbuf;
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
+    size_t mask, rowd;   // evaluation: copied mask, per-sequence double sums and counts
 };
 
 Plan make_plan(const gpt2_config* c) {
@@ -206,6 +207,8 @@ Plan make_plan(const gpt2_config* c) {
     P.logits = take(BT * Vp * es);
     P.loss_rows = take(BT * 4);
     P.loss = take(256);
+    P.mask = take(BT);
+    P.rowd = take((size_t)c->max_batch * 2 * 8);
     P.dres = take(BT * C * 4);
     P.dres_t = take(BT * C * es);
     P.dln = take(BT * C * 4);
@@ -234,7 +237,7 @@ Plan make_plan(const gpt2_config* c) {
 const char* kClasses[] = {"embed_fwd", "layernorm_fwd", "gemm_qkv", "attn_fwd", "gemm_attn_proj", "gemm_fc",
                           "gemm_mlp_proj", "gemm_lm_head", "cross_entropy", "loss_mean", "gemm_lm_head_dx",
                           "gemm_lm_head_dw", "layernorm_bwd", "ln_param_grad", "gemm_dw", "bias_grad", "gemm_dx",
-                          "attn_bwd", "embed_bwd", "grad_norm", "adamw", nullptr};
+                          "attn_bwd", "embed_bwd", "grad_norm", "adamw", "eval_rows", nullptr};
 
 }  // namespace
 
@@ -484,15 +487,11 @@ extern "C" float* gpt2_params_device(gpt2_t* h) { return h ? h->params() : nullp
 extern "C" float* gpt2_grads_device(gpt2_t* h) { return h ? h->grads() : nullptr; }
 
 // =================================================================== forward
-extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T,
-                            float* d_logits, float* d_loss, float* h_loss) {
-    if (!h || !d_idx) return set_error(GPT2_EINVAL, "null argument");
+// Embedding, the blocks, ln_f and the tied lm_head over B x T tokens whose ids are already in
+// the workspace; leaves the logits (storage type) in P.logits and every activation the
+// backward pass reads.
+static int forward_trunk(gpt2_t* h, int B, int T) {
     const gpt2_config& c = h->cfg;
-    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
-    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
-    if (!d_targets && (d_loss || h_loss)) return set_error(GPT2_EINVAL, "a loss needs targets");
-    if (!d_targets && !d_logits) return set_error(GPT2_EINVAL, "without targets, d_logits is required");
-    h->have_fwd = false;
     const int BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
     const int bf = h->bf16;
     const Layout& L = h->L;
@@ -500,10 +499,6 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
     float* prm = h->params();
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
-    int32_t* tgt = h->at<int32_t>(P.tgt);
-    HIPTRY(hipMemcpyAsync(idx, d_idx, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy idx");
-    if (d_targets) HIPTRY(hipMemcpyAsync(tgt, d_targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy targets");
-
     TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<float>(P.x_in[0]), B, T, C, s); }));
     for (int l = 0; l < c.n_layer; ++l) {
         TRY(run(h, "layernorm_fwd", [&] {
@@ -556,6 +551,28 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
         g.epi = EPI_BIAS_T; g.C = h->at<char>(P.logits); g.ldc = Vp;
         TRY(run(h, "gemm_lm_head", [&] { return gemm(g, bf, s); }));
     }
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T,
+                            float* d_logits, float* d_loss, float* h_loss) {
+    if (!h || !d_idx) return set_error(GPT2_EINVAL, "null argument");
+    const gpt2_config& c = h->cfg;
+    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
+    if (!d_targets && (d_loss || h_loss)) return set_error(GPT2_EINVAL, "a loss needs targets");
+    if (!d_targets && !d_logits) return set_error(GPT2_EINVAL, "without targets, d_logits is required");
+    h->have_fwd = false;
+    const int BT = B * T, Vp = c.padded_vocab_size;
+    const int bf = h->bf16;
+    const Plan& P = h->P;
+    hipStream_t s = h->stream;
+    int32_t* idx = h->at<int32_t>(P.idx);
+    int32_t* tgt = h->at<int32_t>(P.tgt);
+    HIPTRY(hipMemcpyAsync(idx, d_idx, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy idx");
+    if (d_targets) HIPTRY(hipMemcpyAsync(tgt, d_targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy targets");
+
+    TRY(forward_trunk(h, B, T));
     if (d_targets) {
         TRY(run(h, "cross_entropy", [&] {
             return cross_entropy(h->at<char>(P.logits), tgt, h->at<float>(P.loss_rows), d_logits, BT, Vp, bf, s);
@@ -573,6 +590,38 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
     } else {
         HIPTRY(convert_to_f32(h->at<char>(P.logits), d_logits, (int64_t)BT * Vp, bf, s), "logits");
     }
+    return GPT2_OK;
+}
+
+// =================================================================== evaluation
+extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask,
+                             int32_t B, int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss) {
+    if (!h || !d_idx || !d_targets) return set_error(GPT2_EINVAL, "null argument");
+    const gpt2_config& c = h->cfg;
+    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
+    h->have_fwd = false;   // the activations are overwritten and no gradient of the loss is formed
+    const int BT = B * T, Vp = c.padded_vocab_size;
+    const int bf = h->bf16;
+    const Plan& P = h->P;
+    hipStream_t s = h->stream;
+    int32_t* idx = h->at<int32_t>(P.idx);
+    int32_t* tgt = h->at<int32_t>(P.tgt);
+    uint8_t* mask = d_mask ? h->at<uint8_t>(P.mask) : nullptr;
+    HIPTRY(hipMemcpyAsync(idx, d_idx, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy idx");
+    HIPTRY(hipMemcpyAsync(tgt, d_targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy targets");
+    if (d_mask) HIPTRY(hipMemcpyAsync(mask, d_mask, (size_t)BT, hipMemcpyDeviceToDevice, s), "copy mask");
+    TRY(forward_trunk(h, B, T));
+    float* loss_rows = h->at<float>(P.loss_rows);
+    TRY(run(h, "cross_entropy", [&] {
+        return cross_entropy(h->at<char>(P.logits), tgt, loss_rows, nullptr, BT, Vp, bf, s, /*write_grad=*/0);
+    }));
+    // without a mask the batch mean is the training forward's loss, reduced the same way
+    TRY(run(h, "eval_rows", [&] {
+        return masked_row_loss(loss_rows, mask, B, T, h->at<double>(P.rowd), d_row_sum, d_row_mean,
+                               mask ? d_loss : nullptr, s);
+    }));
+    if (d_loss && !mask) TRY(run(h, "loss_mean", [&] { return mean_reduce(loss_rows, BT, d_loss, s); }));
     return GPT2_OK;
 }
 

@@ -71,10 +71,16 @@ hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, flo
                   float* out, int accumulate, float* scratch, hipStream_t s);
 int colsum_partial_floats(int rows, int n);
 
-// cross-entropy over rows of logits(T) [n_rows, Vp]: loss_rows[r] = lse - z[y]; logits are
-// overwritten by dz = (softmax - onehot) / n_rows; optional fp32 copy of the logits.
+// cross-entropy over rows of logits(T) [n_rows, Vp]: loss_rows[r] = lse - z[y]; with
+// write_grad the logits are overwritten by dz = (softmax - onehot) / n_rows; optional fp32
+// copy of the logits.
 hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows, float* logits_f32,
-                         int n_rows, int Vp, int is_bf16, hipStream_t s);
+                         int n_rows, int Vp, int is_bf16, hipStream_t s, int write_grad = 1);
+// per sequence b of B (T positions): sum, count and mean of loss_rows over the positions the
+// mask selects (mask null: all); rowd [2B] doubles (sum, count); row_sum / row_mean / total
+// may be null; total = mean over every selected position of the batch
+hipError_t masked_row_loss(const float* loss_rows, const uint8_t* mask, int B, int T, double* rowd,
+                           float* row_sum, float* row_mean, float* total, hipStream_t s);
 hipError_t convert_to_f32(const void* src, float* dst, int64_t n, int is_bf16, hipStream_t s);
 // mean of loss_rows -> *d_loss (single block, fixed order)
 hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s);

@@ -327,12 +327,14 @@ hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, flo
 
 // ================================================================== cross-entropy
 // Per row n of z [rows, Vp]: lse = log sum_j exp z_j (all Vp columns), loss_n = lse - z_{y_n},
-// then z is overwritten by dz = (softmax(z) - onehot(y)) / rows (F.cross_entropy with mean
-// reduction on the flattened logits). One workgroup per row, two passes (the second re-reads
-// the row from cache). The (max, sum) pairs are merged in a fixed order.
+// then (write_grad) z is overwritten by dz = (softmax(z) - onehot(y)) / rows (F.cross_entropy
+// with mean reduction on the flattened logits). One workgroup per row, two passes (the second
+// re-reads the row from cache; evaluation skips it). The (max, sum) pairs are merged in a fixed
+// order.
 template <typename T>
 __global__ void cross_entropy_kernel(T* __restrict__ z, const int32_t* __restrict__ targets,
-                                     float* __restrict__ loss_rows, float* __restrict__ z_f32, int rows, int Vp) {
+                                     float* __restrict__ loss_rows, float* __restrict__ z_f32, int rows, int Vp,
+                                     int write_grad) {
     constexpr int E = 16 / sizeof(T);
     __shared__ float smax[256 / 64], ssum[256 / 64];
     const int row = blockIdx.x;
@@ -378,6 +380,7 @@ __global__ void cross_entropy_kernel(T* __restrict__ z, const int32_t* __restric
     const float lse = M + __logf(S);
     const int y = targets[row];
     if (threadIdx.x == 0) loss_rows[row] = lse - to_f<T>(zr[y]);
+    if (!write_grad) return;
     __syncthreads();  // zr[y] read before any overwrite
     const float inv_n = 1.0f / (float)rows;
     for (int v = threadIdx.x; v < nvec; v += 256) {
@@ -394,10 +397,79 @@ __global__ void cross_entropy_kernel(T* __restrict__ z, const int32_t* __restric
 }
 
 hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows, float* logits_f32, int n_rows,
-                         int Vp, int is_bf16, hipStream_t s) {
+                         int Vp, int is_bf16, hipStream_t s, int write_grad) {
     if (Vp % 8) return hipErrorInvalidValue;
-    if (is_bf16) hipLaunchKernelGGL(cross_entropy_kernel<bf16>, dim3(n_rows), dim3(256), 0, s, (bf16*)logits, targets, loss_rows, logits_f32, n_rows, Vp);
-    else hipLaunchKernelGGL(cross_entropy_kernel<float>, dim3(n_rows), dim3(256), 0, s, (float*)logits, targets, loss_rows, logits_f32, n_rows, Vp);
+    if (is_bf16) hipLaunchKernelGGL(cross_entropy_kernel<bf16>, dim3(n_rows), dim3(256), 0, s, (bf16*)logits, targets, loss_rows, logits_f32, n_rows, Vp, write_grad);
+    else hipLaunchKernelGGL(cross_entropy_kernel<float>, dim3(n_rows), dim3(256), 0, s, (float*)logits, targets, loss_rows, logits_f32, n_rows, Vp, write_grad);
+    return hipGetLastError();
+}
+
+// ================================================================== evaluation reductions
+// Completion scoring ([LVN] chapter 3:28:16-3:41:50): every sequence b is scored by the
+// cross-entropy of the positions its mask selects (the ending's tokens): their sum, their
+// count and their mean (0 when the mask selects nothing). One workgroup per sequence; each
+// thread sums a strided set of positions in double, then a fixed tree. rowd keeps the double
+// sum and count per sequence for the batch total.
+constexpr int EVAL_THREADS = 256;
+__global__ void __launch_bounds__(EVAL_THREADS) masked_row_loss_kernel(
+    const float* __restrict__ loss, const uint8_t* __restrict__ mask, int T, double* __restrict__ rowd,
+    float* __restrict__ row_sum, float* __restrict__ row_mean) {
+    __shared__ double ss[EVAL_THREADS], sc[EVAL_THREADS];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    double sum = 0.0, cnt = 0.0;
+    for (int t = tid; t < T; t += EVAL_THREADS) {
+        const int64_t i = (int64_t)b * T + t;
+        if (!mask || mask[i]) {
+            sum += (double)loss[i];
+            cnt += 1.0;
+        }
+    }
+    ss[tid] = sum;
+    sc[tid] = cnt;
+    __syncthreads();
+    for (int o = EVAL_THREADS / 2; o > 0; o >>= 1) {
+        if (tid < o) {
+            ss[tid] += ss[tid + o];
+            sc[tid] += sc[tid + o];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        rowd[2 * b] = ss[0];
+        rowd[2 * b + 1] = sc[0];
+        if (row_sum) row_sum[b] = (float)ss[0];
+        if (row_mean) row_mean[b] = sc[0] > 0.0 ? (float)(ss[0] / sc[0]) : 0.f;
+    }
+}
+// mean over every selected position of the batch: sum_b sum_b / sum_b count_b (0 if none)
+__global__ void __launch_bounds__(EVAL_THREADS) masked_total_kernel(const double* __restrict__ rowd, int B,
+                                                                    float* __restrict__ out) {
+    __shared__ double ss[EVAL_THREADS], sc[EVAL_THREADS];
+    const int tid = threadIdx.x;
+    double sum = 0.0, cnt = 0.0;
+    for (int b = tid; b < B; b += EVAL_THREADS) {
+        sum += rowd[2 * b];
+        cnt += rowd[2 * b + 1];
+    }
+    ss[tid] = sum;
+    sc[tid] = cnt;
+    __syncthreads();
+    for (int o = EVAL_THREADS / 2; o > 0; o >>= 1) {
+        if (tid < o) {
+            ss[tid] += ss[tid + o];
+            sc[tid] += sc[tid + o];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *out = sc[0] > 0.0 ? (float)(ss[0] / sc[0]) : 0.f;
+}
+hipError_t masked_row_loss(const float* loss_rows, const uint8_t* mask, int B, int T, double* rowd, float* row_sum,
+                           float* row_mean, float* total, hipStream_t s) {
+    hipLaunchKernelGGL(masked_row_loss_kernel, dim3(B), dim3(EVAL_THREADS), 0, s, loss_rows, mask, T, rowd, row_sum,
+                       row_mean);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !total) return e;
+    hipLaunchKernelGGL(masked_total_kernel, dim3(1), dim3(EVAL_THREADS), 0, s, rowd, B, total);
     return hipGetLastError();
 }
 
