@@ -33,7 +33,7 @@ PEAK_HBM = 8.0e12                    # bytes/s
 
 def model_flops_per_token(w, n_params, mode="train"):
     f = 6 * n_params + 6 * w.n_layer * w.seq_len * w.n_embd
-    return f // 3 if mode == "eval" else f     # forward only: 2N + 2LTC
+    return f // 3 if mode in ("eval", "decode") else f     # forward only: 2N + 2LTC
 
 
 def class_costs(w, B, n_params, n_decay, mode="train"):
@@ -61,6 +61,14 @@ def class_costs(w, B, n_params, n_decay, mode="train"):
         "cross_entropy": ("byte", (1 if mode == "eval" else 2) * BT * Vp * es),
         "embed_fwd": ("byte", BT * C * 4 * 3),
     }
+    if mode == "decode":
+        # one new position per sequence: the products stream their bf16 weights (B rows are
+        # far too few to reuse them), the sampler reads each logits row in 5 passes
+        return {
+            "gemm_qkv": ("byte", 3 * C * C * es * L), "gemm_attn_proj": ("byte", C * C * es * L),
+            "gemm_fc": ("byte", F * C * es * L), "gemm_mlp_proj": ("byte", C * F * es * L),
+            "gemm_lm_head": ("byte", Vp * C * es), "topk_sample": ("byte", 5 * B * Vp * es),
+        }
     if mode == "eval":
         k = 1
     costs = {c: (kind, total * k) for c, (kind, total) in per_micro.items()}
@@ -86,6 +94,20 @@ def cpu_baseline(w, mode="train"):
     v = {k: np.zeros_like(a) for k, a in params.items()}
     t0 = time.perf_counter()
     steps = 0
+    if mode == "decode":
+        # the plain sampling loop: a forward over the whole prefix per new token, top-50 draw
+        rng = np.random.default_rng(0)
+        seq = list(x[0, :8])
+        while True:
+            z = O.forward(params, w.n_layer, w.n_head, np.array([seq]), None, want_cache=False)["logits"][0, -1]
+            seq.append(O.topk_sample(z, 50, rng.random())[0])
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or steps >= 32:
+                break
+        return {"value": steps / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"{steps} tokens of 1 sequence after an 8-token prompt (a float32 numpy forward over "
+                          f"the prefix per token, top-50 draw), {el:.1f} s"}
     while True:
         if mode == "eval":
             O.forward(params, w.n_layer, w.n_head, x, y, want_logits=False, want_cache=False)
@@ -204,9 +226,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_step")
-    ap.add_argument("--mode", choices=("train", "eval"), default="train",
+    ap.add_argument("--mode", choices=("train", "eval", "decode"), default="train",
                     help="eval: time forward-only scoring (gpt2_evaluate, the validation-loss form) of "
-                         "one micro-batch instead of the training step")
+                         "one micro-batch instead of the training step; decode: time key/value-cache "
+                         "decoding steps with top-50 sampling of the workload's B sequences after an "
+                         "8-token prompt (one step = one new token per sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
@@ -248,7 +272,26 @@ def main():
     h = st.h
     step_no = [0]
 
+    if args.mode == "decode":
+        prompt_len = 8
+        n_dec = args.warmup + max(1, min(5, args.steps)) + args.steps
+        if prompt_len + n_dec > T:
+            raise SystemExit(f"bench.py: {prompt_len} + {n_dec} decoding positions exceed block_size {T}")
+        gen = torch.Generator().manual_seed(w.seed_base + 3000)
+        uni = torch.rand((n_dec, B), generator=gen).to(dev)
+        toks = [xs[0][:, t].contiguous() for t in range(prompt_len)]
+        G.gpt2_decode_reset(h, B)
+        for t in range(prompt_len - 1):
+            G.gpt2_decode_step(h, toks[t].data_ptr())
+        bufs = [toks[prompt_len - 1], torch.empty(B, dtype=torch.int32, device=dev)]
+
     def step():
+        if args.mode == "decode":
+            i = step_no[0]
+            cur, nxt = bufs[i % 2], bufs[(i + 1) % 2]
+            G.gpt2_decode_step(h, cur.data_ptr(), None, 50, uni[i].data_ptr(), nxt.data_ptr())
+            step_no[0] += 1
+            return
         if args.mode == "eval":
             j = step_no[0] % nb
             G.gpt2_evaluate(h, xs[j].data_ptr(), ys[j].data_ptr(), None, B, T, None, None, d_loss.data_ptr())
@@ -280,7 +323,7 @@ def main():
     costs = class_costs(w, B, n_params, n_decay, args.mode)
     single = [c for c in ("gemm_lm_head", "gemm_lm_head_dx", "gemm_lm_head_dw", "gemm_fc", "gemm_qkv",
                           "gemm_attn_proj", "gemm_mlp_proj", "attn_fwd", "cross_entropy", "adamw",
-                          "layernorm_fwd") if c in kernels]
+                          "layernorm_fwd", "topk_sample") if c in kernels and c in costs]
     dominant = max(single, key=lambda c: kernels[c]["ms_per_step"]) if single else None
 
     # timed region: the dominant class keeps its HIP events (on the library's stream)
@@ -307,11 +350,11 @@ def main():
                     "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant),
                     "launch_ms": round(ms / n, 4), "per_launch": per_launch,
                     "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
-    if args.mode == "eval":
+    if args.mode != "train":
         k = 1
-    loss = float(d_loss[:k].sum().item()) / k
+    loss = float(d_loss[:k].sum().item()) / k if args.mode != "decode" else None
     ms_step = el / args.steps * 1e3
-    tokens = B * T * k
+    tokens = B * T * k if args.mode != "decode" else B
     value = tokens / (el / args.steps)
     fpt = model_flops_per_token(w, n_params, args.mode)
     mfu = value * fpt / PEAK_BF16
@@ -324,17 +367,22 @@ def main():
     out = {
         "metric": ("training tokens/sec and MFU, GPT-2 124M B=16 T=1024 bf16, 1 MI355X"
                    if args.workload == "gpt2_step" else f"training tokens/sec, {args.workload}")
-        if args.mode == "train" else f"evaluation tokens/sec (forward-only scoring), {args.workload}",
+        if args.mode == "train" else (f"evaluation tokens/sec (forward-only scoring), {args.workload}"
+                                      if args.mode == "eval" else
+                                      f"decoded tokens/sec (key/value cache, top-50 sampling), {args.workload}"),
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: GPT-2 L={w.n_layer} H={w.n_head} C={w.n_embd}, B={B}, T={T}, "
                                f"vocab {w.vocab_size} padded to {w.padded_vocab_size}, "
                                + (f"{k} micro-step(s) + AdamW per step" if args.mode == "train"
-                                  else "one forward-only scoring pass (no backward, no update) per step"),
+                                  else "one forward-only scoring pass (no backward, no update) per step"
+                                  if args.mode == "eval" else
+                                  f"one decoding step (one new token for each of B sequences, positions "
+                                  f"8..{8 + args.warmup + max(1, min(5, args.steps)) + args.steps - 1}) per step"),
                    "global_batch": B * k, "seq_len": T, "parallelism": "single GPU"},
         "mfu": round(mfu, 4), "model_flops_per_token": fpt, "peak_flops": PEAK_BF16,
-        "loss": round(loss, 5), "roofline": roofline, "kernels": kernels,
+        "loss": round(loss, 5) if loss is not None else None, "roofline": roofline, "kernels": kernels,
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }

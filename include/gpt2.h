@@ -166,6 +166,42 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int3
 int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask, int32_t B,
                   int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss);
 
+/* ---------------------------------------------------------------- incremental decoding */
+
+/* Sampling as the lecture notes do it (chapter 0:28:07-0:41:44 and the sampling code of
+ * chapter 3:22:33-3:28:16): the logits of the last position go through the softmax, the
+ * top_k most probable tokens are kept (50 there) and one of them is drawn in proportion to
+ * its probability; the token is appended and the loop repeats. Here the keys and values of
+ * the earlier positions stay in a cache, so each step runs the model on one new position per
+ * sequence. The cache lives in the handle's activation buffers: gpt2_forward and
+ * gpt2_evaluate overwrite it (a later step fails with GPT2_ESTATE until a reset), and
+ * decoding overwrites the activations a gpt2_backward would need. */
+#define GPT2_TOPK_MAX 64       /* largest top_k */
+#define GPT2_DECODE_MAX_T 8192 /* largest block_size that decoding supports */
+
+/* Start (or restart) B sequences with an empty cache (B <= max_batch). */
+int gpt2_decode_reset(gpt2_t* h, int32_t B);
+
+/* Append one token to each of the B sequences at position p = the number of steps since the
+ * reset (p < block_size) and compute the logits of that position. A prompt is fed one step
+ * per token; the outputs of all but its last step can be ignored.
+ *   d_tokens    int32 [B] device: the tokens at position p (copied; reusable at return)
+ *   d_logits    float [B, Vp] device or NULL: the logits (fp32 copy of the model's output)
+ *   top_k       1..GPT2_TOPK_MAX, used when any of the three outputs below is requested
+ *   d_uniform   float [B] device, each in [0, 1): the caller's random numbers (needed with d_next)
+ *   d_next      int32 [B] device or NULL: the drawn token: over the top_k logits (all Vp
+ *               columns compete, larger first, equal ones by lower token id), their softmax
+ *               p_1..p_k (the top-k probabilities renormalized), the first i whose cumulative
+ *               sum p_1 + .. + p_i exceeds d_uniform[b] (the last one if rounding leaves none)
+ *   d_topk_idx  int32 [B, top_k] device or NULL: the top_k token ids in that order
+ *   d_topk_prob float [B, top_k] device or NULL: their renormalized probabilities
+ * d_next may be the next step's d_tokens. Nothing synchronizes. */
+int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_logits, int32_t top_k, const float* d_uniform,
+                     int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob);
+
+/* Positions in the cache (-1 without a reset or after the cache was overwritten). */
+int32_t gpt2_decode_position(const gpt2_t* h);
+
 /* Backward pass of the last forward (which must have had targets):
  *   grads = (accumulate ? grads : 0) + grad_scale * d loss / d params
  * grad_scale is the 1/micro_steps factor of gradient accumulation (chapter 2:34:49-2:46:43:

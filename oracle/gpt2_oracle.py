@@ -241,6 +241,26 @@ def masked_row_losses(losses: np.ndarray, mask: Optional[np.ndarray] = None):
     return row_sum, row_mean, total
 
 
+def topk_sample(logits: np.ndarray, k: int, u: float):
+    """One draw of the sampling loop ([LVN] chapter 0:28:07-0:41:44 and the sampling code of
+    chapter 3:22:33-3:28:16): softmax over every column of the last position's logits, keep
+    the k most probable tokens, draw one in proportion to its probability.
+
+    Readings: equal probabilities are ordered by lower token id; the draw is the inverse CDF
+    of the uniform number u in [0, 1) over the k kept tokens in that order (the first whose
+    cumulative renormalized probability exceeds u). Returns (token, kept ids, their
+    renormalized probabilities)."""
+    z = np.asarray(logits, dtype=np.float64)
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    order = np.lexsort((np.arange(z.size), -p))        # larger probability first, then lower id
+    ids = order[:k]
+    kept = p[ids] / p[ids].sum()
+    cdf = np.cumsum(kept)
+    i = int(np.searchsorted(cdf, u, side="right"))
+    return int(ids[min(i, k - 1)]), ids, kept
+
+
 def backward(params: Dict[str, np.ndarray], n_layer: int, n_head: int, cache, grad_scale: float = 1.0):
     """Gradients of ``grad_scale * loss`` w.r.t. every parameter, by the chain rule.
 

@@ -431,6 +431,118 @@ def test_evaluate_full_b16():
     assert tot_all == loss
 
 
+def _decode(st, params, w, prompt, total, k, rng, check_logits):
+    """Feed the prompt [B, P] one token per step, then draw until `total` tokens. At every
+    step: check_logits(step logits [B, Vp] host, oracle-free), and the sampler against the
+    oracle's on the step's own logits (ids exact, probabilities 1e-5, the drawn token wherever
+    u is more than 1e-5 from a cumulative boundary). Returns the final tokens [B, total]."""
+    B, P = prompt.shape
+    seq = np.zeros((B, total), dtype=np.int64)
+    seq[:, :P] = prompt
+    st.decode_reset(B)
+    assert G.gpt2_decode_position(st.h) == 0
+    for t in range(total - 1):
+        u = rng.random(B).astype(np.float32)
+        logits, nxt, ids, probs = st.decode_step(seq[:, t].astype(np.int32), uniform=u, top_k=k)
+        lg = logits.cpu().numpy()
+        check_logits(t, seq[:, :t + 1], lg)
+        nxt, ids, probs = nxt.cpu().numpy(), ids.cpu().numpy(), probs.cpu().numpy()
+        for b in range(B):
+            tok, rids, rkept = O.topk_sample(lg[b], k, float(u[b]))
+            assert np.array_equal(ids[b], rids), (t, b)
+            np.testing.assert_allclose(probs[b], rkept, rtol=0, atol=1e-5)
+            if np.abs(np.cumsum(rkept) - u[b]).min() > 1e-5:
+                assert nxt[b] == tok, (t, b)
+        if t + 1 >= P:
+            seq[:, t + 1] = nxt
+    assert G.gpt2_decode_position(st.h) == total - 1
+    return seq
+
+
+def test_decode_tiny_fp32_matches_oracle():
+    """Key/value-cache decoding in fp32 check mode, 3 sequences, a 6-token prompt continued to
+    the full block of 64 positions with top-50 sampling: every step's logits against the
+    oracle's forward over the whole prefix (1e-4 relative), and the sampler as in _decode."""
+    note("decode tiny fp32")
+    w = synthetic.workload("tiny")
+    params = synthetic.init_params(w, randomize_affine=True)
+    p64 = f64(params)
+    st = make_step(w, "fp32", max_batch=3)
+    st.set_params(params)
+    rng = np.random.default_rng(21)
+    prompt = rng.integers(0, w.vocab_size, (3, 6))
+
+    def check(t, prefix, lg):
+        ref = O.forward(p64, w.n_layer, w.n_head, prefix, None, want_cache=False)["logits"][:, -1]
+        assert rel_max(lg, ref) <= 1e-4, t
+
+    seq = _decode(st, params, w, prompt, w.block_size, 50, rng, check)
+    # the last position of the block still fits; the cache then holds block_size positions
+    lg, _, _, _ = st.decode_step(seq[:, -1].astype(np.int32), uniform=np.zeros(3, np.float32))
+    check(w.block_size - 1, seq, lg.cpu().numpy())
+    with pytest.raises(G.GPT2Error):
+        st.decode_step(np.zeros(3, np.int32), uniform=np.zeros(3, np.float32))
+
+
+def test_decode_124m_bf16_five_sequences():
+    """The pages' sampling setup at the 124M size in bf16: 5 sequences, an 8-token prompt
+    continued to 30 tokens with top-50 sampling. Every step's logits against the oracle's
+    forward over the prefix (cosine >= 0.999 per sequence), the sampler as in _decode, and
+    the cached path against the library's full forward over the final tokens (cosine >=
+    0.9999 at every position)."""
+    note("decode 124M bf16 B=5")
+    w = synthetic.workload("gpt2_step")
+    params = synthetic.init_params(w)
+    p64 = f64(params)
+    st = make_step(w, "bf16", max_batch=5)
+    st.set_params(params)
+    rng = np.random.default_rng(8)
+    prompt = rng.integers(0, w.vocab_size, (5, 8))
+    steps = []
+
+    def check(t, prefix, lg):
+        ref = O.forward(p64, w.n_layer, w.n_head, prefix, None, want_cache=False)["logits"][:, -1]
+        for b in range(lg.shape[0]):
+            assert cosine(lg[b], ref[b]) >= 0.999, (t, b)
+        steps.append(lg)
+
+    seq = _decode(st, params, w, prompt, 30, 50, rng, check)
+    _, full = st.forward(seq[:, :29].astype(np.int32), None, want_logits=True)
+    full = full.cpu().numpy()
+    for t, lg in enumerate(steps):
+        for b in range(5):
+            assert cosine(lg[b], full[b, t]) >= 0.9999, (t, b)
+    assert G.gpt2_decode_position(st.h) == -1   # the forward overwrote the cache
+
+
+def test_decode_state_and_errors():
+    """Decoding needs a reset; B is bounded by max_batch; top_k by 1..64 and the vocabulary;
+    drawing needs the uniform numbers; k = 1 draws the argmax (lowest id among equal maxima)."""
+    note("decode errors")
+    w = synthetic.workload("tiny")
+    st = make_step(w, "fp32", max_batch=2)
+    st.set_params(synthetic.init_params(w))
+    tok = np.array([3, 5], dtype=np.int32)
+    with pytest.raises(G.GPT2Error):
+        st.decode_step(tok)
+    with pytest.raises(G.GPT2Error):
+        G.gpt2_decode_reset(st.h, 3)
+    st.decode_reset(2)
+    for bad_k in (0, 65):
+        with pytest.raises(G.GPT2Error):
+            st.decode_step(tok, uniform=np.zeros(2, np.float32), top_k=bad_k)
+    st.decode_reset(2)
+    d_tok = torch.from_numpy(tok).cuda()
+    d_next = torch.empty(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(G.GPT2Error):
+        G.gpt2_decode_step(st.h, d_tok.data_ptr(), None, 50, None, d_next.data_ptr())
+    st.decode_reset(2)
+    logits, nxt, ids, _ = st.decode_step(tok, uniform=np.array([0.99, 0.5], np.float32), top_k=1)
+    lg = logits.cpu().numpy()
+    assert nxt.cpu().numpy().tolist() == [int(np.argmax(lg[0])), int(np.argmax(lg[1]))]
+    assert ids.cpu().numpy()[:, 0].tolist() == nxt.cpu().numpy().tolist()
+
+
 def test_zero_wte_exact_cross_entropy():
     """wte = 0: every logit is 0, so the loss is ln(50304) up to fp32 rounding."""
     note("zero wte exact CE")

@@ -431,3 +431,72 @@ def test_eval_pins_catch_planted_mistakes(mistake, monkeypatch):
     monkeypatch.setattr(O, "masked_row_losses", bad)
     with pytest.raises(AssertionError):
         test_masked_row_losses_hand_values()
+
+
+# ----------------------------------------------------------------- sampling
+def test_topk_sample_hand_values():
+    """z = [1, 3, 3, 2, 0], k = 2: the kept tokens are 1 and 2 (equal, lower id first), each
+    with probability 1/2; u < 1/2 draws token 1, u >= 1/2 token 2; k = 1 is the argmax for any
+    u (the lowest id among equal maxima)."""
+    z = np.array([1.0, 3.0, 3.0, 2.0, 0.0])
+    tok, ids, kept = O.topk_sample(z, 2, 0.0)
+    assert ids.tolist() == [1, 2] and tok == 1
+    np.testing.assert_allclose(kept, [0.5, 0.5], rtol=0, atol=1e-15)
+    assert O.topk_sample(z, 2, 0.4999)[0] == 1
+    assert O.topk_sample(z, 2, 0.5)[0] == 2
+    assert O.topk_sample(z, 2, 0.9999999)[0] == 2
+    for u in (0.0, 0.3, 0.999):
+        assert O.topk_sample(z, 1, u)[0] == 1
+    # k = 3 keeps token 3 as well: probabilities e^3 : e^3 : e^2
+    _, ids, kept = O.topk_sample(z, 3, 0.0)
+    e = np.exp([3.0, 3.0, 2.0])
+    assert ids.tolist() == [1, 2, 3]
+    np.testing.assert_allclose(kept, e / e.sum(), rtol=1e-15)
+
+
+def test_topk_sample_matches_softmax_topk_renormalized():
+    """The kept probabilities are the k largest entries of the full softmax, renormalized, as
+    the pages compute them (softmax over all columns, top-k, then a draw proportional to the
+    kept probabilities); and over a fine grid of uniform numbers each kept token is drawn with
+    its probability."""
+    rng = np.random.default_rng(7)
+    z = rng.standard_normal(300) * 2.0
+    k = 50
+    tok, ids, kept = O.topk_sample(z, k, 0.5)
+    full = np.exp(z - z.max())
+    full /= full.sum()
+    top = np.sort(full)[::-1][:k]
+    np.testing.assert_allclose(kept, top / top.sum(), rtol=1e-12)
+    assert set(ids.tolist()) == set(np.argsort(-full)[:k].tolist())
+    n = 100000
+    counts = np.zeros(z.size)
+    for u in (np.arange(n) + 0.5) / n:
+        counts[O.topk_sample(z, k, u)[0]] += 1
+    np.testing.assert_allclose(counts[ids] / n, kept, atol=2.0 / n)
+    assert counts.sum() == counts[ids].sum()
+
+
+@pytest.mark.parametrize("mistake", ["ties_by_higher_id", "no_renormalization"])
+def test_sampling_pins_catch_planted_mistakes(mistake, monkeypatch):
+    good = O.topk_sample
+
+    def bad(logits, k, u):
+        z = np.asarray(logits, dtype=np.float64)
+        p = np.exp(z - z.max())
+        p /= p.sum()
+        if mistake == "ties_by_higher_id":
+            order = np.lexsort((-np.arange(z.size), -p))
+            ids = order[:k]
+            kept = p[ids] / p[ids].sum()
+        else:
+            ids = np.lexsort((np.arange(z.size), -p))[:k]
+            kept = p[ids]
+        cdf = np.cumsum(kept)
+        i = int(np.searchsorted(cdf, u, side="right"))
+        return int(ids[min(i, k - 1)]), ids, kept
+
+    monkeypatch.setattr(O, "topk_sample", bad)
+    with pytest.raises(AssertionError):
+        test_topk_sample_hand_values()
+    monkeypatch.setattr(O, "topk_sample", good)
+

@@ -60,6 +60,9 @@ _SIGS = {
     "gpt2_set_grads": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "gpt2_get_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     "gpt2_evaluate": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "gpt2_decode_reset": (ctypes.c_int, [_P, ctypes.c_int32]),
+    "gpt2_decode_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "gpt2_decode_position": (ctypes.c_int32, [_P]),
     "gpt2_set_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     "gpt2_params_device": (_P, [_P]),
     "gpt2_grads_device": (_P, [_P]),
@@ -195,6 +198,19 @@ def gpt2_forward(h, d_idx, d_targets, B, T, d_logits=None, d_loss=None, want_hos
 
 def gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum=None, d_row_mean=None, d_loss=None) -> None:
     _check(_lib.gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss))
+
+
+def gpt2_decode_reset(h, B: int) -> None:
+    _check(_lib.gpt2_decode_reset(h, B))
+
+
+def gpt2_decode_step(h, d_tokens, d_logits=None, top_k=50, d_uniform=None, d_next=None, d_topk_idx=None,
+                     d_topk_prob=None) -> None:
+    _check(_lib.gpt2_decode_step(h, d_tokens, d_logits, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob))
+
+
+def gpt2_decode_position(h) -> int:
+    return _lib.gpt2_decode_position(h)
 
 
 def gpt2_backward(h, grad_scale: float, accumulate: int) -> None:
@@ -344,6 +360,32 @@ class GPT2Step:
                       B, T, p, p + 4 * B, p + 8 * B)
         o = out.cpu().numpy()
         return o[:B].copy(), o[B:2 * B].copy(), float(o[2 * B])
+
+    def decode_reset(self, B):
+        gpt2_decode_reset(self.h, B)
+
+    def decode_step(self, tokens, uniform=None, top_k=50, want_logits=True):
+        """One decoding step for every cached sequence: returns (logits [B, Vp] fp32 tensor or
+        None, next [B] int32 tensor or None, topk ids [B, k], topk probs [B, k]) on the device;
+        sampling outputs only when ``uniform`` ([B] in [0, 1)) is given."""
+        torch = self.torch
+        tok = tokens if isinstance(tokens, torch.Tensor) else torch.from_numpy(tokens)
+        tok = tok.to(self.device, torch.int32).contiguous()
+        B = tok.numel()
+        logits = torch.empty((B, self.cfg.padded_vocab_size), dtype=torch.float32, device=self.device) \
+            if want_logits else None
+        nxt = ids = probs = u = None
+        if uniform is not None:
+            u = uniform if isinstance(uniform, torch.Tensor) else torch.from_numpy(uniform)
+            u = u.to(self.device, torch.float32).contiguous()
+            nxt = torch.empty(B, dtype=torch.int32, device=self.device)
+            ids = torch.empty((B, top_k), dtype=torch.int32, device=self.device)
+            probs = torch.empty((B, top_k), dtype=torch.float32, device=self.device)
+        gpt2_decode_step(self.h, tok.data_ptr(), logits.data_ptr() if logits is not None else None, top_k,
+                         u.data_ptr() if u is not None else None, nxt.data_ptr() if nxt is not None else None,
+                         ids.data_ptr() if ids is not None else None, probs.data_ptr() if probs is not None else None)
+        self._keep = (tok, u)
+        return logits, nxt, ids, probs
 
     def backward(self, grad_scale=1.0, accumulate=False):
         gpt2_backward(self.h, grad_scale, 1 if accumulate else 0)

@@ -237,7 +237,7 @@ Plan make_plan(const gpt2_config* c) {
 const char* kClasses[] = {"embed_fwd", "layernorm_fwd", "gemm_qkv", "attn_fwd", "gemm_attn_proj", "gemm_fc",
                           "gemm_mlp_proj", "gemm_lm_head", "cross_entropy", "loss_mean", "gemm_lm_head_dx",
                           "gemm_lm_head_dw", "layernorm_bwd", "ln_param_grad", "gemm_dw", "bias_grad", "gemm_dx",
-                          "attn_bwd", "embed_bwd", "grad_norm", "adamw", "eval_rows", nullptr};
+                          "attn_bwd", "embed_bwd", "grad_norm", "adamw", "eval_rows", "attn_decode", "topk_sample", nullptr};
 
 }  // namespace
 
@@ -252,6 +252,8 @@ struct gpt2 {
     // state of the last forward
     bool have_fwd = false;
     int B = 0, T = 0;
+    // incremental decoding: sequences in the key/value cache (0: no cache) and their length
+    int dec_B = 0, dec_pos = 0;
     // timing
     bool timing = false;
     std::string filter;
@@ -563,6 +565,7 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
     if (!d_targets && (d_loss || h_loss)) return set_error(GPT2_EINVAL, "a loss needs targets");
     if (!d_targets && !d_logits) return set_error(GPT2_EINVAL, "without targets, d_logits is required");
     h->have_fwd = false;
+    h->dec_B = 0;   // the forward overwrites the key/value cache
     const int BT = B * T, Vp = c.padded_vocab_size;
     const int bf = h->bf16;
     const Plan& P = h->P;
@@ -601,6 +604,7 @@ extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_t
     if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
     if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
     h->have_fwd = false;   // the activations are overwritten and no gradient of the loss is formed
+    h->dec_B = 0;
     const int BT = B * T, Vp = c.padded_vocab_size;
     const int bf = h->bf16;
     const Plan& P = h->P;
@@ -624,6 +628,110 @@ extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_t
     if (d_loss && !mask) TRY(run(h, "loss_mean", [&] { return mean_reduce(loss_rows, BT, d_loss, s); }));
     return GPT2_OK;
 }
+
+// =================================================================== incremental decoding
+extern "C" int gpt2_decode_reset(gpt2_t* h, int32_t B) {
+    if (!h) return set_error(GPT2_EINVAL, "handle is null");
+    const gpt2_config& c = h->cfg;
+    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    if (c.block_size > GPT2_DECODE_MAX_T)
+        return set_error(GPT2_EINVAL, "decoding supports block_size <= %d", GPT2_DECODE_MAX_T);
+    h->have_fwd = false;
+    h->dec_B = B;
+    h->dec_pos = 0;
+    return GPT2_OK;
+}
+
+// One new position of every cached sequence: the blocks run on B rows (one per sequence),
+// the qkv product writes its rows straight into the cache (row b*block_size + pos of the
+// layer's qkv buffer), and the attention reads the cache.
+extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_logits, int32_t top_k,
+                                const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob) {
+    if (!h || !d_tokens) return set_error(GPT2_EINVAL, "null argument");
+    if (!h->dec_B) return set_error(GPT2_ESTATE, "decoding needs gpt2_decode_reset first");
+    const gpt2_config& c = h->cfg;
+    const int B = h->dec_B, pos = h->dec_pos, Tmax = c.block_size;
+    if (pos >= Tmax) return set_error(GPT2_EINVAL, "the cache is full (block_size=%d positions)", Tmax);
+    const bool sample = d_next || d_topk_idx || d_topk_prob;
+    if (sample && (top_k < 1 || top_k > GPT2_TOPK_MAX || top_k > c.padded_vocab_size))
+        return set_error(GPT2_EINVAL, "top_k=%d outside [1, %d]", top_k, GPT2_TOPK_MAX);
+    if (d_next && !d_uniform) return set_error(GPT2_EINVAL, "drawing the next token needs d_uniform");
+    const int C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
+    const int bf = h->bf16;
+    const size_t es = bf ? 2 : 4;
+    const Layout& L = h->L;
+    const Plan& P = h->P;
+    float* prm = h->params();
+    hipStream_t s = h->stream;
+    int32_t* idx = h->at<int32_t>(P.idx);
+    HIPTRY(hipMemcpyAsync(idx, d_tokens, (size_t)B * 4, hipMemcpyDeviceToDevice, s), "copy tokens");
+    h->dec_B = 0;   // until this step has been enqueued completely
+    TRY(run(h, "embed_fwd", [&] {
+        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<float>(P.x_in[0]), B, 1, C, s);
+    }));
+    for (int l = 0; l < c.n_layer; ++l) {
+        TRY(run(h, "layernorm_fwd", [&] {
+            return layernorm_forward(h->at<float>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
+                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), B, C, bf, s);
+        }));
+        GemmDesc g;
+        g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
+        g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 0;
+        g.M = B; g.N = 3 * C; g.K = C;
+        g.epi = EPI_BIAS_T; g.C = h->at<char>(P.qkv[l]) + (size_t)pos * 3 * C * es; g.ldc = (int64_t)Tmax * 3 * C;
+        g.bias = prm + L.b_qkv[l];
+        TRY(run(h, "gemm_qkv", [&] { return gemm(g, bf, s); }));
+        TRY(run(h, "attn_decode", [&] {
+            return attention_decode(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), B, Tmax, pos, H, hs, bf, s);
+        }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.att[l]); g.lda = C;
+        g.B = h->wop(L.w_o[l]); g.ldb = C;
+        g.M = B; g.N = C; g.K = C;
+        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.resid = h->at<float>(P.x_in[l]); g.ldr = C;
+        TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
+        TRY(run(h, "layernorm_fwd", [&] {
+            return layernorm_forward(h->at<float>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
+                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), B, C, bf, s);
+        }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.h2[l]); g.lda = C;
+        g.B = h->wop(L.w_fc[l]); g.ldb = C;
+        g.M = B; g.N = F; g.K = C;
+        g.epi = EPI_BIAS_GELU; g.C = h->at<char>(P.u[l]); g.C2 = h->at<char>(P.a[l]); g.ldc = F; g.bias = prm + L.b_fc[l];
+        TRY(run(h, "gemm_fc", [&] { return gemm(g, bf, s); }));
+        g = GemmDesc();
+        g.A = h->at<char>(P.a[l]); g.lda = F;
+        g.B = h->wop(L.w_pr[l]); g.ldb = F;
+        g.M = B; g.N = C; g.K = F;
+        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.resid = h->at<float>(P.x_mid[l]); g.ldr = C;
+        TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
+    }
+    TRY(run(h, "layernorm_fwd", [&] {
+        return layernorm_forward(h->at<float>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
+                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), B, C, bf, s);
+    }));
+    {
+        GemmDesc g;
+        g.A = h->at<char>(P.hf); g.lda = C;
+        g.B = h->wop(L.wte); g.ldb = C;
+        g.M = B; g.N = Vp; g.K = C;
+        g.epi = EPI_BIAS_T; g.C = h->at<char>(P.logits); g.ldc = Vp;
+        TRY(run(h, "gemm_lm_head", [&] { return gemm(g, bf, s); }));
+    }
+    if (d_logits) HIPTRY(convert_to_f32(h->at<char>(P.logits), d_logits, (int64_t)B * Vp, bf, s), "logits");
+    if (sample)
+        TRY(run(h, "topk_sample", [&] {
+            return topk_sample(h->at<char>(P.logits), B, Vp, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob, bf, s);
+        }));
+    h->dec_B = B;
+    h->dec_pos = pos + 1;
+    return GPT2_OK;
+}
+
+extern "C" int32_t gpt2_decode_position(const gpt2_t* h) { return h && h->dec_B ? h->dec_pos : -1; }
 
 // =================================================================== backward
 extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {

@@ -114,4 +114,17 @@ hipError_t attention_backward(const void* qkv, const void* y, const void* dy, co
                               hipStream_t s);
 void attention_setup();
 
+// ------------------------------------------------------------------ incremental decoding
+// attention of the query at position pos of each of B sequences over the cached keys/values
+// at 0..pos; qkv rows (b, t) -> b*Tmax + t (3C wide), y(T) [B, C]
+hipError_t attention_decode(const void* qkv, void* y, int B, int Tmax, int pos, int H, int hs, int is_bf16,
+                            hipStream_t s);
+size_t attention_decode_lds(int hs, int Tmax);
+// top-k of each logits row (T) [B, Vp] (larger first, ties by lower id), their renormalized
+// softmax, and the inverse-CDF draw with u[b] in [0, 1); every output pointer may be null
+// except u when next is set
+constexpr int TOPK_MAX = 64;
+hipError_t topk_sample(const void* logits, int B, int Vp, int k, const float* u, int32_t* next, int32_t* topk_idx,
+                       float* topk_prob, int is_bf16, hipStream_t s);
+
 }  // namespace gpt2k
