@@ -67,7 +67,7 @@ def test_tiny_fp32_forward_backward(randomize):
     _grads_fp32_check(st, ref_g)
 
 
-@pytest.mark.parametrize("B,T", [(3, 50), (1, 1), (2, 64), (4, 17)])
+@pytest.mark.parametrize("B,T", [(3, 50), (1, 1), (2, 8), (2, 64), (4, 17)])
 def test_tiny_fp32_ragged(B, T):
     note(f"tiny fp32 ragged B={B} T={T}")
     w = synthetic.workload("tiny")
@@ -457,6 +457,25 @@ def _decode(st, params, w, prompt, total, k, rng, check_logits):
             seq[:, t + 1] = nxt
     assert G.gpt2_decode_position(st.h) == total - 1
     return seq
+
+
+def test_few_rows_bf16_forward():
+    """A forward of only 16 rows (B=2, T=8) at the 124M widths with 2 layers, bf16: the
+    products take the few-row path (every forward epilogue: bias, residual, GELU, and the
+    50304-column lm_head); logits (cosine >= 0.999) and loss (bf16 bar) against the oracle."""
+    note("few rows bf16 B=2 T=8")
+    w = synthetic.workload("gpt2_step", n_layer=2, batch=2, seq_len=8)
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x, y, want_cache=False)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    loss, logits = st.forward(x, y, want_logits=True)
+    assert abs(loss - ref["loss"]) <= 2e-2
+    lg = logits.cpu().numpy()
+    for b in range(2):
+        for t in range(8):
+            assert cosine(lg[b, t], ref["logits"][b, t]) >= 0.999, (b, t)
 
 
 def test_decode_tiny_fp32_matches_oracle():

@@ -109,8 +109,9 @@ hipError_t attention_decode(const void* qkv, void* y, int B, int Tmax, int pos, 
 // one if rounding leaves every cumulative sum at or below u).
 //
 // Selection: radix select of the k-th largest order-preserving 32-bit key in four 8-bit passes
-// (LDS histograms), then an ordered compaction (block scans in token order) of the keys above
-// it plus the lowest-id keys equal to it, then one wave sorts the k entries.
+// (LDS histograms), then an ordered compaction (block scans in
+// token order) of the keys above it plus the lowest-id keys equal to it, then one wave sorts
+// the k entries.
 constexpr int TK_THREADS = 1024;
 
 DEV uint32_t order_key(float f) {
@@ -139,12 +140,19 @@ DEV int block_excl_scan(int v, int* total, int* wsum) {
     return before + inc - v;
 }
 
-template <typename T>
+// IN_LDS (bf16 rows of at most TK_LDS_MAX ids): the row is first copied into LDS with 16-byte
+// loads, so the five passes below read LDS; otherwise they read the row from global memory.
+// Thread t owns the contiguous ids [per t, per t + per), so the compaction keeps token order.
+constexpr int TK_LDS_MAX = 65536;
+
+template <typename T, bool IN_LDS>
 __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __restrict__ logits, int Vp, int k,
                                                                  const float* __restrict__ u,
                                                                  int32_t* __restrict__ next,
                                                                  int32_t* __restrict__ topk_idx,
                                                                  float* __restrict__ topk_prob) {
+    constexpr int E = 16 / sizeof(T);
+    extern __shared__ __attribute__((aligned(16))) char tk_row[];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_state[3];
     __shared__ int wsum[TK_THREADS / 64];
@@ -152,14 +160,25 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
     __shared__ float sel_val[TOPK_MAX];
     const int b = blockIdx.x, tid = threadIdx.x;
     const T* z = logits + (int64_t)b * Vp;
+    const T* src = z;
+    if constexpr (IN_LDS) {
+        T* row = (T*)tk_row;
+#pragma unroll 8
+        for (int c = tid; c < Vp / E; c += TK_THREADS) *(uint4*)(row + c * E) = ld16(z + c * E);
+        __syncthreads();
+        src = row;
+    }
+    const int per = (Vp + TK_THREADS - 1) / TK_THREADS;
+    const int j0 = min(Vp, tid * per), j1 = min(Vp, j0 + per);
+    auto key_at = [&](int j) { return order_key(to_f<T>(src[j])); };
 
     uint32_t prefix = 0, mask = 0;
     int need = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
         if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int j = tid; j < Vp; j += TK_THREADS) {
-            const uint32_t key = order_key(to_f<T>(z[j]));
+        for (int j = j0; j < j1; ++j) {
+            const uint32_t key = key_at(j);
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
@@ -180,12 +199,10 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
         __syncthreads();
     }
     // prefix is now the k-th largest key; the keys above it and the `need` lowest-id keys equal
-    // to it are the selection. Thread tid owns the token ids [tid*per, tid*per + per).
-    const int per = (Vp + TK_THREADS - 1) / TK_THREADS;
-    const int j0 = tid * per, j1 = min(Vp, j0 + per);
+    // to it are the selection
     int n_gt = 0, n_eq = 0;
     for (int j = j0; j < j1; ++j) {
-        const uint32_t key = order_key(to_f<T>(z[j]));
+        const uint32_t key = key_at(j);
         n_gt += key > prefix;
         n_eq += key == prefix;
     }
@@ -195,13 +212,12 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
     const int pos0 = block_excl_scan(n_gt + eq_take, &tot, wsum);
     int p = pos0, eq_seen = 0;
     for (int j = j0; j < j1; ++j) {
-        const float v = to_f<T>(z[j]);
-        const uint32_t key = order_key(v);
+        const uint32_t key = key_at(j);
         bool take = key > prefix;
         if (key == prefix) take = eq_seen++ < eq_take;
         if (take) {
             sel_idx[p] = j;
-            sel_val[p] = v;
+            sel_val[p] = to_f<T>(src[j]);
             ++p;
         }
     }
@@ -219,7 +235,7 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
     }
     const int id = (int)(uint32_t)e;
     // the value again from the row (exact: the row is unchanged)
-    const float zv = lane < k ? to_f<T>(z[id]) : -INFINITY;
+    const float zv = lane < k ? to_f<T>(src[id]) : -INFINITY;
     const float zmax = __shfl(zv, 0);
     const float pr = lane < k ? expf(zv - zmax) : 0.f;
     float cdf = pr;
@@ -242,14 +258,21 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
 
 hipError_t topk_sample(const void* logits, int B, int Vp, int k, const float* u, int32_t* next, int32_t* topk_idx,
                        float* topk_prob, int is_bf16, hipStream_t s) {
-    if (k < 1 || k > TOPK_MAX || k > Vp) return hipErrorInvalidValue;
-    if (is_bf16)
-        topk_sample_kernel<bf16><<<dim3(B), dim3(TK_THREADS), 0, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx,
-                                                                       topk_prob);
+    if (k < 1 || k > TOPK_MAX || k > Vp || Vp % 8) return hipErrorInvalidValue;
+    const dim3 grid(B), blk(TK_THREADS);
+    if (is_bf16 && Vp <= TK_LDS_MAX)
+        topk_sample_kernel<bf16, true><<<grid, blk, (size_t)Vp * 2, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx,
+                                                                         topk_prob);
+    else if (is_bf16)
+        topk_sample_kernel<bf16, false><<<grid, blk, 0, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx, topk_prob);
     else
-        topk_sample_kernel<float><<<dim3(B), dim3(TK_THREADS), 0, s>>>((const float*)logits, Vp, k, u, next, topk_idx,
-                                                                        topk_prob);
+        topk_sample_kernel<float, false><<<grid, blk, 0, s>>>((const float*)logits, Vp, k, u, next, topk_idx, topk_prob);
     return hipGetLastError();
+}
+
+void decode_setup() {
+    (void)hipFuncSetAttribute((const void*)topk_sample_kernel<bf16, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              TK_LDS_MAX * 2);
 }
 
 }  // namespace gpt2k

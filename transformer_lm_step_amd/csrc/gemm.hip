@@ -705,6 +705,88 @@ static bool mm_ok(const GemmDesc& d, int ksplit_len) {
     return true;
 }
 
+// ====================================================================== skinny products
+// Products with few rows (M <= SK_MAX_M: one new position per sequence when decoding), both
+// operands k-contiguous, bf16 storage (the epilogue is the tiled path's): every weight row is
+// streamed once by one wave (lanes take consecutive 16-byte chunks of k), the M activation rows
+// come from cache, and each lane keeps M partial sums for its column. A fixed butterfly reduces
+// them across the wave; a workgroup's four columns (one per wave) then meet in LDS and go
+// through the same epilogue as the tiled path. (Splitting a column's k over several waves
+// measured slower: at k = 768 most of their lanes have no chunk.)
+constexpr int SK_MAX_M = 16;
+constexpr int SK_THREADS = 256;
+
+template <typename T, int EPI>
+__global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
+    constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
+    __shared__ float res[SK_MAX_M][4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n0 = blockIdx.x * 4, n = n0 + wave;
+    float acc[SK_MAX_M];
+#pragma unroll
+    for (int m = 0; m < SK_MAX_M; ++m) acc[m] = 0.f;
+    if (n < p.N) {
+        const T* w = (const T*)p.B + (int64_t)n * p.ldb;
+        // every row's load is issued before any use (rows past M repeat row M - 1; their sums
+        // are never stored), so a chunk costs one round trip, not one per row
+        const T* arow[SK_MAX_M];
+#pragma unroll
+        for (int m = 0; m < SK_MAX_M; ++m) arow[m] = (const T*)p.A + (int64_t)min(m, p.M - 1) * p.lda;
+#pragma unroll 2
+        for (int k = lane * E; k < p.K; k += 64 * E) {
+            const uint4 wr = ld16(w + k);
+            uint4 ar[SK_MAX_M];
+#pragma unroll
+            for (int m = 0; m < SK_MAX_M; ++m) ar[m] = ld16(arow[m] + k);
+            const T* we = (const T*)&wr;
+            float wf[E];
+#pragma unroll
+            for (int q = 0; q < E; ++q) wf[q] = to_f<T>(we[q]);
+#pragma unroll
+            for (int m = 0; m < SK_MAX_M; ++m) {
+                const T* ae = (const T*)&ar[m];
+                float s = 0.f;
+#pragma unroll
+                for (int q = 0; q < E; ++q) s += to_f<T>(ae[q]) * wf[q];
+                acc[m] += s;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < SK_MAX_M; ++m) acc[m] = wave_sum(acc[m]);
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < SK_MAX_M; ++m) res[m][wave] = acc[m];
+    }
+    __syncthreads();
+    const int m = threadIdx.x;
+    if (m < p.M) {
+        const float4 v = make_float4(res[m][0], res[m][1], res[m][2], res[m][3]);
+        typename EpiIn<EPI>::T in;
+        if (epi_reads<EPI>(p) && epi_vec(p, m, n0)) in = epi_load<EPI>(p, m, n0);
+        epi4<EPI>(p, m, n0, v, in);
+    }
+}
+
+template <typename T>
+static bool skinny_ok(const GemmDesc& d, int nsplit) {
+    constexpr int E = 16 / sizeof(T);
+    if (d.M > SK_MAX_M || d.a_layout != 0 || d.b_layout != 0 || nsplit != 1 || d.rowsum) return false;
+    if (d.N > 16384) return false;   // very wide products (the vocabulary) fill the GPU on the tiled path
+    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID_F32 && d.epi != EPI_BIAS_GELU) return false;
+    if (d.K % E || d.lda % E || d.ldb % E) return false;
+    return (((uintptr_t)d.A | (uintptr_t)d.B) & 15) == 0;
+}
+
+template <typename T>
+static hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t s) {
+    const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
+    if (epi == EPI_BIAS_T) gemm_skinny_kernel<T, EPI_BIAS_T><<<grid, blk, 0, s>>>(a);
+    else if (epi == EPI_BIAS_RESID_F32) gemm_skinny_kernel<T, EPI_BIAS_RESID_F32><<<grid, blk, 0, s>>>(a);
+    else gemm_skinny_kernel<T, EPI_BIAS_GELU><<<grid, blk, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     GemmArgs a{};
@@ -727,6 +809,9 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
                 al(d.resid) && al(d.aux) && al(d.partial);
     }
     int epi = d.epi;
+    if constexpr (sizeof(T) == 2) {
+        if (skinny_ok<T>(d, nsplit)) return launch_skinny<T>(a, epi, s);
+    }
     if (nsplit > 1) {
         // partials, then a fixed-order reduce into the fp32 output
         a.C = d.partial; a.ldc = d.N; a.part_stride = (int64_t)d.M * d.N;

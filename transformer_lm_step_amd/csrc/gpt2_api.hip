@@ -403,6 +403,7 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
         gemm_setup();
         attention_setup();
         rows_setup();
+        decode_setup();
         g_setup_done = true;
     }
     // parameters per the GPT-2 initialization, gradients and moments zero

@@ -126,5 +126,6 @@ size_t attention_decode_lds(int hs, int Tmax);
 constexpr int TOPK_MAX = 64;
 hipError_t topk_sample(const void* logits, int B, int Vp, int k, const float* u, int32_t* next, int32_t* topk_idx,
                        float* topk_prob, int is_bf16, hipStream_t s);
+void decode_setup();
 
 }  // namespace gpt2k
