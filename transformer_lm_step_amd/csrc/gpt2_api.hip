@@ -750,7 +750,9 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     hipStream_t s = h->stream;
     float* dres = h->at<float>(P.dres);
     char* dres_t = h->at<char>(P.dres_t);
-    float* dln = h->at<float>(P.dln);
+    // gradient of a LayerNorm's output, in the storage type: under the autocast recipe it is the
+    // bf16 input gradient of the following product, cast to fp32 where LayerNorm runs
+    char* dln = h->at<char>(P.dln);
     float* lnpart = h->at<float>(P.lnpart);
     float* cspart = h->at<float>(P.cspart);
     float* sumscr = h->at<float>(P.sumscr);
@@ -796,7 +798,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.A = h->at<char>(P.logits); g.lda = Vp; g.a_layout = 0;
         g.B = h->wop(L.wte); g.ldb = C; g.b_layout = 1;
         g.M = BT; g.N = C; g.K = Vp;
-        g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = grad_scale; g.beta = 0;
+        g.epi = EPI_BIAS_T; g.C = dln; g.ldc = C; g.alpha = grad_scale;
         TRY(run(h, "gemm_lm_head_dx", [&] { return gemm(g, bf, s); }));
         g = GemmDesc();
         g.A = h->at<char>(P.logits); g.lda = Vp; g.a_layout = 1;
@@ -824,7 +826,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             g.A = h->at<char>(P.du); g.lda = F; g.a_layout = 0;
             g.B = h->wop(L.w_fc[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = F;
-            g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
+            g.epi = EPI_BIAS_T; g.C = dln; g.ldc = C; g.alpha = 1.f;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
@@ -849,7 +851,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             g.A = h->at<char>(P.dqkv); g.lda = 3 * C; g.a_layout = 0;
             g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = 3 * C;
-            g.epi = EPI_F32; g.C = dln; g.ldc = C; g.alpha = 1.f; g.beta = 0;
+            g.epi = EPI_BIAS_T; g.C = dln; g.ldc = C; g.alpha = 1.f;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the attn.c_proj bias gradient)

@@ -53,8 +53,8 @@ hipError_t layernorm_forward(const float* x, const float* w, const float* b, voi
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s);
 // LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; dres_t = T copy of dres (may be
 // null); partial[blk][0:C] = sum dh*xhat, [C:2C] = sum dh, [2C:3C] = sum of the incoming dres
-// (zero without accumulate) over the block's rows.
-hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
+// (zero without accumulate) over the block's rows. dh is in the storage type T.
+hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
                               const float* w, float* dres, void* dres_t, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);

@@ -135,7 +135,7 @@ int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 
 // NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers
 template <typename T, int NV>
 __global__ void __launch_bounds__(256) layernorm_backward_kernel(
-    const float* __restrict__ dh, const float* __restrict__ x, const float* __restrict__ mean,
+    const T* __restrict__ dh, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres, T* __restrict__ dres_t,
     int accumulate, float* __restrict__ partial, int rows, int C) {
     extern __shared__ float sred[];  // [4][3C]
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     const int r0 = (blockIdx.x * 4 + wave) * LNB_ROWS;
     for (int row = r0; row < r0 + LNB_ROWS && row < rows; ++row) {
         const float mu = mean[row], r = rstd[row];
-        const float4* dr = (const float4*)(dh + (int64_t)row * C);
+        const T* dr = dh + (int64_t)row * C;
         const float4* xr = (const float4*)(x + (int64_t)row * C);
         float4* o = (float4*)(dres + (int64_t)row * C);
         float4 xh[NV], dxh[NV], old[NV];
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
             const int c = lane + 64 * j;
             xh[j] = dxh[j] = old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < nv) {
-                const float4 d = dr[c], xx = xr[c];
+                const float4 d = load4<T>(dr + 4 * c), xx = xr[c];
                 if (accumulate) old[j] = o[c];
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
 }
 
 template <typename T>
-static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const float* dh, const float* x,
+static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const T* dh, const float* x,
                                 const float* mean, const float* rstd, const float* w, float* dres, T* dres_t,
                                 int acc, float* partial, int rows, int C) {
 #define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<T, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
@@ -218,16 +218,16 @@ static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, cons
     return hipGetLastError();
 }
 
-hipError_t layernorm_backward(const float* dh, const float* x, const float* mean, const float* rstd,
+hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
                               const float* w, float* dres, void* dres_t, int accumulate_dres, float* partial,
                               int nblk, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     const size_t lds = 12 * (size_t)C * sizeof(float);
     if (is_bf16)
-        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, dh, x, mean, rstd, w, dres, (bf16*)dres_t,
+        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, x, mean, rstd, w, dres, (bf16*)dres_t,
                                    accumulate_dres, partial, rows, C);
-    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, dh, x, mean, rstd, w, dres, (float*)dres_t,
-                                accumulate_dres, partial, rows, C);
+    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, x, mean, rstd, w, dres,
+                                (float*)dres_t, accumulate_dres, partial, rows, C);
 }
 
 // Column sums of partial [np, n] (row stride `stride`), deterministic, in two launches:
