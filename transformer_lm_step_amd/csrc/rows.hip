@@ -820,8 +820,19 @@ DEV void store_shadow4(bf16* sh, int64_t i, const float4& pp) {
     b[0] = (bf16)pp.x; b[1] = (bf16)pp.y; b[2] = (bf16)pp.z; b[3] = (bf16)pp.w;
     ((bf16x4*)sh)[i] = b;
 }
-// Each thread updates float4 groups i and i + stride per iteration, all eight loads issued
-// before any arithmetic so two groups' memory latency overlaps.
+// Each thread updates AW_UNROLL float4 groups (i, i + stride, ...) per iteration, every load
+// issued before any arithmetic so their memory latency overlaps; every array is touched once,
+// so the accesses are non-temporal (no cache lines kept for them).
+constexpr int AW_UNROLL = 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+DEV float4 ntload(const float* p, int64_t i) {
+    const f32x4 v = __builtin_nontemporal_load((const f32x4*)p + i);
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+DEV void ntstore(float* p, int64_t i, const float4& v) {
+    const f32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (f32x4*)p + i);
+}
 __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ shadow, int64_t n4, int64_t n_decay4,
@@ -830,22 +841,23 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
     const float c = norm_coef[1];
     const float step = lr / bc1, inv_bc2_sqrt = 1.0f / bc2_sqrt, kd = 1.0f - lr * wd;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += 2 * stride) {
-        const int64_t j = i + stride;
-        const bool two = j < n4;
-        float4 p0 = ((float4*)p)[i], m0 = ((float4*)m)[i], v0 = ((float4*)v)[i];
-        const float4 g0 = ((const float4*)g)[i];
-        float4 p1, m1, v1, g1;
-        if (two) {
-            p1 = ((float4*)p)[j]; m1 = ((float4*)m)[j]; v1 = ((float4*)v)[j]; g1 = ((const float4*)g)[j];
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n4; i0 += AW_UNROLL * stride) {
+        float4 pp[AW_UNROLL], gg[AW_UNROLL], mm[AW_UNROLL], vv[AW_UNROLL];
+#pragma unroll
+        for (int u = 0; u < AW_UNROLL; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i < n4) {
+                pp[u] = ntload(p, i); mm[u] = ntload(m, i); vv[u] = ntload(v, i); gg[u] = ntload(g, i);
+            }
         }
-        adamw4(p0, g0, m0, v0, i < n_decay4 ? kd : 1.0f, c, beta1, beta2, eps, step, inv_bc2_sqrt);
-        ((float4*)p)[i] = p0; ((float4*)m)[i] = m0; ((float4*)v)[i] = v0;
-        if (shadow && i < n_decay4) store_shadow4(shadow, i, p0);
-        if (two) {
-            adamw4(p1, g1, m1, v1, j < n_decay4 ? kd : 1.0f, c, beta1, beta2, eps, step, inv_bc2_sqrt);
-            ((float4*)p)[j] = p1; ((float4*)m)[j] = m1; ((float4*)v)[j] = v1;
-            if (shadow && j < n_decay4) store_shadow4(shadow, j, p1);
+#pragma unroll
+        for (int u = 0; u < AW_UNROLL; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i < n4) {
+                adamw4(pp[u], gg[u], mm[u], vv[u], i < n_decay4 ? kd : 1.0f, c, beta1, beta2, eps, step, inv_bc2_sqrt);
+                ntstore(p, i, pp[u]); ntstore(m, i, mm[u]); ntstore(v, i, vv[u]);
+                if (shadow && i < n_decay4) store_shadow4(shadow, i, pp[u]);
+            }
         }
     }
 }
