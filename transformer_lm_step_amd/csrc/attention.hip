@@ -844,9 +844,10 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
 
 // dQ for 128 queries per workgroup (32 per wave), streaming 64-key chunks of K and V.
 __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+                                                                   const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
-                                                                   const float* __restrict__ D,
+                                                                   float* __restrict__ D,
                                                                    bf16* __restrict__ dqkv, int T_, int H, float sc,
                                                                    float scale) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][K | V]
@@ -868,17 +869,27 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
 
     bf16x8 qf[2][2], of[2][2];
     float L[2], Dq[2];
+    const bf16* yb = y + (int64_t)b * T_ * C;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int q = qw0 + qb * 16 + col;
         const bool ok = q < T_;
+        float dsum = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             qf[qb][ks] = ok ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
             of[qb][ks] = ok ? frag_global<bf16>(dyb + (int64_t)q * C + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+            // D = sum_d dO o O of this query row (the softmax-gradient correction term): this
+            // lane's 8 dimensions, then the 4 lane groups of the row
+            const bf16x8 yf = ok ? frag_global<bf16>(yb + (int64_t)q * C + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dsum += (float)of[qb][ks][e] * (float)yf[e];
         }
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
         L[qb] = ok ? lse[(int64_t)bh * T_ + q] * kLog2e : 0.f;
-        Dq[qb] = ok ? D[(int64_t)bh * T_ + q] : 0.f;
+        Dq[qb] = ok ? dsum : 0.f;
+        if (ok && g == 0) D[(int64_t)bh * T_ + q] = dsum;   // for the dK/dV kernel, which runs next
     }
     floatx4 dq[4][2];
 #pragma unroll
@@ -988,22 +999,25 @@ static hipError_t bwd_launch(const void* qkv, const void* y, const void* dy, con
     const float sc = kLog2e / sqrtf((float)HS);
     const float scale = 1.0f / sqrtf((float)HS);
     const int64_t n = (int64_t)B * T_ * H;
-    attn_bwd_pre_kernel<T, HS><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>((const T*)y, (const T*)dy, D,
-                                                                                      B * T_, T_, H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     dim3 grid((T_ + 127) / 128, B * H);
+    hipError_t e;
     if constexpr (sizeof(T) == 2 && HS == 64) {
+        // the dQ kernel forms D itself (from the dO and O rows it loads) and stores it for the
+        // dK/dV kernel, so it runs first and no separate pass over O and dO is needed
+        attn_bwd_dq_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (const bf16*)y,
+                                                                         (const bf16*)dy, lse, D, (bf16*)dqkv, T_, H,
+                                                                         sc, scale);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
         attn_bwd_dkv_ts_kernel<<<grid, dim3(A_THREADS), ts_dkv_lds(), s>>>((const bf16*)qkv, (const bf16*)dy, lse,
                                                                           (const float*)D, (bf16*)dqkv, T_, H, sc,
                                                                           scale);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        attn_bwd_dq_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (const bf16*)dy, lse,
-                                                                         (const float*)D, (bf16*)dqkv, T_, H, sc,
-                                                                         scale);
         return hipGetLastError();
     }
+    attn_bwd_pre_kernel<T, HS><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>((const T*)y, (const T*)dy, D,
+                                                                                      B * T_, T_, H);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     attn_bwd_dkv_kernel<T, HS><<<grid, dim3(A_THREADS), dkv_lds<T, HS>(), s>>>((const T*)qkv, (const T*)dy, lse,
                                                                               (const float*)D, (T*)dqkv, T_, H, sc, scale);
     e = hipGetLastError();
