@@ -18,6 +18,8 @@
 // backward uses the same device: dK/dV per key block (S = Q K^T so P sums over queries),
 // and dQ per query block (S^T again) -- two kernels instead of atomics, so dQ is
 // deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -788,24 +790,31 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col
-        const bool need_mask = (q0 < kw0 + 32) || (q0 + 64 > T_);
+        // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col. Only chunks
+        // that cross the diagonal or the end of the sequence are masked: the two forms are
+        // compiled separately, so the others carry no compares or selects.
+        auto p_ds = [&](auto masked) {
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
+            for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ql = qb * 16 + g * 4 + i;
-                const int q = q0 + ql;
-                const float L = sL[ql] * kLog2e, Dq = sD[ql];
+                for (int i = 0; i < 4; ++i) {
+                    const int ql = qb * 16 + g * 4 + i;
+                    const int q = q0 + ql;
+                    const float L = sL[ql] * kLog2e, Dq = sD[ql];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int key = kw0 + kb * 16 + col;
-                    float p = exp2_raw(fmaf(s[qb][kb][i], sc, -L));
-                    if (need_mask && !(key <= q && q < T_)) p = 0.f;
-                    s[qb][kb][i] = p;
-                    dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const int key = kw0 + kb * 16 + col;
+                        float p = exp2_raw(fmaf(s[qb][kb][i], sc, -L));
+                        if constexpr (decltype(masked)::value) {
+                            if (!(key <= q && q < T_)) p = 0.f;
+                        }
+                        s[qb][kb][i] = p;
+                        dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
+                    }
                 }
-            }
+        };
+        if ((q0 < kw0 + 32) || (q0 + 64 > T_)) p_ds(std::true_type{});
+        else p_ds(std::false_type{});
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -843,7 +852,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
 }
 
 // dQ for 128 queries per workgroup (32 per wave), streaming 64-key chunks of K and V.
-__global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+__global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
@@ -930,21 +939,27 @@ __global__ void __launch_bounds__(A_THREADS, 3) attn_bwd_dq_ts_kernel(const bf16
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col
-        const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
+        // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col; masked and unmasked forms
+        // compiled separately, as in the dK/dV kernel
+        auto ds = [&](auto masked) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const int q = qw0 + qb * 16 + col;
+                for (int qb = 0; qb < 2; ++qb) {
+                    const int q = qw0 + qb * 16 + col;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = k0 + kb * 16 + g * 4 + i;
-                    float p = exp2_raw(fmaf(s[kb][qb][i], sc, -L[qb]));
-                    if (need_mask && !(key <= q && key < T_)) p = 0.f;
-                    dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = k0 + kb * 16 + g * 4 + i;
+                        float p = exp2_raw(fmaf(s[kb][qb][i], sc, -L[qb]));
+                        if constexpr (decltype(masked)::value) {
+                            if (!(key <= q && key < T_)) p = 0.f;
+                        }
+                        dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
+                    }
                 }
-            }
+        };
+        if ((k0 + 63 > qw0) || (k0 + 64 > T_)) ds(std::true_type{});
+        else ds(std::false_type{});
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
