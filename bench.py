@@ -244,8 +244,8 @@ def main():
                      os.path.join(ROOT, "profiles", "traffic.json"))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the data-parallel sharding is described in the design notes, not implemented)", file=sys.stderr)
+        print(f"bench.py: the GPT-2 step library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(data-parallel sharding over several GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -27,7 +27,7 @@ What is computed (each function cites the passage it follows):
     clip: global L2 norm over all gradients, coefficient min(1, max_norm/(norm+1e-6))
     AdamW: decoupled weight decay on tensors with >= 2 dims, bias-corrected moments
 
-Readings where the pages leave a detail open (also listed in the design notes):
+Readings where the pages leave a detail open:
 
 * LayerNorm is ``nn.LayerNorm(n_embd)`` with its defaults: eps 1e-5, biased variance.
 * The attention scale is the library default 1/sqrt(head_dim) (no scale is passed).
