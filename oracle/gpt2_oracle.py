@@ -26,6 +26,8 @@ What is computed (each function cites the passage it follows):
     backward: the chain rule written out for every op, gradients of the two uses of wte add
     clip: global L2 norm over all gradients, coefficient min(1, max_norm/(norm+1e-6))
     AdamW: decoupled weight decay on tensors with >= 2 dims, bias-corrected moments
+    evaluation: per-position losses reduced per row over a mask (masked_row_losses)
+    sampling: softmax, the k most probable tokens, an inverse-CDF draw (topk_sample)
 
 Readings where the pages leave a detail open:
 
