@@ -987,7 +987,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
 
 constexpr size_t ts_fwd_lds() { return 2 * 2 * TS_BYTES; }
 #ifndef ATT_FWD_QB
-#define ATT_FWD_QB 2
+#define ATT_FWD_QB 1
 #endif
 constexpr size_t ts_dkv_lds() { return 2 * (2 * TS_BYTES + 512); }
 
