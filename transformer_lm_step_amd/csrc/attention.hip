@@ -708,8 +708,10 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
     }
 }
 
-// dK, dV for 128 keys per workgroup (32 per wave), streaming 64-query chunks of Q, dO, lse, D.
-__global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
+// dK, dV for 64 * KBW keys per workgroup (16 * KBW per wave), streaming 64-query chunks of Q, dO,
+// lse, D.
+template <int KBW>
+__global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
                                                                     const bf16* __restrict__ dy,
                                                                     const float* __restrict__ lse,
                                                                     const float* __restrict__ D,
@@ -730,12 +732,13 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int k0 = kblk * 128, kw0 = k0 + wave * 32;
+    constexpr int KW = 16 * KBW, KBLK = 4 * KW;   // keys per wave, per workgroup
+    const int k0 = kblk * KBLK, kw0 = k0 + wave * KW;
     const uint32_t lds0 = lds_addr(smem);
 
-    bf16x8 kf[2][2], vf[2][2];
+    bf16x8 kf[KBW][2], vf[KBW][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
         const int key = kw0 + kb * 16 + col;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -744,11 +747,11 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
             vf[kb][ks] = key < T_ ? frag_global<bf16>(base + off + 2 * C) : frag_zero<bf16>();
         }
     }
-    floatx4 dk[4][2], dv[4][2];
+    floatx4 dk[4][KBW], dv[4][KBW];
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dk[d][kb] = dv[d][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < KBW; ++kb) dk[d][kb] = dv[d][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int qc0 = k0 / 64, nqc = (T_ + 63) / 64;
     const bool wave_live = kw0 < T_;
@@ -772,18 +775,18 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
         const char* sO = sQ + TS_BYTES;
         const float* sL = (const float*)(sQ + 2 * TS_BYTES);
         const float* sD = sL + 64;
-        floatx4 s[4][2], dp[4][2];
+        floatx4 s[4][KBW], dp[4][KBW];
         __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[qb][kb] = dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < KBW; ++kb) s[qb][kb] = dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8 qa = ts_nat(sQ, qb * 16, ks, lane);
                 const bf16x8 oa = ts_nat(sO, qb * 16, ks, lane);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < KBW; ++kb) {
                     mma8(s[qb][kb], qa, kf[kb][ks]);
                     mma8(dp[qb][kb], oa, vf[kb][ks]);
                 }
@@ -802,7 +805,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                     const int q = q0 + ql;
                     const float L = sL[ql] * kLog2e, Dq = sD[ql];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
+                    for (int kb = 0; kb < KBW; ++kb) {
                         const int key = kw0 + kb * 16 + col;
                         float p = exp2_raw(fmaf(s[qb][kb][i], sc, -L));
                         if constexpr (decltype(masked)::value) {
@@ -813,14 +816,14 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                     }
                 }
         };
-        if ((q0 < kw0 + 32) || (q0 + 64 > T_)) p_ds(std::true_type{});
+        if ((q0 < kw0 + KW) || (q0 + 64 > T_)) p_ds(std::true_type{});
         else p_ds(std::false_type{});
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            bf16x8 pf[2], df[2];
+            bf16x8 pf[KBW], df[KBW];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KBW; ++kb) {
                 pf[kb] = frag_from_acc<bf16>(s[2 * st][kb], s[2 * st + 1][kb]);
                 df[kb] = frag_from_acc<bf16>(dp[2 * st][kb], dp[2 * st + 1][kb]);
             }
@@ -829,7 +832,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
                 const bf16x8 oat = ts_tr(sO, d * 16, 32 * st, 32 * st + 16, lane);
                 const bf16x8 qat = ts_tr(sQ, d * 16, 32 * st, 32 * st + 16, lane);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < KBW; ++kb) {
                     mma8(dv[d][kb], oat, pf[kb]);
                     mma8(dk[d][kb], qat, df[kb]);
                 }
@@ -839,7 +842,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
     }
     if (!wave_live) return;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KBW; ++kb) {
         const int key = kw0 + kb * 16 + col;
         if (key >= T_) continue;
         bf16* r = dqkv + ((int64_t)b * T_ + key) * ld + h * HS;
@@ -851,8 +854,9 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dkv_ts_kernel(const bf1
     }
 }
 
-// dQ for 128 queries per workgroup (32 per wave), streaming 64-key chunks of K and V.
-__global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+// dQ for 64 * QBW queries per workgroup (16 * QBW per wave), streaming 64-key chunks of K and V.
+template <int QBW>
+__global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
@@ -863,7 +867,8 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
     constexpr int HS = 64, STAGE = 2 * TS_BYTES;
     int bx, by;
     xcd_remap(bx, by);
-    const int nqb = (T_ + 127) / 128;
+    constexpr int QW = 16 * QBW, QBLK = 4 * QW;   // queries per wave, per workgroup
+    const int nqb = (T_ + QBLK - 1) / QBLK;
     const int qblk = nqb - 1 - bx;
     const int bh = by, b = bh / H, h = bh % H;
     const int C = H * HS;
@@ -873,14 +878,14 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int q0 = qblk * 128, qw0 = q0 + wave * 32;
+    const int q0 = qblk * QBLK, qw0 = q0 + wave * QW;
     const uint32_t lds0 = lds_addr(smem);
 
-    bf16x8 qf[2][2], of[2][2];
-    float L[2], Dq[2];
+    bf16x8 qf[QBW][2], of[QBW][2];
+    float L[QBW], Dq[QBW];
     const bf16* yb = y + (int64_t)b * T_ * C;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         const int q = qw0 + qb * 16 + col;
         const bool ok = q < T_;
         float dsum = 0.f;
@@ -900,11 +905,13 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
         Dq[qb] = ok ? dsum : 0.f;
         if (ok && g == 0) D[(int64_t)bh * T_ + q] = dsum;   // for the dK/dV kernel, which runs next
     }
-    floatx4 dq[4][2];
+    floatx4 dq[4][QBW];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) dq[d][0] = dq[d][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) dq[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int kend = min(q0 + 128, T_);
+    const int kend = min(q0 + QBLK, T_);
     const int nchunk = (kend + 63) / 64;
     const bool wave_live = qw0 < T_;
     const TsOff offkv = ts_offsets(ld, 64, wave, lane);
@@ -919,20 +926,21 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
         dma_wait_barrier();
         if (c + 1 < nchunk) issue(c + 1);
         const int k0 = c * 64;
-        if (!wave_live || k0 > qw0 + 31) continue;
+        if (!wave_live || k0 > qw0 + QW - 1) continue;
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
-        floatx4 s[4][2], dp[4][2];
+        floatx4 s[4][QBW], dp[4][QBW];
         __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb) s[kb][qb] = dp[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8 ka = ts_nat(sK, kb * 16, ks, lane);
                 const bf16x8 va = ts_nat(sV, kb * 16, ks, lane);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < QBW; ++qb) {
                     mma8(s[kb][qb], ka, qf[qb][ks]);
                     mma8(dp[kb][qb], va, of[qb][ks]);
                 }
@@ -945,7 +953,7 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < QBW; ++qb) {
                     const int q = qw0 + qb * 16 + col;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -963,20 +971,21 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const bf16x8 d0 = frag_from_acc<bf16>(dp[2 * st][0], dp[2 * st + 1][0]);
-            const bf16x8 d1 = frag_from_acc<bf16>(dp[2 * st][1], dp[2 * st + 1][1]);
+            bf16x8 dfr[QBW];
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb) dfr[qb] = frag_from_acc<bf16>(dp[2 * st][qb], dp[2 * st + 1][qb]);
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const bf16x8 kat = ts_tr(sK, d * 16, 32 * st, 32 * st + 16, lane);
-                mma8(dq[d][0], kat, d0);
-                mma8(dq[d][1], kat, d1);
+#pragma unroll
+                for (int qb = 0; qb < QBW; ++qb) mma8(dq[d][qb], kat, dfr[qb]);
             }
         }
         __builtin_amdgcn_s_setprio(0);
     }
     if (!wave_live) return;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QBW; ++qb) {
         const int q = qw0 + qb * 16 + col;
         if (q >= T_) continue;
         bf16* r = dqkv + ((int64_t)b * T_ + q) * ld + h * HS;
@@ -988,6 +997,12 @@ __global__ void __launch_bounds__(A_THREADS, 2) attn_bwd_dq_ts_kernel(const bf16
 constexpr size_t ts_fwd_lds() { return 2 * 2 * TS_BYTES; }
 #ifndef ATT_FWD_QB
 #define ATT_FWD_QB 1
+#endif
+#ifndef ATT_DKV_KB
+#define ATT_DKV_KB 1
+#endif
+#ifndef ATT_DQ_QB
+#define ATT_DQ_QB 1
 #endif
 constexpr size_t ts_dkv_lds() { return 2 * (2 * TS_BYTES + 512); }
 
@@ -1019,14 +1034,14 @@ static hipError_t bwd_launch(const void* qkv, const void* y, const void* dy, con
     if constexpr (sizeof(T) == 2 && HS == 64) {
         // the dQ kernel forms D itself (from the dO and O rows it loads) and stores it for the
         // dK/dV kernel, so it runs first and no separate pass over O and dO is needed
-        attn_bwd_dq_ts_kernel<<<grid, dim3(A_THREADS), ts_fwd_lds(), s>>>((const bf16*)qkv, (const bf16*)y,
-                                                                         (const bf16*)dy, lse, D, (bf16*)dqkv, T_, H,
-                                                                         sc, scale);
+        const dim3 gq((T_ + 64 * ATT_DQ_QB - 1) / (64 * ATT_DQ_QB), B * H);
+        attn_bwd_dq_ts_kernel<ATT_DQ_QB><<<gq, dim3(A_THREADS), ts_fwd_lds(), s>>>(
+            (const bf16*)qkv, (const bf16*)y, (const bf16*)dy, lse, D, (bf16*)dqkv, T_, H, sc, scale);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        attn_bwd_dkv_ts_kernel<<<grid, dim3(A_THREADS), ts_dkv_lds(), s>>>((const bf16*)qkv, (const bf16*)dy, lse,
-                                                                          (const float*)D, (bf16*)dqkv, T_, H, sc,
-                                                                          scale);
+        const dim3 gk((T_ + 64 * ATT_DKV_KB - 1) / (64 * ATT_DKV_KB), B * H);
+        attn_bwd_dkv_ts_kernel<ATT_DKV_KB><<<gk, dim3(A_THREADS), ts_dkv_lds(), s>>>(
+            (const bf16*)qkv, (const bf16*)dy, lse, (const float*)D, (bf16*)dqkv, T_, H, sc, scale);
         return hipGetLastError();
     }
     attn_bwd_pre_kernel<T, HS><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>((const T*)y, (const T*)dy, D,
@@ -1068,8 +1083,8 @@ void attention_setup() {
     ASET(bf16, 64) ASET(bf16, 32) ASET(float, 64) ASET(float, 32)
 #undef ASET
     (void)hipFuncSetAttribute((const void*)attn_fwd_ts_kernel<ATT_FWD_QB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
-    (void)hipFuncSetAttribute((const void*)attn_bwd_dq_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
-    (void)hipFuncSetAttribute((const void*)attn_bwd_dkv_ts_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_dkv_lds());
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dq_ts_kernel<ATT_DQ_QB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_fwd_lds());
+    (void)hipFuncSetAttribute((const void*)attn_bwd_dkv_ts_kernel<ATT_DKV_KB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ts_dkv_lds());
 }
 
 }  // namespace gpt2k
