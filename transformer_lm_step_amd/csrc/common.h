@@ -158,17 +158,29 @@ constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
 // LDS byte address of a shared-memory pointer
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_char_t)(p); }
 
+// A wave-uniform pointer held in scalar registers: the compiler can leave a uniform value that
+// it computed with vector instructions (an integer division, say) in vector registers, which
+// the scalar operand of the direct loads below cannot take; readfirstlane of a value already in
+// scalar registers costs nothing.
+DEV const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 // One direct load: the wave's 64 lanes each move 16 bytes from base + voff to LDS address
 // lds + 16 * lane (global_load_lds_dwordx4; base and lds wave-uniform). Inline asm (M0 and
 // the load in one block, no register results), so the compiler does not make later LDS reads
 // wait for it; kernels order these loads with explicit vmcnt waits and barriers. Loads the
 // compiler does not track only make its own vmcnt waits stricter (the counter drains in order).
 DEV void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(uniform_ptr(base))
+                 : "memory");
 }
 // the same with 4 bytes per lane (LDS address lds + 4 * lane)
 DEV void dma4(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(uniform_ptr(base))
+                 : "memory");
 }
 // wait for this wave's direct loads, then a bare barrier (no fence: a fence would also drain
 // loads issued for later tiles). Afterwards every wave's loads issued before it have landed
@@ -177,6 +189,10 @@ DEV void dma_wait_barrier() {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Barrier for LDS traffic only: this wave's LDS accesses are complete, then every wave meets.
+// Unlike __syncthreads() it does not wait for the wave's global stores to complete, so a
+// workgroup can stage the next part of its output in LDS while earlier stores drain.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Two transposing LDS reads (ds_read_b64_tr_b16) joined into one 8-value fragment. Within
 // each 16-lane group the instruction gives lane i, as its j-th value, element (i % 4) of the

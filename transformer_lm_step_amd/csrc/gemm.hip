@@ -402,31 +402,53 @@ DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
     else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
 }
 
+// Epilogue steps that depend on the column only: the scale alpha (plain output and gradient
+// accumulation) and the bias.
+template <int EPI>
+constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_F32; }
+template <int EPI>
+constexpr bool epi_bias() { return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU; }
+// bias of columns n..n+3 (0 past the matrix edge or without a bias)
+DEV float4 bias4(const GemmArgs& p, int n) {
+    if (!p.bias) return make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.vec && n + 3 < p.N) return *(const float4*)(p.bias + n);
+    float b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[r] = n + r < p.N ? p.bias[n + r] : 0.f;
+    return make_float4(b[0], b[1], b[2], b[3]);
+}
+// accumulators of columns n..n+3 with alpha and the bias applied. BIAS: 0 no bias, 1 a bias
+// known to be present with n..n+3 inside the matrix (one vector load), 2 checked (bias4).
+template <int EPI, int BIAS = 2>
+DEV float4 epi_pre(const GemmArgs& p, const float4& v, int n) {
+    const float al = epi_alpha<EPI>() ? p.alpha : 1.f;
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (epi_bias<EPI>()) {
+        if constexpr (BIAS == 1) b = *(const float4*)(p.bias + n);
+        else if constexpr (BIAS == 2) b = bias4(p, n);
+    }
+    return make_float4(al * v.x + b.x, al * v.y + b.y, al * v.z + b.z, al * v.w + b.w);
+}
+
 // Epilogue on 4 consecutive columns n..n+3 of row m (v = accumulators): vector accesses when
 // the 4 columns are inside the matrix and the rows are 16-byte friendly, else per element.
 // `in` is epi_load(p, m, n) on the vector path of an epilogue that reads (unused otherwise).
-template <int EPI>
+// CHECK = false: the caller knows the chunk is inside the matrix and vector-friendly.
+// PRE = true: v already has alpha and the bias applied (epi_pre).
+template <int EPI, bool CHECK = true, bool PRE = false>
 DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename EpiIn<EPI>::T& in) {
-    if (m >= p.M) return;
-    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+    if (CHECK && m >= p.M) return;
+    const float4 w4 = PRE ? v4 : epi_pre<EPI>(p, v4, n);
+    const float v[4] = {w4.x, w4.y, w4.z, w4.w};
     const int64_t o = (int64_t)m * p.ldc + n;
-    if (p.vec && n + 3 < p.N) {
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU) {
-            if (p.bias) {
-                const float4 b4 = *(const float4*)(p.bias + n);
-                bias[0] = b4.x; bias[1] = b4.y; bias[2] = b4.z; bias[3] = b4.w;
-            }
-        }
+    if (!CHECK || (p.vec && n + 3 < p.N)) {
         if constexpr (EPI == EPI_BIAS_T) {
-            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(p.alpha * v[0] + bias[0], p.alpha * v[1] + bias[1],
-                                                   p.alpha * v[2] + bias[2], p.alpha * v[3] + bias[3]);
+            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0], v[1], v[2], v[3]);
         } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
             const float4 rr = in;
-            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0] + bias[0], rr.y + v[1] + bias[1],
-                                                      rr.z + v[2] + bias[2], rr.w + v[3] + bias[3]);
+            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
-            const bf16x4 u = to_bf16x4(v[0] + bias[0], v[1] + bias[1], v[2] + bias[2], v[3] + bias[3]);
+            const bf16x4 u = to_bf16x4(v[0], v[1], v[2], v[3]);
             *(bf16x4*)((bf16*)p.C + o) = u;
             *(bf16x4*)((bf16*)p.C2 + o) = to_bf16x4(gelu_f((float)u[0]), gelu_f((float)u[1]), gelu_f((float)u[2]),
                                                     gelu_f((float)u[3]));
@@ -437,10 +459,9 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
         } else if constexpr (EPI == EPI_F32) {
             float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
             if (p.beta) old = in;
-            *(float4*)((float*)p.C + o) = make_float4(old.x + p.alpha * v[0], old.y + p.alpha * v[1],
-                                                      old.z + p.alpha * v[2], old.w + p.alpha * v[3]);
+            *(float4*)((float*)p.C + o) = make_float4(old.x + v[0], old.y + v[1], old.z + v[2], old.w + v[3]);
         } else {  // EPI_PARTIAL
-            *(float4*)((float*)p.C + (int64_t)blockIdx.y * p.part_stride + o) = v4;
+            *(float4*)((float*)p.C + (int64_t)blockIdx.y * p.part_stride + o) = w4;
         }
         return;
     }
@@ -449,20 +470,19 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
         const int nn = n + r;
         if (nn >= p.N) continue;
         const int64_t e = o + r;
-        const float b = (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU) && p.bias ? p.bias[nn] : 0.f;
         if constexpr (EPI == EPI_BIAS_T) {
-            ((bf16*)p.C)[e] = (bf16)(p.alpha * v[r] + b);
+            ((bf16*)p.C)[e] = (bf16)v[r];
         } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + nn] + v[r] + b;
+            ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + nn] + v[r];
         } else if constexpr (EPI == EPI_BIAS_GELU) {
-            const bf16 u = (bf16)(v[r] + b);
+            const bf16 u = (bf16)v[r];
             ((bf16*)p.C)[e] = u;
             ((bf16*)p.C2)[e] = (bf16)gelu_f((float)u);
         } else if constexpr (EPI == EPI_GELU_BWD) {
             ((bf16*)p.C)[e] = (bf16)(v[r] * gelu_grad_f((float)((const bf16*)p.aux)[(int64_t)m * p.ldaux + nn]));
         } else if constexpr (EPI == EPI_F32) {
             const float old = p.beta ? ((const float*)p.C)[e] : 0.f;
-            ((float*)p.C)[e] = old + p.alpha * v[r];
+            ((float*)p.C)[e] = old + v[r];
         } else {  // EPI_PARTIAL
             ((float*)p.C)[(int64_t)blockIdx.y * p.part_stride + e] = v[r];
         }
@@ -484,12 +504,13 @@ DEV bf16x8 to_bf16x8(const float (&v)[8]) {
     for (int q = 0; q < 8; ++q) o[q] = (bf16)v[q];
     return o;
 }
-// epi4 on 8 consecutive columns n..n+7 (a: the first 4 accumulators, b: the next 4); `in` is
-// the 8 saved pre-activations of the GELU derivative on the vector path
-template <int EPI>
+// epi4 on 8 consecutive columns n..n+7 (a: the first 4 values, b: the next 4, with alpha and
+// the bias applied); `in` is the 8 saved pre-activations of the GELU derivative on the vector
+// path
+template <int EPI, bool CHECK = true>
 DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b, const typename EpiIn8<EPI>::T& in) {
-    if (m >= p.M) return;
-    if (p.vec8 && n + 7 < p.N) {
+    if (CHECK && m >= p.M) return;
+    if (!CHECK || (p.vec8 && n + 7 < p.N)) {
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         const int64_t o = (int64_t)m * p.ldc + n;
         float r[8];
@@ -497,26 +518,14 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
 #pragma unroll
             for (int q = 0; q < 8; ++q) r[q] = v[q] * gelu_grad_f((float)in[q]);
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
-        } else {
-            float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (p.bias) {
-                const float4 b0 = *(const float4*)(p.bias + n), b1 = *(const float4*)(p.bias + n + 4);
-                bias[0] = b0.x; bias[1] = b0.y; bias[2] = b0.z; bias[3] = b0.w;
-                bias[4] = b1.x; bias[5] = b1.y; bias[6] = b1.z; bias[7] = b1.w;
-            }
-            if constexpr (EPI == EPI_BIAS_T) {
+        } else if constexpr (EPI == EPI_BIAS_T) {
+            *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(v);
+        } else {  // EPI_BIAS_GELU
+            const bf16x8 u = to_bf16x8(v);
+            *(bf16x8*)((bf16*)p.C + o) = u;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) r[q] = p.alpha * v[q] + bias[q];
-                *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
-            } else {  // EPI_BIAS_GELU
-#pragma unroll
-                for (int q = 0; q < 8; ++q) r[q] = v[q] + bias[q];
-                const bf16x8 u = to_bf16x8(r);
-                *(bf16x8*)((bf16*)p.C + o) = u;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) r[q] = gelu_f((float)u[q]);
-                *(bf16x8*)((bf16*)p.C2 + o) = to_bf16x8(r);
-            }
+            for (int q = 0; q < 8; ++q) r[q] = gelu_f((float)u[q]);
+            *(bf16x8*)((bf16*)p.C2 + o) = to_bf16x8(r);
         }
         return;
     }
@@ -526,42 +535,37 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
         if (epi_vec(p, m, n)) i0 = epi_load<EPI>(p, m, n);
         if (epi_vec(p, m, n + 4)) i1 = epi_load<EPI>(p, m, n + 4);
     }
-    epi4<EPI>(p, m, n, a, i0);
-    epi4<EPI>(p, m, n + 4, b, i1);
+    epi4<EPI, true, true>(p, m, n, a, i0);
+    epi4<EPI, true, true>(p, m, n + 4, b, i1);
 }
 
-// LDS-staged epilogue: the fp32 tile passes through LDS in two halves of 64 rows (the waves
+// LDS-staged epilogues. The fp32 tile passes through LDS in two halves of 64 rows (the waves
 // with wm == h write half h with 16-byte stores, conflict-free with rows padded by 16 bytes),
-// then all threads apply the epilogue to 8-column (bf16 outputs) or 4-column (fp32 outputs)
-// chunks along the rows, so every global load and store of the epilogue covers whole row
-// segments with 16-byte accesses.
-template <int EPI, int FM, int FN, int BN>
-DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm, int wn,
-                      int lane, int tid) {
-    constexpr bool WIDE = epi_wide<EPI>();
-    constexpr int CW = WIDE ? 8 : 4;       // columns per chunk
+// then all threads apply the epilogue to chunks along the rows, so every global load and store
+// of the epilogue covers whole row segments with 16-byte accesses.
+//
+// bf16 outputs: 8-column chunks. CHK: per-chunk edge checks; BIAS: as in epi_pre.
+template <int EPI, int FM, int FN, int BN, bool CHK, int BIAS>
+DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm,
+                           int wn, int lane, int tid) {
+    static_assert(epi_wide<EPI>(), "bf16-output epilogues only");
     constexpr int LDW = BN + 4;            // floats per staged row
-    constexpr int CPR = BN / CW;           // chunks per row
+    constexpr int CPR = BN / 8;            // chunks per row
     constexpr int NIT = 64 * CPR / GTHREADS;  // chunks per thread and half
     static_assert(64 * CPR % GTHREADS == 0, "whole chunks per thread");
-    typedef typename std::conditional<WIDE, typename EpiIn8<EPI>::T, typename EpiIn<EPI>::T>::type In;
+    typedef typename EpiIn8<EPI>::T In;
     float* st = (float*)smem;
-    const bool reads = epi_reads<EPI>(p);
-    __syncthreads();                       // every wave is done reading the last K tile
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    lds_barrier();                         // every wave is done reading the last K tile
+    // the two halves (a generic lambda called twice, so both are laid out straight)
+    auto half = [&](auto hc) {
+        constexpr int h = decltype(hc)::value;
         In in[NIT];
-        if (reads) {
+        if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int k = tid + it * GTHREADS, r = k / CPR, c = k - r * CPR;
-                const int m = m0 + 64 * h + r, n = n0 + CW * c;
-                if constexpr (WIDE) {
-                    if constexpr (EPI == EPI_GELU_BWD)
-                        if (epi_vec8(p, m, n)) in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
-                } else {
-                    if (epi_vec(p, m, n)) in[it] = epi_load<EPI>(p, m, n);
-                }
+                const int m = m0 + 64 * h + r, n = n0 + 8 * c;
+                if (!CHK || epi_vec8(p, m, n)) in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
             }
         }
         if (wm == h) {
@@ -572,17 +576,90 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
                     *(float4*)(st + (16 * i + (lane & 15)) * LDW + wn * (BN / 2) + 16 * j + 4 * (lane >> 4)) =
                         make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int k = tid + it * GTHREADS, r = k / CPR, c = k - r * CPR;
-            if constexpr (WIDE)
-                epi8<EPI>(p, m0 + 64 * h + r, n0 + 8 * c, *(const float4*)(st + r * LDW + 8 * c),
-                          *(const float4*)(st + r * LDW + 8 * c + 4), in[it]);
-            else
-                epi4<EPI>(p, m0 + 64 * h + r, n0 + 4 * c, *(const float4*)(st + r * LDW + 4 * c), in[it]);
+            const int m = m0 + 64 * h + r, n = n0 + 8 * c;
+            epi8<EPI, CHK>(p, m, n, epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c), n),
+                           epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c + 4), n + 4), in[it]);
         }
-        __syncthreads();
+        lds_barrier();
+    };
+    half(std::integral_constant<int, 0>{});
+    half(std::integral_constant<int, 1>{});
+}
+// fp32 outputs (residual add, gradient output, split-K partials): 4-column chunks (already
+// 16-byte accesses), alpha and the bias applied per chunk by epi4. Split-K partials of
+// a tile inside the matrix skip the per-chunk checks. (The bf16 epilogues' form, with alpha and
+// the bias ahead of epi4 and LDS-only barriers, measured 9-12% slower here.)
+template <int EPI, int FM, int FN, int BN>
+DEV void store_staged_f32(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm,
+                          int wn, int lane, int tid) {
+    constexpr int LDW = BN + 4, CPR = BN / 4, NIT = 64 * CPR / GTHREADS;
+    static_assert(64 * CPR % GTHREADS == 0, "whole chunks per thread");
+    typedef typename EpiIn<EPI>::T In;
+    float* st = (float*)smem;
+    const bool reads = epi_reads<EPI>(p);
+    const bool full = EPI == EPI_PARTIAL && m0 + 128 <= p.M && n0 + BN <= p.N && p.vec;
+    __syncthreads();                       // every wave is done reading the last K tile
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        // (the half as a lambda: the compiler then keeps all of a half's input loads in flight
+        // together, measured faster than the same code written inline)
+        auto half = [&](auto check) {
+            constexpr bool CHK = decltype(check)::value;
+            In in[NIT];
+            if (reads) {
+#pragma unroll
+                for (int it = 0; it < NIT; ++it) {
+                    const int k = tid + it * GTHREADS, r = k / CPR, c4 = k - r * CPR;
+                    const int m = m0 + 64 * h + r, n = n0 + 4 * c4;
+                    if (epi_vec(p, m, n)) in[it] = epi_load<EPI>(p, m, n);
+                }
+            }
+            if (wm == h) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        *(float4*)(st + (16 * i + (lane & 15)) * LDW + wn * (BN / 2) + 16 * j + 4 * (lane >> 4)) =
+                            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int k = tid + it * GTHREADS, r = k / CPR, c4 = k - r * CPR;
+                epi4<EPI, CHK>(p, m0 + 64 * h + r, n0 + 4 * c4, *(const float4*)(st + r * LDW + 4 * c4), in[it]);
+            }
+            __syncthreads();
+        };
+        if constexpr (EPI == EPI_PARTIAL) {
+            if (full) half(std::false_type{});
+            else half(std::true_type{});
+        } else {
+            half(std::true_type{});
+        }
+    }
+}
+// For bf16 outputs, a tile inside the matrix with vector-friendly rows takes a straight-line
+// form without per-chunk checks or bias branches, so its LDS reads and stores are issued back
+// to back. The choice is made once per tile: were the two forms to meet between the halves,
+// the compiler would wait there for every store of the first half (a wait it places where
+// paths with outstanding loads join).
+template <int EPI, int FM, int FN, int BN>
+DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm, int wn,
+                      int lane, int tid) {
+    if constexpr (epi_wide<EPI>()) {
+        const bool full = m0 + 128 <= p.M && n0 + BN <= p.N && p.vec8;
+        if (full && epi_bias<EPI>() && p.bias)
+            store_staged_bf16<EPI, FM, FN, BN, false, 1>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+        else if (full)
+            store_staged_bf16<EPI, FM, FN, BN, false, 0>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+        else
+            store_staged_bf16<EPI, FM, FN, BN, true, 2>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+    } else {
+        store_staged_f32<EPI, FM, FN, BN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
     }
 }
 
