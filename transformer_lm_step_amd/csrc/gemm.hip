@@ -591,8 +591,8 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
 }
 // fp32 outputs (residual add, gradient output, split-K partials): 4-column chunks (already
 // 16-byte accesses), alpha and the bias applied per chunk by epi4. Split-K partials of
-// a tile inside the matrix skip the per-chunk checks. (The bf16 epilogues' form, with alpha and
-// the bias ahead of epi4 and LDS-only barriers, measured 9-12% slower here.)
+// a tile inside the matrix skip the per-chunk checks. (Applying alpha and the bias ahead of
+// epi4, as the bf16 form does, measured 9-12% slower here.)
 template <int EPI, int FM, int FN, int BN>
 DEV void store_staged_f32(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* smem, int m0, int n0, int wm,
                           int wn, int lane, int tid) {
@@ -602,7 +602,7 @@ DEV void store_staged_f32(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char*
     float* st = (float*)smem;
     const bool reads = epi_reads<EPI>(p);
     const bool full = EPI == EPI_PARTIAL && m0 + 128 <= p.M && n0 + BN <= p.N && p.vec;
-    __syncthreads();                       // every wave is done reading the last K tile
+    lds_barrier();                       // every wave is done reading the last K tile
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         // (the half as a lambda: the compiler then keeps all of a half's input loads in flight
@@ -626,13 +626,13 @@ DEV void store_staged_f32(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char*
                         *(float4*)(st + (16 * i + (lane & 15)) * LDW + wn * (BN / 2) + 16 * j + 4 * (lane >> 4)) =
                             make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int k = tid + it * GTHREADS, r = k / CPR, c4 = k - r * CPR;
                 epi4<EPI, CHK>(p, m0 + 64 * h + r, n0 + 4 * c4, *(const float4*)(st + r * LDW + 4 * c4), in[it]);
             }
-            __syncthreads();
+            lds_barrier();
         };
         if constexpr (EPI == EPI_PARTIAL) {
             if (full) half(std::false_type{});
