@@ -521,12 +521,15 @@ __global__ void __launch_bounds__(A_THREADS) attn_bwd_dq_kernel(const T* __restr
 // Fragments whose k index runs along the tile's rows (V^T, Q^T, dO^T, K^T) come from the
 // transposing LDS read; its row choice per 16-lane group also produces the key/query order
 // of a fragment built from two 16x16 accumulator blocks, so no tile is ever transposed.
-// The 16-byte chunk c of row r sits in slot c ^ ts_swz(r), which keeps both the 16-byte row
-// reads (16 rows x one chunk) and the transposing reads (8 rows x 32 bytes per half-wave)
-// free of bank conflicts.
+// The 16-byte chunk c of row r sits in slot c ^ ts_swz(r): row bits 1, 2, 3 flip the slot
+// by 3, 4, 6. That keeps both reads free of bank conflicts, the 16-byte row reads (16 rows x
+// 4 chunks per instruction) and the transposing 8-byte reads (8 rows x 2 chunks per
+// half-wave): a probe of the two read patterns reads 0 conflict cycles for both, where a
+// swizzle of row bits 1..3 into slot bits 1, 2, 0 left half of the 16-byte reads' cycles in
+// conflicts (and the GEMM's (r >> 1) & 7 half of the transposing reads').
 constexpr int TS_BYTES = 64 * 128;
 
-DEV int ts_swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+DEV int ts_swz(int r) { return (-((r >> 1) & 1) & 3) ^ (-((r >> 2) & 1) & 4) ^ (-((r >> 3) & 1) & 6); }
 
 // Byte offsets of this wave's share (rows 16w..16w+15) of a 64-row tile whose row r starts at
 // src + r*ld; rows >= nrows repeat the last valid row (finite values, masked out by the
