@@ -57,7 +57,9 @@ def class_costs(w, B, n_params, n_decay, mode="train"):
         "attn_fwd": ("flop", attn_fwd * L),
         "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
         "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * 4 + BT * C * es + 8 * BT)),
-        "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 * 4 + BT * C * es + 8 * BT)),
+        # x (fp32), dh and the residual gradient written (storage type), mean and rstd; all but
+        # the final LayerNorm's also read the incoming residual gradient
+        "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 + 2 * BT * C * es + 8 * BT) + 2 * L * BT * C * es),
         "cross_entropy": ("byte", (1 if mode == "eval" else 2) * BT * Vp * es),
         "embed_fwd": ("byte", BT * C * 4 * 3),
     }

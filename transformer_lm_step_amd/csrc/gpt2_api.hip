@@ -165,7 +165,7 @@ struct Plan {
     // offsets in bytes
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
-    size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dres_t, dln, datt, dqkv, du, Dbuf;
+    size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dln, datt, dqkv, du, Dbuf;
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
     size_t mask, rowd;   // evaluation: copied mask, per-sequence double sums and counts
 };
@@ -209,9 +209,8 @@ Plan make_plan(const gpt2_config* c) {
     P.loss = take(256);
     P.mask = take(BT);
     P.rowd = take((size_t)c->max_batch * 2 * 8);
-    P.dres = take(BT * C * 4);
-    P.dres_t = take(BT * C * es);
-    P.dln = take(BT * C * 4);
+    P.dres = take(BT * C * es);
+    P.dln = take(BT * C * es);
     P.datt = take(BT * C * es);
     P.dqkv = take(BT * 3 * C * es);
     P.du = take(BT * F * es);
@@ -748,8 +747,8 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     float* grd = h->grads();
     float* prm = h->params();
     hipStream_t s = h->stream;
-    float* dres = h->at<float>(P.dres);
-    char* dres_t = h->at<char>(P.dres_t);
+    // gradient of the residual stream, in the storage type (like every activation gradient)
+    char* dres = h->at<char>(P.dres);
     // gradient of a LayerNorm's output, in the storage type: under the autocast recipe it is the
     // bf16 input gradient of the following product, cast to fp32 where LayerNorm runs
     char* dln = h->at<char>(P.dln);
@@ -764,7 +763,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
                       int64_t bias_off) -> int {
         TRY(run(h, "layernorm_bwd", [&] {
-            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres_t, accum_dres, lnpart, lnblk, BT, C, bf, s);
+            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, accum_dres, lnpart, lnblk, BT, C, bf, s);
         }));
         // LayerNorm weight and bias gradients are adjacent in the arena; the third partial
         // (column sums of the incoming residual gradient) is the projection bias gradient
@@ -811,10 +810,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
-        TRY(dw(dres_t, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
+        TRY(dw(dres, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
         {
             GemmDesc g;
-            g.A = dres_t; g.lda = C; g.a_layout = 0;
+            g.A = dres; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_pr[l]); g.ldb = F; g.b_layout = 1;
             g.M = BT; g.N = F; g.K = C;
             g.epi = EPI_GELU_BWD; g.C = h->at<char>(P.du); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
@@ -832,10 +831,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
         TRY(ln_bwd(h->at<float>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1, L.b_pr[l]));
         // x_mid = x_in + y Wo^T + bo
-        TRY(dw(dres_t, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
+        TRY(dw(dres, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
         {
             GemmDesc g;
-            g.A = dres_t; g.lda = C; g.a_layout = 0;
+            g.A = dres; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_o[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = C;
             g.epi = EPI_BIAS_T; g.C = h->at<char>(P.datt); g.ldc = C; g.alpha = 1.f;
@@ -861,7 +860,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     if (!acc && T < c.block_size)
         HIPTRY(fill(grd + L.wpe + (int64_t)T * C, (int64_t)(c.block_size - T) * C, 0.f, s), "zero wpe tail");
     TRY(run(h, "embed_bwd", [&] {
-        return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc,
+        return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc, bf,
                               h->at<char>(P.ebscratch), s);
     }));
     return GPT2_OK;

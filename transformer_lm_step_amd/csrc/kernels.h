@@ -51,11 +51,11 @@ hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe,
 // LayerNorm forward: out(T) = (x - mean) * rstd * w + b ; saves mean, rstd (fp32)
 hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s);
-// LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; dres_t = T copy of dres (may be
-// null); partial[blk][0:C] = sum dh*xhat, [C:2C] = sum dh, [2C:3C] = sum of the incoming dres
-// (zero without accumulate) over the block's rows. dh is in the storage type T.
+// LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; partial[blk][0:C] = sum dh*xhat,
+// [C:2C] = sum dh, [2C:3C] = sum of the incoming dres (zero without accumulate) over the
+// block's rows. dh and the residual gradient dres are in the storage type T.
 hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
-                              const float* w, float* dres, void* dres_t, int accumulate_dres,
+                              const float* w, void* dres, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);
 // out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order); scratch holds
@@ -85,11 +85,12 @@ hipError_t convert_to_f32(const void* src, float* dst, int64_t n, int is_bf16, h
 // mean of loss_rows -> *d_loss (single block, fixed order)
 hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s);
 
-// embedding backward (deterministic): dwte[idx[r]] += dx[r] in ascending r, dwpe[t] (+)= sum_b dx[b,t]
+// embedding backward (deterministic): dwte[idx[r]] += dx[r] in ascending r, dwpe[t] (+)= sum_b dx[b,t];
+// dx in the storage type (bf16 if is_bf16, else fp32)
 size_t embed_backward_scratch_bytes(int rows, int C);
 void rows_setup();
-hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int T,
-                          int C, int accumulate_wpe, void* scratch, hipStream_t s);
+hipError_t embed_backward(const int32_t* idx, const void* dx, float* dwte, float* dwpe, int B, int T,
+                          int C, int accumulate_wpe, int is_bf16, void* scratch, hipStream_t s);
 
 // global grad norm + clip coefficient, AdamW
 int norm_blocks();

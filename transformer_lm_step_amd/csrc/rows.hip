@@ -136,7 +136,7 @@ int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 
 template <typename T, int NV>
 __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     const T* __restrict__ dh, const float* __restrict__ x, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres, T* __restrict__ dres_t,
+    const float* __restrict__ rstd, const float* __restrict__ w, T* __restrict__ dres,
     int accumulate, float* __restrict__ partial, int rows, int C) {
     extern __shared__ float sred[];  // [4][3C]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
         const float mu = mean[row], r = rstd[row];
         const T* dr = dh + (int64_t)row * C;
         const float4* xr = (const float4*)(x + (int64_t)row * C);
-        float4* o = (float4*)(dres + (int64_t)row * C);
+        T* o = dres + (int64_t)row * C;
         float4 xh[NV], dxh[NV], old[NV];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
             xh[j] = dxh[j] = old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < nv) {
                 const float4 d = load4<T>(dr + 4 * c), xx = xr[c];
-                if (accumulate) old[j] = o[c];
+                if (accumulate) old[j] = load4<T>(o + 4 * c);
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
                 s1 += (dxh[j].x + dxh[j].y) + (dxh[j].z + dxh[j].w);
@@ -181,8 +181,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
                                              old[j].y + r * (dxh[j].y - m1 - xh[j].y * m2),
                                              old[j].z + r * (dxh[j].z - m1 - xh[j].z * m2),
                                              old[j].w + r * (dxh[j].w - m1 - xh[j].w * m2));
-                o[c] = g;
-                if (dres_t) store4<T>(dres_t + (int64_t)row * C + 4 * c, g.x, g.y, g.z, g.w);
+                store4<T>(o + 4 * c, g.x, g.y, g.z, g.w);
             }
         }
     }
@@ -205,10 +204,10 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
 
 template <typename T>
 static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const T* dh, const float* x,
-                                const float* mean, const float* rstd, const float* w, float* dres, T* dres_t,
-                                int acc, float* partial, int rows, int C) {
+                                const float* mean, const float* rstd, const float* w, T* dres, int acc,
+                                float* partial, int rows, int C) {
 #define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<T, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
-                                   dres, dres_t, acc, partial, rows, C)
+                                   dres, acc, partial, rows, C)
     if (nv4 <= 64) LNB(1);
     else if (nv4 <= 128) LNB(2);
     else if (nv4 <= 192) LNB(3);
@@ -219,15 +218,15 @@ static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, cons
 }
 
 hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
-                              const float* w, float* dres, void* dres_t, int accumulate_dres, float* partial,
+                              const float* w, void* dres, int accumulate_dres, float* partial,
                               int nblk, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     const size_t lds = 12 * (size_t)C * sizeof(float);
     if (is_bf16)
-        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, x, mean, rstd, w, dres, (bf16*)dres_t,
+        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, x, mean, rstd, w, (bf16*)dres,
                                    accumulate_dres, partial, rows, C);
-    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, x, mean, rstd, w, dres,
-                                (float*)dres_t, accumulate_dres, partial, rows, C);
+    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, x, mean, rstd, w, (float*)dres,
+                                accumulate_dres, partial, rows, C);
 }
 
 // Column sums of partial [np, n] (row stride `stride`), deterministic, in two launches:
@@ -660,8 +659,9 @@ __global__ void __launch_bounds__(EB_THREADS) eb_sort_kernel(const int32_t* __re
     }
 }
 
+template <typename T>
 __global__ void eb_segment_kernel(const EbMeta* meta, const int32_t* __restrict__ srow,
-                                  const int32_t* __restrict__ seg_begin, const float* __restrict__ dx, int row0,
+                                  const int32_t* __restrict__ seg_begin, const T* __restrict__ dx, int row0,
                                   int C, float* __restrict__ part) {
     const int nseg = meta->nseg;
     const int nv = C >> 2;
@@ -670,7 +670,7 @@ __global__ void eb_segment_kernel(const EbMeta* meta, const int32_t* __restrict_
         for (int c = threadIdx.x; c < nv; c += blockDim.x) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int i = b; i < e; ++i) {
-                const float4 v = ((const float4*)(dx + (int64_t)(row0 + srow[i]) * C))[c];
+                const float4 v = load4<T>(dx + (int64_t)(row0 + srow[i]) * C + 4 * c);
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             ((float4*)(part + (int64_t)sg * C))[c] = acc;
@@ -697,16 +697,18 @@ __global__ void eb_run_kernel(const EbMeta* meta, const int32_t* __restrict__ ru
     }
 }
 
-__global__ void dwpe_kernel(const float* __restrict__ dx, float* __restrict__ dwpe, int B, int T, int C, int accumulate) {
+template <typename S>
+__global__ void dwpe_kernel(const S* __restrict__ dx, float* __restrict__ dwpe, int B, int T, int C, int accumulate) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over T*C
     if (i >= (int64_t)T * C) return;
     float s = 0.f;
-    for (int b = 0; b < B; ++b) s += dx[(int64_t)b * T * C + i];
+    for (int b = 0; b < B; ++b) s += to_f<S>(dx[(int64_t)b * T * C + i]);
     dwpe[i] = accumulate ? dwpe[i] + s : s;
 }
 
-hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B, int T, int C,
-                          int accumulate_wpe, void* scratch, hipStream_t s) {
+template <typename S>
+static hipError_t embed_backward_t(const int32_t* idx, const S* dx, float* dwte, float* dwpe, int B, int T, int C,
+                                   int accumulate_wpe, void* scratch, hipStream_t s) {
     const int rows = B * T;
     char* p = (char*)scratch;
     EbMeta* meta = (EbMeta*)p;
@@ -725,7 +727,7 @@ hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, floa
                            seg_begin, run_id, run_seg);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(eb_segment_kernel, dim3(2048), dim3(C / 4 < 256 ? ((C / 4 + 63) / 64) * 64 : 256), 0, s,
+        hipLaunchKernelGGL(eb_segment_kernel<S>, dim3(2048), dim3(C / 4 < 256 ? ((C / 4 + 63) / 64) * 64 : 256), 0, s,
                            meta, srow, seg_begin, dx, r0, C, part);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -735,8 +737,15 @@ hipError_t embed_backward(const int32_t* idx, const float* dx, float* dwte, floa
         if (e != hipSuccess) return e;
     }
     const int64_t tc = (int64_t)T * C;
-    hipLaunchKernelGGL(dwpe_kernel, dim3((unsigned)((tc + 255) / 256)), dim3(256), 0, s, dx, dwpe, B, T, C, accumulate_wpe);
+    hipLaunchKernelGGL(dwpe_kernel<S>, dim3((unsigned)((tc + 255) / 256)), dim3(256), 0, s, dx, dwpe, B, T, C,
+                       accumulate_wpe);
     return hipGetLastError();
+}
+hipError_t embed_backward(const int32_t* idx, const void* dx, float* dwte, float* dwpe, int B, int T, int C,
+                          int accumulate_wpe, int is_bf16, void* scratch, hipStream_t s) {
+    if (is_bf16)
+        return embed_backward_t(idx, (const bf16*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, s);
+    return embed_backward_t(idx, (const float*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, s);
 }
 
 void rows_setup() {
