@@ -56,12 +56,13 @@ def class_costs(w, B, n_params, n_decay, mode="train"):
         "gemm_dw": ("flop", 2 * BT * C * (3 * C + C + F + F) * L),
         "attn_fwd": ("flop", attn_fwd * L),
         "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
-        "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * 4 + BT * C * es + 8 * BT)),
-        # x (fp32), dh and the residual gradient written (storage type), mean and rstd; all but
-        # the final LayerNorm's also read the incoming residual gradient
-        "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * 4 + 2 * BT * C * es + 8 * BT) + 2 * L * BT * C * es),
+        # the residual stream and the LayerNorm output in the storage type, mean and rstd
+        "layernorm_fwd": ("byte", (2 * L + 1) * (2 * BT * C * es + 8 * BT)),
+        # x, dh and the residual gradient written (storage type), mean and rstd; all but the
+        # final LayerNorm's also read the incoming residual gradient
+        "layernorm_bwd": ("byte", (2 * L + 1) * (3 * BT * C * es + 8 * BT) + 2 * L * BT * C * es),
         "cross_entropy": ("byte", (1 if mode == "eval" else 2) * BT * Vp * es),
-        "embed_fwd": ("byte", BT * C * 4 * 3),
+        "embed_fwd": ("byte", BT * C * (4 + 4 + es)),   # fp32 wte and wpe rows, x in the storage type
     }
     if mode == "decode":
         # one new position per sequence: the products stream their bf16 weights (B rows are

@@ -90,7 +90,6 @@ DEV typename FragT<T>::type frag_from_acc(const floatx4& a, const floatx4& b) {
 template <typename T>
 DEV void store4v(T* p, const floatx4& v, float s) {
     if constexpr (sizeof(T) == 2) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 o;
         o[0] = (bf16)(v[0] * s); o[1] = (bf16)(v[1] * s); o[2] = (bf16)(v[2] * s); o[3] = (bf16)(v[3] * s);
         *(bf16x4*)p = o;

@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx8 __attribute__((ext_vector_type(8)));

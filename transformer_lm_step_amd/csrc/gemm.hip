@@ -38,7 +38,7 @@ struct GemmArgs {
     void* C; int64_t ldc;       // main output (storage type or fp32, per epilogue)
     void* C2;                   // second output (GELU activation)
     const float* bias;
-    const float* resid; int64_t ldr;
+    const void* resid; int64_t ldr;   // residual input (storage type)
     const void* aux; int64_t ldaux;   // pre-activation u for the GELU derivative
     float alpha;
     int beta;                   // 1: add into the fp32 output
@@ -175,7 +175,7 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
         const int n = nw + j * 16 + (lane & 15);
         const bool nok = !CHECK || n < p.N;
         float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
+        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU)
             bias = (p.bias && nok) ? p.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -186,8 +186,8 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                 const int m = mb + r;
                 const bool ok = !CHECK || (nok && m < p.M);
                 extra[r] = 0.f;
-                if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    if (ok) extra[r] = p.resid[(int64_t)m * p.ldr + n];
+                if constexpr (EPI == EPI_BIAS_RESID) {
+                    if (ok) extra[r] = to_f<T>(((const T*)p.resid)[(int64_t)m * p.ldr + n]);
                 } else if constexpr (EPI == EPI_GELU_BWD) {
                     if (ok) extra[r] = to_f<T>(((const T*)p.aux)[(int64_t)m * p.ldaux + n]);
                 } else if constexpr (EPI == EPI_F32) {
@@ -202,8 +202,8 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                 const int64_t o = (int64_t)m * p.ldc + n;
                 if constexpr (EPI == EPI_BIAS_T) {
                     ((T*)p.C)[o] = from_f<T>(p.alpha * v + bias);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    ((float*)p.C)[o] = extra[r] + v + bias;
+                } else if constexpr (EPI == EPI_BIAS_RESID) {
+                    ((T*)p.C)[o] = from_f<T>(extra[r] + v + bias);
                 } else if constexpr (EPI == EPI_BIAS_GELU) {
                     const T u = from_f<T>(v + bias);
                     ((T*)p.C)[o] = u;
@@ -378,7 +378,6 @@ DEV bf16x8 mm_frag(const char* t, int rb, int ks, int lane) {
 // Epilogue of the LDS-streamed path. Its MFMAs take B as the first operand, so acc[i][j] is a
 // block of C^T: lane l holds row m = mw + 16i + (l & 15) and the 4 consecutive columns
 // n = nw + 16j + 4(l >> 4) + r, r = 0..3.
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
     bf16x4 o;
     o[0] = (bf16)a; o[1] = (bf16)b; o[2] = (bf16)c; o[3] = (bf16)d;
@@ -389,15 +388,16 @@ DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
 // loads of a whole staged half are in flight together instead of one after each store.
 template <int EPI> struct EpiIn { typedef float4 T; };
 template <> struct EpiIn<EPI_GELU_BWD> { typedef bf16x4 T; };
+template <> struct EpiIn<EPI_BIAS_RESID> { typedef bf16x4 T; };
 template <int EPI>
 DEV bool epi_reads(const GemmArgs& p) {
-    return EPI == EPI_BIAS_RESID_F32 || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
+    return EPI == EPI_BIAS_RESID || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
 }
 // 1 if the 4 columns n..n+3 of row m take the vector path
 DEV bool epi_vec(const GemmArgs& p, int m, int n) { return m < p.M && p.vec && n + 3 < p.N; }
 template <int EPI>
 DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
-    if constexpr (EPI == EPI_BIAS_RESID_F32) return *(const float4*)(p.resid + (int64_t)m * p.ldr + n);
+    if constexpr (EPI == EPI_BIAS_RESID) return *(const bf16x4*)((const bf16*)p.resid + (int64_t)m * p.ldr + n);
     else if constexpr (EPI == EPI_GELU_BWD) return *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
     else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
 }
@@ -407,7 +407,7 @@ DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
 template <int EPI>
 constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_F32; }
 template <int EPI>
-constexpr bool epi_bias() { return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU; }
+constexpr bool epi_bias() { return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU; }
 // bias of columns n..n+3 (0 past the matrix edge or without a bias)
 DEV float4 bias4(const GemmArgs& p, int n) {
     if (!p.bias) return make_float4(0.f, 0.f, 0.f, 0.f);
@@ -444,9 +444,10 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
     if (!CHECK || (p.vec && n + 3 < p.N)) {
         if constexpr (EPI == EPI_BIAS_T) {
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            const float4 rr = in;
-            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]);
+        } else if constexpr (EPI == EPI_BIAS_RESID) {
+            const bf16x4 rr = in;
+            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4((float)rr[0] + v[0], (float)rr[1] + v[1], (float)rr[2] + v[2],
+                                                   (float)rr[3] + v[3]);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             const bf16x4 u = to_bf16x4(v[0], v[1], v[2], v[3]);
             *(bf16x4*)((bf16*)p.C + o) = u;
@@ -472,8 +473,8 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
         const int64_t e = o + r;
         if constexpr (EPI == EPI_BIAS_T) {
             ((bf16*)p.C)[e] = (bf16)v[r];
-        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            ((float*)p.C)[e] = p.resid[(int64_t)m * p.ldr + nn] + v[r];
+        } else if constexpr (EPI == EPI_BIAS_RESID) {
+            ((bf16*)p.C)[e] = (bf16)((float)((const bf16*)p.resid)[(int64_t)m * p.ldr + nn] + v[r]);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             const bf16 u = (bf16)v[r];
             ((bf16*)p.C)[e] = u;
@@ -493,9 +494,12 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
 // segment is written with 16-byte stores (measured 9-18% faster on the forward products than
 // 8-byte stores: the epilogue's store instructions, not its bytes, were what it waited on).
 template <int EPI>
-constexpr bool epi_wide() { return EPI == EPI_BIAS_T || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD; }
+constexpr bool epi_wide() {
+    return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD;
+}
 template <int EPI> struct EpiIn8 { typedef int T; };
 template <> struct EpiIn8<EPI_GELU_BWD> { typedef bf16x8 T; };
+template <> struct EpiIn8<EPI_BIAS_RESID> { typedef bf16x8 T; };
 DEV bool epi_vec8(const GemmArgs& p, int m, int n) { return m < p.M && p.vec8 && n + 7 < p.N; }
 
 DEV bf16x8 to_bf16x8(const float (&v)[8]) {
@@ -505,8 +509,8 @@ DEV bf16x8 to_bf16x8(const float (&v)[8]) {
     return o;
 }
 // epi4 on 8 consecutive columns n..n+7 (a: the first 4 values, b: the next 4, with alpha and
-// the bias applied); `in` is the 8 saved pre-activations of the GELU derivative on the vector
-// path
+// the bias applied); `in` is the 8 residual values or saved pre-activations (GELU derivative)
+// on the vector path
 template <int EPI, bool CHECK = true>
 DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b, const typename EpiIn8<EPI>::T& in) {
     if (CHECK && m >= p.M) return;
@@ -520,6 +524,10 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
         } else if constexpr (EPI == EPI_BIAS_T) {
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(v);
+        } else if constexpr (EPI == EPI_BIAS_RESID) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) r[q] = (float)in[q] + v[q];
+            *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
         } else {  // EPI_BIAS_GELU
             const bf16x8 u = to_bf16x8(v);
             *(bf16x8*)((bf16*)p.C + o) = u;
@@ -560,12 +568,17 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     auto half = [&](auto hc) {
         constexpr int h = decltype(hc)::value;
         In in[NIT];
-        if constexpr (EPI == EPI_GELU_BWD) {
+        if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_BIAS_RESID) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int k = tid + it * GTHREADS, r = k / CPR, c = k - r * CPR;
                 const int m = m0 + 64 * h + r, n = n0 + 8 * c;
-                if (!CHK || epi_vec8(p, m, n)) in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+                if (!CHK || epi_vec8(p, m, n)) {
+                    if constexpr (EPI == EPI_GELU_BWD)
+                        in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+                    else
+                        in[it] = *(const bf16x8*)((const bf16*)p.resid + (int64_t)m * p.ldr + n);
+                }
             }
         }
         if (wm == h) {
@@ -589,7 +602,7 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     half(std::integral_constant<int, 0>{});
     half(std::integral_constant<int, 1>{});
 }
-// fp32 outputs (residual add, gradient output, split-K partials): 4-column chunks (already
+// fp32 outputs (gradient output, split-K partials): 4-column chunks (already
 // 16-byte accesses), alpha and the bias applied per chunk by epi4. Split-K partials of
 // a tile inside the matrix skip the per-chunk checks. (Applying alpha and the bias ahead of
 // epi4, as the bf16 form does, measured 9-12% slower here.)
@@ -924,7 +937,7 @@ static bool skinny_ok(const GemmDesc& d, int nsplit) {
     constexpr int E = 16 / sizeof(T);
     if (d.M > SK_MAX_M || d.a_layout != 0 || d.b_layout != 0 || nsplit != 1 || d.rowsum) return false;
     if (d.N > 16384) return false;   // very wide products (the vocabulary) fill the GPU on the tiled path
-    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID_F32 && d.epi != EPI_BIAS_GELU) return false;
+    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID && d.epi != EPI_BIAS_GELU) return false;
     if (d.K % E || d.lda % E || d.ldb % E) return false;
     return (((uintptr_t)d.A | (uintptr_t)d.B) & 15) == 0;
 }
@@ -933,7 +946,7 @@ template <typename T>
 static hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
     if (epi == EPI_BIAS_T) gemm_skinny_kernel<T, EPI_BIAS_T><<<grid, blk, 0, s>>>(a);
-    else if (epi == EPI_BIAS_RESID_F32) gemm_skinny_kernel<T, EPI_BIAS_RESID_F32><<<grid, blk, 0, s>>>(a);
+    else if (epi == EPI_BIAS_RESID) gemm_skinny_kernel<T, EPI_BIAS_RESID><<<grid, blk, 0, s>>>(a);
     else gemm_skinny_kernel<T, EPI_BIAS_GELU><<<grid, blk, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -958,7 +971,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
         auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
         a.vec = d.ldc % 4 == 0 && d.ldr % 4 == 0 && d.ldaux % 4 == 0 && al(d.C) && al(d.C2) && al(d.bias) &&
                 al(d.resid) && al(d.aux) && al(d.partial);
-        a.vec8 = a.vec && d.ldc % 8 == 0 && d.ldaux % 8 == 0;
+        a.vec8 = a.vec && d.ldc % 8 == 0 && d.ldaux % 8 == 0 && d.ldr % 8 == 0;
     }
     int epi = d.epi;
     if constexpr (sizeof(T) == 2) {
@@ -995,7 +1008,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 #define MM_CASE_WIDE(AL, BL, EP)                                                              \
     if (wide && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 192>(a, nsplit, s); else
             MM_CASE_WIDE(0, 0, EPI_BIAS_T)
-            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID_F32)
+            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID)
             MM_CASE_WIDE(0, 1, EPI_F32)
             MM_CASE_WIDE(0, 1, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_BIAS_GELU)
@@ -1003,7 +1016,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(1, 1, EPI_PARTIAL)
             MM_CASE_WIDE(1, 1, EPI_F32)
             MM_CASE(0, 0, EPI_BIAS_T)
-            MM_CASE(0, 0, EPI_BIAS_RESID_F32)
+            MM_CASE(0, 0, EPI_BIAS_RESID)
             MM_CASE(0, 0, EPI_BIAS_GELU)
             MM_CASE(0, 1, EPI_GELU_BWD)
             MM_CASE(0, 1, EPI_F32)
@@ -1020,7 +1033,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 #define GEMM_CASE(AL, BL, EP) \
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_tiled<T, AL, BL, EP>(a, nsplit, bm, bn, s); else
     GEMM_CASE(0, 0, EPI_BIAS_T)
-    GEMM_CASE(0, 0, EPI_BIAS_RESID_F32)
+    GEMM_CASE(0, 0, EPI_BIAS_RESID)
     GEMM_CASE(0, 0, EPI_BIAS_GELU)
     GEMM_CASE(0, 1, EPI_GELU_BWD)
     GEMM_CASE(0, 1, EPI_F32)
@@ -1078,7 +1091,7 @@ static void set_lds_mm() {
 }
 
 void gemm_setup() {
-    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 192>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();
@@ -1090,14 +1103,14 @@ void gemm_setup() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
     (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_F32, 128, 128, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
-    set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();
     set_lds_mm<0, 1, EPI_PARTIAL, 128, 128>(); set_lds_mm<1, 1, EPI_F32, 128, 128>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 128>();
     // allow the dynamic LDS size (above the 64 KiB default) for every instantiation
 #define SETUP_T(T)                                                                                          \
-    set_lds_all<T, 0, 0, EPI_BIAS_T>(); set_lds_all<T, 0, 0, EPI_BIAS_RESID_F32>();                        \
+    set_lds_all<T, 0, 0, EPI_BIAS_T>(); set_lds_all<T, 0, 0, EPI_BIAS_RESID>();                        \
     set_lds_all<T, 0, 0, EPI_BIAS_GELU>(); set_lds_all<T, 0, 1, EPI_GELU_BWD>();                           \
     set_lds_all<T, 0, 1, EPI_F32>(); set_lds_all<T, 0, 1, EPI_BIAS_T>(); set_lds_all<T, 1, 1, EPI_F32>(); \
     set_lds_all<T, 1, 1, EPI_PARTIAL>(); set_lds_all<T, 0, 1, EPI_PARTIAL>();

@@ -186,9 +186,9 @@ Plan make_plan(const gpt2_config* c) {
     P.shadow = bf ? take(L.decay_end * 2) : 0;
     P.idx = take(BT * 4);
     P.tgt = take(BT * 4);
-    for (int l = 0; l <= c->n_layer; ++l) P.x_in.push_back(take(BT * C * 4));
+    for (int l = 0; l <= c->n_layer; ++l) P.x_in.push_back(take(BT * C * es));
     for (int l = 0; l < c->n_layer; ++l) {
-        P.x_mid.push_back(take(BT * C * 4));
+        P.x_mid.push_back(take(BT * C * es));
         P.h1.push_back(take(BT * C * es));
         P.mean1.push_back(take(BT * 4));
         P.rstd1.push_back(take(BT * 4));
@@ -501,10 +501,10 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
     float* prm = h->params();
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
-    TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<float>(P.x_in[0]), B, T, C, s); }));
+    TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<char>(P.x_in[0]), B, T, C, bf, s); }));
     for (int l = 0; l < c.n_layer; ++l) {
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<float>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
+            return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
                                      h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), BT, C, bf, s);
         }));
         GemmDesc g;
@@ -520,11 +520,11 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = BT; g.N = C; g.K = C;
-        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
-        g.resid = h->at<float>(P.x_in[l]); g.ldr = C;
+        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<float>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
+            return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
                                      h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), BT, C, bf, s);
         }));
         g = GemmDesc();
@@ -537,12 +537,12 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = BT; g.N = C; g.K = F;
-        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
-        g.resid = h->at<float>(P.x_mid[l]); g.ldr = C;
+        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
     }
     TRY(run(h, "layernorm_fwd", [&] {
-        return layernorm_forward(h->at<float>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
+        return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
                                  h->at<float>(P.meanf), h->at<float>(P.rstdf), BT, C, bf, s);
     }));
     {
@@ -667,11 +667,11 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
     HIPTRY(hipMemcpyAsync(idx, d_tokens, (size_t)B * 4, hipMemcpyDeviceToDevice, s), "copy tokens");
     h->dec_B = 0;   // until this step has been enqueued completely
     TRY(run(h, "embed_fwd", [&] {
-        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<float>(P.x_in[0]), B, 1, C, s);
+        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, bf, s);
     }));
     for (int l = 0; l < c.n_layer; ++l) {
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<float>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
+            return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
                                      h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), B, C, bf, s);
         }));
         GemmDesc g;
@@ -688,11 +688,11 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = B; g.N = C; g.K = C;
-        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
-        g.resid = h->at<float>(P.x_in[l]); g.ldr = C;
+        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<float>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
+            return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
                                      h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), B, C, bf, s);
         }));
         g = GemmDesc();
@@ -705,12 +705,12 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = B; g.N = C; g.K = F;
-        g.epi = EPI_BIAS_RESID_F32; g.C = h->at<float>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
-        g.resid = h->at<float>(P.x_mid[l]); g.ldr = C;
+        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
     }
     TRY(run(h, "layernorm_fwd", [&] {
-        return layernorm_forward(h->at<float>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
+        return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
                                  h->at<float>(P.meanf), h->at<float>(P.rstdf), B, C, bf, s);
     }));
     {
@@ -760,7 +760,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
 
     // LayerNorm backward; with bias_off >= 0 the incoming residual gradient's column sum
     // (gathered by the same kernel) is the bias gradient of the projection at that offset
-    auto ln_bwd = [&](const float* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
+    auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
                       int64_t bias_off) -> int {
         TRY(run(h, "layernorm_bwd", [&] {
             return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, accum_dres, lnpart, lnblk, BT, C, bf, s);
@@ -806,7 +806,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.epi = EPI_F32; g.C = grd + L.wte; g.ldc = C; g.alpha = grad_scale; g.beta = acc;
         TRY(run(h, "gemm_lm_head_dw", [&] { return gemm(g, bf, s); }));
     }
-    TRY(ln_bwd(h->at<float>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0, -1));
+    TRY(ln_bwd(h->at<char>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0, -1));
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
@@ -829,7 +829,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
-        TRY(ln_bwd(h->at<float>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1, L.b_pr[l]));
+        TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1, L.b_pr[l]));
         // x_mid = x_in + y Wo^T + bo
         TRY(dw(dres, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
         {
@@ -854,7 +854,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the attn.c_proj bias gradient)
-        TRY(ln_bwd(h->at<float>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1, L.b_o[l]));
+        TRY(ln_bwd(h->at<char>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1, L.b_o[l]));
     }
     // embeddings: token rows scatter-add on top of the lm_head gradient, position rows
     if (!acc && T < c.block_size)
@@ -936,8 +936,8 @@ extern "C" int gpt2_debug_tensor(gpt2_t* h, const char* which, int32_t layer, fl
     int64_t n = 0;
     bool f32 = false;
     std::string w = which;
-    if (w == "x_in" && layer >= 0 && layer <= c.n_layer) { off = P.x_in[layer]; n = BT * C; f32 = true; }
-    else if (w == "x_out") { off = P.x_in[c.n_layer]; n = BT * C; f32 = true; }
+    if (w == "x_in" && layer >= 0 && layer <= c.n_layer) { off = P.x_in[layer]; n = BT * C; }
+    else if (w == "x_out") { off = P.x_in[c.n_layer]; n = BT * C; }
     else if (w == "hf") { off = P.hf; n = BT * C; }
     else if (w == "dz") { off = P.logits; n = BT * c.padded_vocab_size; }
     else if (lay && w == "h1") { off = P.h1[layer]; n = BT * C; }

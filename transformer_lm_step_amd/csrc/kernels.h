@@ -9,7 +9,7 @@ namespace gpt2k {
 // ------------------------------------------------------------------ GEMM
 enum Epi {
     EPI_BIAS_T = 0,          // C(T)   = alpha*acc + bias[n]           (bias may be null)
-    EPI_BIAS_RESID_F32 = 1,  // C(f32) = resid[m][n] + acc + bias[n]
+    EPI_BIAS_RESID = 1,      // C(T)   = resid(T)[m][n] + acc + bias[n]
     EPI_BIAS_GELU = 2,       // C(T)   = u = acc + bias[n];  C2(T) = gelu_tanh(u)
     EPI_GELU_BWD = 3,        // C(T)   = acc * gelu_tanh'(aux[m][n])
     EPI_F32 = 4,             // C(f32) = (beta ? C : 0) + alpha*acc
@@ -24,7 +24,7 @@ struct GemmDesc {
     void* C = nullptr; int64_t ldc = 0;
     void* C2 = nullptr;
     const float* bias = nullptr;
-    const float* resid = nullptr; int64_t ldr = 0;
+    const void* resid = nullptr; int64_t ldr = 0;   // storage type
     const void* aux = nullptr; int64_t ldaux = 0;
     float alpha = 1.f;
     int beta = 0;
@@ -46,15 +46,16 @@ void gemm_setup();
 size_t gemm_lds_bytes();
 
 // ------------------------------------------------------------------ elementwise / rows
-hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, float* x,
-                         int B, int T, int C, hipStream_t s);
-// LayerNorm forward: out(T) = (x - mean) * rstd * w + b ; saves mean, rstd (fp32)
-hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
+// x(T) [B*T, C] = wte[idx] + wpe[t] (the residual stream is in the storage type)
+hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, void* x, int B, int T,
+                         int C, int is_bf16, hipStream_t s);
+// LayerNorm forward: out(T) = (x(T) - mean) * rstd * w + b ; saves mean, rstd (fp32)
+hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s);
 // LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; partial[blk][0:C] = sum dh*xhat,
 // [C:2C] = sum dh, [2C:3C] = sum of the incoming dres (zero without accumulate) over the
-// block's rows. dh and the residual gradient dres are in the storage type T.
-hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
+// block's rows. dh, x and the residual gradient dres are in the storage type T.
+hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, const float* rstd,
                               const float* w, void* dres, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);

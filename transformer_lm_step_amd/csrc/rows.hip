@@ -7,31 +7,52 @@
 
 namespace gpt2k {
 
+// 4 consecutive values of a storage-type row as fp32, and back
+template <typename T> DEV void store4(T* p, float a, float b, float c, float d);
+template <> DEV void store4<float>(float* p, float a, float b, float c, float d) { *(float4*)p = make_float4(a, b, c, d); }
+template <> DEV void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *(bf16x4*)p = v;
+}
+template <typename T> DEV float4 load4(const T* p);
+template <> DEV float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <> DEV float4 load4<bf16>(const bf16* p) {
+    const bf16x4 v = *(const bf16x4*)p;
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
 // ================================================================== embedding forward
 // x[b,t,:] = wte[idx[b,t],:] + wpe[t,:] ("Code you'll write", forward pass: token and
-// position embeddings are added). One wave per token row, float4 accesses.
+// position embeddings are added), stored in the storage type. One wave per token row.
+template <typename T>
 __global__ void embed_forward_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
-                                     const float* __restrict__ wpe, float* __restrict__ x, int rows,
-                                     int T, int C) {
+                                     const float* __restrict__ wpe, T* __restrict__ x, int rows,
+                                     int T_, int C) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
-    const int t = row % T;
+    const int t = row % T_;
     const int64_t id = idx[row];
     const int nv = C >> 2;
     const float4* e = (const float4*)(wte + id * C);
     const float4* p = (const float4*)(wpe + (int64_t)t * C);
-    float4* o = (float4*)(x + (int64_t)row * C);
+    T* o = x + (int64_t)row * C;
     for (int c = lane; c < nv; c += 64) {
         const float4 a = e[c], b = p[c];
-        o[c] = make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+        store4<T>(o + 4 * c, a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
     }
 }
 
-hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, float* x, int B, int T,
-                         int C, hipStream_t s) {
+hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, void* x, int B, int T,
+                         int C, int is_bf16, hipStream_t s) {
     const int rows = B * T;
-    hipLaunchKernelGGL(embed_forward_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe, x, rows, T, C);
+    if (is_bf16)
+        hipLaunchKernelGGL(embed_forward_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe, (bf16*)x,
+                           rows, T, C);
+    else
+        hipLaunchKernelGGL(embed_forward_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe,
+                           (float*)x, rows, T, C);
     return hipGetLastError();
 }
 
@@ -41,25 +62,9 @@ hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe,
 constexpr int LN_NV = 8;
 constexpr float LN_EPS = 1e-5f;
 
-template <typename T> DEV void store4(T* p, float a, float b, float c, float d);
-template <> DEV void store4<float>(float* p, float a, float b, float c, float d) { *(float4*)p = make_float4(a, b, c, d); }
-template <> DEV void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    bf16x4 v;
-    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
-    *(bf16x4*)p = v;
-}
-template <typename T> DEV float4 load4(const T* p);
-template <> DEV float4 load4<float>(const float* p) { return *(const float4*)p; }
-template <> DEV float4 load4<bf16>(const bf16* p) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 v = *(const bf16x4*)p;
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
-}
-
 // NV = float4 per lane needed for C (C <= 256 * NV): the row is held in registers sized to C
 template <typename T, int NV>
-__global__ void __launch_bounds__(256) layernorm_forward_kernel(const float* __restrict__ x, const float* __restrict__ w,
+__global__ void __launch_bounds__(256) layernorm_forward_kernel(const T* __restrict__ x, const float* __restrict__ w,
                                                                 const float* __restrict__ b, T* __restrict__ out,
                                                                 float* __restrict__ mean, float* __restrict__ rstd,
                                                                 int rows, int C) {
@@ -67,13 +72,13 @@ __global__ void __launch_bounds__(256) layernorm_forward_kernel(const float* __r
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int nv = C >> 2;
-    const float4* xr = (const float4*)(x + (int64_t)row * C);
+    const T* xr = x + (int64_t)row * C;
     float4 v[NV];
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
-        v[j] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j] = c < nv ? load4<T>(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
     }
     const float mu = wave_sum(s) / (float)C;
@@ -101,7 +106,7 @@ __global__ void __launch_bounds__(256) layernorm_forward_kernel(const float* __r
 }
 
 template <typename T>
-static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const float* x, const float* w, const float* b, T* out,
+static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const T* x, const float* w, const float* b, T* out,
                                 float* mean, float* rstd, int rows, int C) {
 #define LNF(NV) hipLaunchKernelGGL((layernorm_forward_kernel<T, NV>), g, dim3(256), 0, s, x, w, b, out, mean, rstd, rows, C)
     if (nv4 <= 64) LNF(1);
@@ -113,12 +118,12 @@ static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const float* x, 
     return hipGetLastError();
 }
 
-hipError_t layernorm_forward(const float* x, const float* w, const float* b, void* out, float* mean,
+hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     dim3 g((rows + 3) / 4);
-    if (is_bf16) return ln_fwd_launch<bf16>(C / 4, g, s, x, w, b, (bf16*)out, mean, rstd, rows, C);
-    return ln_fwd_launch<float>(C / 4, g, s, x, w, b, (float*)out, mean, rstd, rows, C);
+    if (is_bf16) return ln_fwd_launch<bf16>(C / 4, g, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+    return ln_fwd_launch<float>(C / 4, g, s, (const float*)x, w, b, (float*)out, mean, rstd, rows, C);
 }
 
 // Backward through y = xhat*w + b, xhat = (x - mean)*rstd:
@@ -135,7 +140,7 @@ int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 
 // NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers
 template <typename T, int NV>
 __global__ void __launch_bounds__(256) layernorm_backward_kernel(
-    const T* __restrict__ dh, const float* __restrict__ x, const float* __restrict__ mean,
+    const T* __restrict__ dh, const T* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, T* __restrict__ dres,
     int accumulate, float* __restrict__ partial, int rows, int C) {
     extern __shared__ float sred[];  // [4][3C]
@@ -152,7 +157,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     for (int row = r0; row < r0 + LNB_ROWS && row < rows; ++row) {
         const float mu = mean[row], r = rstd[row];
         const T* dr = dh + (int64_t)row * C;
-        const float4* xr = (const float4*)(x + (int64_t)row * C);
+        const T* xr = x + (int64_t)row * C;
         T* o = dres + (int64_t)row * C;
         float4 xh[NV], dxh[NV], old[NV];
         float s1 = 0.f, s2 = 0.f;
@@ -161,7 +166,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
             const int c = lane + 64 * j;
             xh[j] = dxh[j] = old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < nv) {
-                const float4 d = load4<T>(dr + 4 * c), xx = xr[c];
+                const float4 d = load4<T>(dr + 4 * c), xx = load4<T>(xr + 4 * c);
                 if (accumulate) old[j] = load4<T>(o + 4 * c);
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
@@ -203,7 +208,7 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
 }
 
 template <typename T>
-static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const T* dh, const float* x,
+static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const T* dh, const T* x,
                                 const float* mean, const float* rstd, const float* w, T* dres, int acc,
                                 float* partial, int rows, int C) {
 #define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<T, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
@@ -217,16 +222,16 @@ static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, cons
     return hipGetLastError();
 }
 
-hipError_t layernorm_backward(const void* dh, const float* x, const float* mean, const float* rstd,
+hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, const float* rstd,
                               const float* w, void* dres, int accumulate_dres, float* partial,
                               int nblk, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     const size_t lds = 12 * (size_t)C * sizeof(float);
     if (is_bf16)
-        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, x, mean, rstd, w, (bf16*)dres,
-                                   accumulate_dres, partial, rows, C);
-    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, x, mean, rstd, w, (float*)dres,
-                                accumulate_dres, partial, rows, C);
+        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, (const bf16*)x, mean, rstd, w,
+                                   (bf16*)dres, accumulate_dres, partial, rows, C);
+    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, (const float*)x, mean, rstd, w,
+                                (float*)dres, accumulate_dres, partial, rows, C);
 }
 
 // Column sums of partial [np, n] (row stride `stride`), deterministic, in two launches:
@@ -824,7 +829,6 @@ DEV void adamw4(float4& pp, const float4& gg, float4& mm, float4& vv, float keep
     }
 }
 DEV void store_shadow4(bf16* sh, int64_t i, const float4& pp) {
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     bf16x4 b;
     b[0] = (bf16)pp.x; b[1] = (bf16)pp.y; b[2] = (bf16)pp.z; b[3] = (bf16)pp.w;
     ((bf16x4*)sh)[i] = b;
