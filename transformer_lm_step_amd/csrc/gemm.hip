@@ -709,11 +709,12 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // row sums of A: the waves of the first column tile with wn == 0 add up the A fragments
-    // they read anyway (lane group g holds 8 of each 32 k for row 16i + (lane & 15))
-    float rs[FM];
+    // row sums of A: the waves of the first column tile with wn == 0 multiply the A fragments
+    // they read anyway by a fragment of ones (one more MFMA per fragment, fp32 accumulation);
+    // every column of rs[i] then holds the sum over k of row 16i + (lane & 15)
+    floatx4 rs[ROWSUM ? FM : 1];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) rs[i] = 0.f;
+    for (int i = 0; i < (ROWSUM ? FM : 1); ++i) rs[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     const bool do_rs = ROWSUM && tn == 0 && wn == 0;
 
     if (nt > 0) {
@@ -742,16 +743,9 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
             for (int i = 0; i < FM; ++i) af[i] = mm_frag<ALAY, BM>(As, wm * TM + 16 * i, ks, lane);
             if constexpr (ROWSUM) {
                 if (do_rs) {
-                    // each 32-bit word holds two bf16: their fp32 values are (w << 16) and
-                    // (w & 0xffff0000)
+                    const bf16x8 ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-                    for (int i = 0; i < FM; ++i) {
-                        const uint4 w = __builtin_bit_cast(uint4, af[i]);
-                        rs[i] += ((__uint_as_float(w.x << 16) + __uint_as_float(w.x & 0xffff0000u)) +
-                                  (__uint_as_float(w.y << 16) + __uint_as_float(w.y & 0xffff0000u))) +
-                                 ((__uint_as_float(w.z << 16) + __uint_as_float(w.z & 0xffff0000u)) +
-                                  (__uint_as_float(w.w << 16) + __uint_as_float(w.w & 0xffff0000u)));
-                    }
+                    for (int i = 0; i < FM; ++i) mma8(rs[i], ones, af[i]);
                 }
             }
 #pragma unroll
@@ -767,11 +761,8 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
         if (do_rs) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                float v = rs[i];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
                 const int m = m0 + wm * TM + 16 * i + (lane & 15);
-                if (lane < 16 && m < p.M) p.rowsum_part[(int64_t)blockIdx.y * p.M + m] = v;
+                if (lane < 16 && m < p.M) p.rowsum_part[(int64_t)blockIdx.y * p.M + m] = rs[i][0];
             }
         }
     }
