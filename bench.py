@@ -61,7 +61,9 @@ def class_costs(w, B, n_params, n_decay, mode="train"):
         # x, dh and the residual gradient written (storage type), mean and rstd; all but the
         # final LayerNorm's also read the incoming residual gradient
         "layernorm_bwd": ("byte", (2 * L + 1) * (3 * BT * C * es + 8 * BT) + 2 * L * BT * C * es),
-        "cross_entropy": ("byte", (1 if mode == "eval" else 2) * BT * Vp * es),
+        # the per-row, per-192-column-tile softmax statistics the logits product stores; training
+        # also reads the logits once and writes their gradient over them
+        "cross_entropy": ("byte", BT * (Vp // 192) * 8 + (0 if mode == "eval" else 2 * BT * Vp * es)),
         "embed_fwd": ("byte", BT * C * (4 + 4 + es)),   # fp32 wte and wpe rows, x in the storage type
     }
     if mode == "decode":
@@ -152,13 +154,13 @@ def traffic_for(kernel_class):
 
 
 # Kernel classes whose kernel can be told apart in a counter trace by name (and, for the
-# kernel shared by the qkv and lm_head products, by grid size).
+# kernel of the qkv product, by the smallest grid among its launches).
 TRAFFIC_CLASSES = {
     "gemm_fc": ("gemm_mm_kernel<0, 0, 2,", None),
-    "gemm_lm_head": ("gemm_mm_kernel<0, 0, 0,", "max"),
+    "gemm_lm_head": ("gemm_mm_kernel<0, 0, 6,", None),
     "gemm_qkv": ("gemm_mm_kernel<0, 0, 0,", "min"),
     "gemm_lm_head_dw": ("gemm_mm_kernel<1, 1, 4,", None),
-    "cross_entropy": ("cross_entropy_kernel", None),
+    "cross_entropy": ("cross_entropy_tiled_kernel", None),
     "adamw": ("adamw_kernel", None),
     "attn_fwd": ("attn_fwd_ts_kernel", None),
     "layernorm_fwd": ("layernorm_forward_kernel", None),

@@ -402,12 +402,16 @@ DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
     else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
 }
 
+constexpr float kLog2eF = 1.4426950408889634f;
+
 // Epilogue steps that depend on the column only: the scale alpha (plain output and gradient
 // accumulation) and the bias.
 template <int EPI>
-constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_F32; }
+constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_F32; }
 template <int EPI>
-constexpr bool epi_bias() { return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU; }
+constexpr bool epi_bias() {
+    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+}
 // bias of columns n..n+3 (0 past the matrix edge or without a bias)
 DEV float4 bias4(const GemmArgs& p, int n) {
     if (!p.bias) return make_float4(0.f, 0.f, 0.f, 0.f);
@@ -495,7 +499,8 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
 // 8-byte stores: the epilogue's store instructions, not its bytes, were what it waited on).
 template <int EPI>
 constexpr bool epi_wide() {
-    return EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD;
+    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU ||
+           EPI == EPI_GELU_BWD;
 }
 template <int EPI> struct EpiIn8 { typedef int T; };
 template <> struct EpiIn8<EPI_GELU_BWD> { typedef bf16x8 T; };
@@ -522,7 +527,7 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
 #pragma unroll
             for (int q = 0; q < 8; ++q) r[q] = v[q] * gelu_grad_f((float)in[q]);
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
-        } else if constexpr (EPI == EPI_BIAS_T) {
+        } else if constexpr (EPI == EPI_BIAS_T || EPI == EPI_LOGITS) {
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(v);
         } else if constexpr (EPI == EPI_BIAS_RESID) {
 #pragma unroll
@@ -563,6 +568,9 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     static_assert(64 * CPR % GTHREADS == 0, "whole chunks per thread");
     typedef typename EpiIn8<EPI>::T In;
     float* st = (float*)smem;
+    float* stats = st + 64 * LDW;          // EPI_LOGITS: 64 rows x CPR (max, sum) pairs
+    static_assert(EPI != EPI_LOGITS || 4 * 64 * LDW + 8 * 64 * CPR <= 2 * (128 + BN) * 128,
+                  "staged rows and statistics fit in the main loop's LDS");
     lds_barrier();                         // every wave is done reading the last K tile
     // the two halves (a generic lambda called twice, so both are laid out straight)
     auto half = [&](auto hc) {
@@ -594,10 +602,49 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
         for (int it = 0; it < NIT; ++it) {
             const int k = tid + it * GTHREADS, r = k / CPR, c = k - r * CPR;
             const int m = m0 + 64 * h + r, n = n0 + 8 * c;
-            epi8<EPI, CHK>(p, m, n, epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c), n),
-                           epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c + 4), n + 4), in[it]);
+            const float4 a = epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c), n);
+            const float4 b = epi_pre<EPI, BIAS>(p, *(const float4*)(st + r * LDW + 8 * c + 4), n + 4);
+            epi8<EPI, CHK>(p, m, n, a, b, in[it]);
+            if constexpr (EPI == EPI_LOGITS) {
+                // softmax statistics of the 8 stored (bf16-rounded) values: max, sum exp(z - max)
+                const float z[8] = {(float)(bf16)a.x, (float)(bf16)a.y, (float)(bf16)a.z, (float)(bf16)a.w,
+                                    (float)(bf16)b.x, (float)(bf16)b.y, (float)(bf16)b.z, (float)(bf16)b.w};
+                float mx = z[0];
+#pragma unroll
+                for (int q = 1; q < 8; ++q) mx = fmaxf(mx, z[q]);
+                float sm = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sm += __builtin_amdgcn_exp2f((z[q] - mx) * kLog2eF);
+                ((float2*)stats)[r * CPR + c] = make_float2(mx, sm);
+            }
         }
         lds_barrier();
+        if constexpr (EPI == EPI_LOGITS) {
+            // four threads per row (lanes 4r..4r+3 of a wave) merge a quarter of the row's chunk
+            // statistics each, then combine with two butterfly steps
+            static_assert(CPR % 4 == 0 && GTHREADS == 256, "a quarter row of chunks per thread");
+            constexpr int CQ = CPR / 4;
+            const int r = tid >> 2;
+            const float2* rs = (const float2*)stats + r * CPR + (tid & 3) * CQ;
+            float2 v[CQ];
+#pragma unroll
+            for (int c = 0; c < CQ; ++c) v[c] = rs[c];
+            float mx = v[0].x;
+#pragma unroll
+            for (int c = 1; c < CQ; ++c) mx = fmaxf(mx, v[c].x);
+#pragma unroll
+            for (int o = 1; o < 4; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            float sm = 0.f;
+#pragma unroll
+            for (int c = 0; c < CQ; ++c) sm += v[c].y * __builtin_amdgcn_exp2f((v[c].x - mx) * kLog2eF);
+#pragma unroll
+            for (int o = 1; o < 4; o <<= 1) sm += __shfl_xor(sm, o);
+            if ((tid & 3) == 0) {
+                const int tiles = p.N / BN;
+                ((float2*)p.C2)[(int64_t)(m0 + 64 * h + r) * tiles + n0 / BN] = make_float2(mx, sm);
+            }
+            lds_barrier();
+        }
     };
     half(std::integral_constant<int, 0>{});
     half(std::integral_constant<int, 1>{});
@@ -665,6 +712,11 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
                       int lane, int tid) {
     if constexpr (epi_wide<EPI>()) {
         const bool full = m0 + 128 <= p.M && n0 + BN <= p.N && p.vec8;
+        if constexpr (EPI == EPI_LOGITS) {  // whole tiles only (gemm_logits_tiles)
+            if (p.bias) store_staged_bf16<EPI, FM, FN, BN, false, 1>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+            else store_staged_bf16<EPI, FM, FN, BN, false, 0>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+            return;
+        }
         if (full && epi_bias<EPI>() && p.bias)
             store_staged_bf16<EPI, FM, FN, BN, false, 1>(p, acc, smem, m0, n0, wm, wn, lane, tid);
         else if (full)
@@ -965,6 +1017,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
         a.vec8 = a.vec && d.ldc % 8 == 0 && d.ldaux % 8 == 0 && d.ldr % 8 == 0;
     }
     int epi = d.epi;
+    if (epi == EPI_LOGITS && !gemm_logits_tiles(d, sizeof(T) == 2)) return hipErrorInvalidValue;
     if constexpr (sizeof(T) == 2) {
         if (skinny_ok<T>(d, nsplit)) return launch_skinny<T>(a, epi, s);
     }
@@ -984,7 +1037,9 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             // 128x128 tiles: N = 768 gives 512 tiles instead of 768, N = 2304 three rounds
             // instead of 4.5, N = 50304 = 262 x 192. 256x256 tiles measured slower everywhere.
             bool wide = false;
-            if (d.bn) {
+            if (epi == EPI_LOGITS) {
+                wide = true;
+            } else if (d.bn) {
                 wide = d.bn == 192;
             } else if (nsplit == 1 && d.N % 192 == 0) {
                 auto fill = [&](int bn) {
@@ -999,6 +1054,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 #define MM_CASE_WIDE(AL, BL, EP)                                                              \
     if (wide && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 192>(a, nsplit, s); else
             MM_CASE_WIDE(0, 0, EPI_BIAS_T)
+            MM_CASE_WIDE(0, 0, EPI_LOGITS)
             MM_CASE_WIDE(0, 0, EPI_BIAS_RESID)
             MM_CASE_WIDE(0, 1, EPI_F32)
             MM_CASE_WIDE(0, 1, EPI_BIAS_T)
@@ -1051,6 +1107,14 @@ reduce:
     return e;
 }
 
+int gemm_logits_tiles(const GemmDesc& d, int is_bf16) {
+    const bool ok = is_bf16 && !d.no_dl && d.a_layout == 0 && d.b_layout == 0 && d.nsplit <= 1 &&
+                    (d.bn == 0 || d.bn == 192) && d.M % 128 == 0 && d.N % 192 == 0 && d.ldc % 8 == 0 &&
+                    (((uintptr_t)d.C | (uintptr_t)d.C2 | (uintptr_t)d.bias) & 15) == 0 && d.C2 &&
+                    mm_ok(d, ((d.K + MM_BK - 1) / MM_BK) * MM_BK);
+    return ok ? d.N / 192 : 0;
+}
+
 int gemm_fuses_rowsum(const GemmDesc& d, int is_bf16) {
     if (!is_bf16 || d.no_dl || d.a_layout != 1) return 0;
     // the same split and tile-K rules dispatch applies
@@ -1082,7 +1146,7 @@ static void set_lds_mm() {
 }
 
 void gemm_setup() {
-    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 192>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_LOGITS, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();

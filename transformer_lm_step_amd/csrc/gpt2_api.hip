@@ -165,7 +165,7 @@ struct Plan {
     // offsets in bytes
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
-    size_t hf, meanf, rstdf, logits, loss_rows, loss, dres, dln, datt, dqkv, du, Dbuf;
+    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, dqkv, du, Dbuf;
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
     size_t mask, rowd;   // evaluation: copied mask, per-sequence double sums and counts
 };
@@ -205,6 +205,7 @@ Plan make_plan(const gpt2_config* c) {
     P.meanf = take(BT * 4);
     P.rstdf = take(BT * 4);
     P.logits = take(BT * Vp * es);
+    P.lstats = take(BT * ((Vp + 191) / 192) * 8);   // per row and 192-column tile: (max, sum)
     P.loss_rows = take(BT * 4);
     P.loss = take(256);
     P.mask = take(BT);
@@ -251,6 +252,7 @@ struct gpt2 {
     // state of the last forward
     bool have_fwd = false;
     int B = 0, T = 0;
+    int lm_tiles = 0;   // > 0: the logits product also stored per-tile softmax statistics
     // incremental decoding: sequences in the key/value cache (0: no cache) and their length
     int dec_B = 0, dec_pos = 0;
     // timing
@@ -550,10 +552,26 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.A = h->at<char>(P.hf); g.lda = C;
         g.B = h->wop(L.wte); g.ldb = C;  // tied lm_head: logits = hf wte^T, no bias
         g.M = BT; g.N = Vp; g.K = C;
-        g.epi = EPI_BIAS_T; g.C = h->at<char>(P.logits); g.ldc = Vp;
+        g.epi = EPI_LOGITS; g.C = h->at<char>(P.logits); g.ldc = Vp; g.C2 = h->at<char>(P.lstats);
+        h->lm_tiles = gemm_logits_tiles(g, bf);
+        if (!h->lm_tiles) { g.epi = EPI_BIAS_T; g.C2 = nullptr; }
         TRY(run(h, "gemm_lm_head", [&] { return gemm(g, bf, s); }));
     }
     return GPT2_OK;
+}
+
+// Per-row loss (and, with write_grad, the logits overwritten by their gradient) after
+// forward_trunk: from the statistics the logits product stored when it could, else two passes.
+static int loss_rows_after_trunk(gpt2_t* h, int BT, float* loss_rows, float* d_logits, int write_grad) {
+    const Plan& P = h->P;
+    const int Vp = h->cfg.padded_vocab_size;
+    int32_t* tgt = h->at<int32_t>(P.tgt);
+    return run(h, "cross_entropy", [&] {
+        if (h->lm_tiles)
+            return cross_entropy_tiled(h->at<char>(P.logits), h->at<float>(P.lstats), h->lm_tiles, tgt, loss_rows,
+                                       d_logits, BT, Vp, h->stream, write_grad);
+        return cross_entropy(h->at<char>(P.logits), tgt, loss_rows, d_logits, BT, Vp, h->bf16, h->stream, write_grad);
+    });
 }
 
 extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T,
@@ -577,9 +595,7 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
 
     TRY(forward_trunk(h, B, T));
     if (d_targets) {
-        TRY(run(h, "cross_entropy", [&] {
-            return cross_entropy(h->at<char>(P.logits), tgt, h->at<float>(P.loss_rows), d_logits, BT, Vp, bf, s);
-        }));
+        TRY(loss_rows_after_trunk(h, BT, h->at<float>(P.loss_rows), d_logits, 1));
         float* dl = h->at<float>(P.loss);
         TRY(run(h, "loss_mean", [&] { return mean_reduce(h->at<float>(P.loss_rows), BT, dl, s); }));
         if (d_loss) HIPTRY(hipMemcpyAsync(d_loss, dl, 4, hipMemcpyDeviceToDevice, s), "copy loss");
@@ -617,9 +633,7 @@ extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_t
     if (d_mask) HIPTRY(hipMemcpyAsync(mask, d_mask, (size_t)BT, hipMemcpyDeviceToDevice, s), "copy mask");
     TRY(forward_trunk(h, B, T));
     float* loss_rows = h->at<float>(P.loss_rows);
-    TRY(run(h, "cross_entropy", [&] {
-        return cross_entropy(h->at<char>(P.logits), tgt, loss_rows, nullptr, BT, Vp, bf, s, /*write_grad=*/0);
-    }));
+    TRY(loss_rows_after_trunk(h, BT, loss_rows, nullptr, /*write_grad=*/0));
     // without a mask the batch mean is the training forward's loss, reduced the same way
     TRY(run(h, "eval_rows", [&] {
         return masked_row_loss(loss_rows, mask, B, T, h->at<double>(P.rowd), d_row_sum, d_row_mean,

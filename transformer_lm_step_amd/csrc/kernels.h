@@ -14,6 +14,9 @@ enum Epi {
     EPI_GELU_BWD = 3,        // C(T)   = acc * gelu_tanh'(aux[m][n])
     EPI_F32 = 4,             // C(f32) = (beta ? C : 0) + alpha*acc
     EPI_PARTIAL = 5,         // internal: split-K partials
+    EPI_LOGITS = 6,          // C(bf16) = alpha*acc + bias[n], and C2 (fp32 pairs) = for every row m
+                             // and 192-column tile t: (max, sum exp(z - max)) of that row's
+                             // bf16-rounded outputs in the tile, at C2[2 * (m * tiles + t)]
 };
 
 struct GemmDesc {
@@ -39,6 +42,9 @@ struct GemmDesc {
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+// number of 192-column tiles (the C2 row length of EPI_LOGITS) if gemm() can run d with
+// EPI_LOGITS (bf16, both operands k-contiguous, whole 128 x 192 tiles), else 0
+int gemm_logits_tiles(const GemmDesc& d, int is_bf16);
 // 1 if gemm() computes d.rowsum itself (LDS-streamed bf16 path), 0 if the caller must
 int gemm_fuses_rowsum(const GemmDesc& d, int is_bf16);
 void gemm_pick_tile(int M, int N, int nsplit, int is_bf16, int* bm, int* bn);
@@ -77,6 +83,12 @@ int colsum_partial_floats(int rows, int n);
 // copy of the logits.
 hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows, float* logits_f32,
                          int n_rows, int Vp, int is_bf16, hipStream_t s, int write_grad = 1);
+// the same for bf16 logits whose per-tile softmax statistics the lm_head product produced
+// (EPI_LOGITS: `tiles` (max, sum) pairs per row): one pass over each row instead of two, and
+// none without write_grad or logits_f32
+hipError_t cross_entropy_tiled(void* logits, const float* stats, int tiles, const int32_t* targets,
+                               float* loss_rows, float* logits_f32, int n_rows, int Vp, hipStream_t s,
+                               int write_grad = 1);
 // per sequence b of B (T positions): sum, count and mean of loss_rows over the positions the
 // mask selects (mask null: all); rowd [2B] doubles (sum, count); row_sum / row_mean / total
 // may be null; total = mean over every selected position of the batch

@@ -408,6 +408,88 @@ hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows,
     return hipGetLastError();
 }
 
+// The same loss and gradient when the logits product has already stored, for every row and every
+// 192-column tile of it, the tile's (max, sum exp(z - max)) over the stored values: the row's
+// log-sum-exp comes from merging its `tiles` pairs (in a fixed order), so the logits are read
+// once (only to write the gradient over them, or to copy them to fp32) instead of twice.
+__global__ void __launch_bounds__(256) cross_entropy_tiled_kernel(bf16* __restrict__ z, const float2* __restrict__ stats,
+                                                                  int tiles, const int32_t* __restrict__ targets,
+                                                                  float* __restrict__ loss_rows, float* __restrict__ z_f32,
+                                                                  int rows, int Vp, int write_grad) {
+    __shared__ float smax[256 / 64], ssum[256 / 64];
+    const int row = blockIdx.x;
+    bf16* zr = z + (int64_t)row * Vp;
+    const float2* sr = stats + (int64_t)row * tiles;
+    float mx = -INFINITY, sm = 0.f;
+    for (int t = threadIdx.x; t < tiles; t += 256) {
+        const float2 v = sr[t];
+        const float nm = fmaxf(mx, v.x);
+        sm = (mx == -INFINITY ? 0.f : sm * __expf(mx - nm)) + v.y * __expf(v.x - nm);
+        mx = nm;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float om = __shfl_xor(mx, o), os = __shfl_xor(sm, o);
+        const float nm = fmaxf(mx, om);
+        sm = (mx == -INFINITY ? 0.f : sm * __expf(mx - nm)) + (om == -INFINITY ? 0.f : os * __expf(om - nm));
+        mx = nm;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { smax[w] = mx; ssum[w] = sm; }
+    __syncthreads();
+    float M = smax[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, smax[i]);
+    float S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S += smax[i] == -INFINITY ? 0.f : ssum[i] * __expf(smax[i] - M);
+    const float lse = M + __logf(S);
+    const int y = targets[row];
+    if (threadIdx.x == 0) loss_rows[row] = lse - (float)zr[y];
+    if (!write_grad && !z_f32) return;
+    __syncthreads();  // zr[y] read before any overwrite
+    const float inv_n = 1.0f / (float)rows;
+    const float lse2 = lse * 1.4426950408889634f;
+    const int nvec = Vp / 8;
+    // CE_U chunks per thread and trip, all loaded before any is used (more bytes in flight)
+    constexpr int CE_U = 4;
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += 256 * CE_U) {
+        uint4 raw[CE_U];
+#pragma unroll
+        for (int u = 0; u < CE_U; ++u)
+            if (v0 + 256 * u < nvec) raw[u] = ld16(zr + (v0 + 256 * u) * 8);
+#pragma unroll
+        for (int u = 0; u < CE_U; ++u) {
+            const int v = v0 + 256 * u;
+            if (v >= nvec) break;
+            bf16* e = (bf16*)&raw[u];
+            float vals[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vals[q] = (float)e[q];
+            if (z_f32) {
+                *(float4*)(z_f32 + (int64_t)row * Vp + v * 8) = make_float4(vals[0], vals[1], vals[2], vals[3]);
+                *(float4*)(z_f32 + (int64_t)row * Vp + v * 8 + 4) = make_float4(vals[4], vals[5], vals[6], vals[7]);
+            }
+            if (write_grad) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float p = __builtin_amdgcn_exp2f(vals[q] * 1.4426950408889634f - lse2);
+                    e[q] = (bf16)((p - (v * 8 + q == y ? 1.f : 0.f)) * inv_n);
+                }
+                st16(zr + v * 8, raw[u]);
+            }
+        }
+    }
+}
+
+hipError_t cross_entropy_tiled(void* logits, const float* stats, int tiles, const int32_t* targets, float* loss_rows,
+                               float* logits_f32, int n_rows, int Vp, hipStream_t s, int write_grad) {
+    if (Vp % 8 || tiles < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cross_entropy_tiled_kernel, dim3(n_rows), dim3(256), 0, s, (bf16*)logits, (const float2*)stats,
+                       tiles, targets, loss_rows, logits_f32, n_rows, Vp, write_grad);
+    return hipGetLastError();
+}
+
 // ================================================================== evaluation reductions
 // Completion scoring ([LVN] chapter 3:28:16-3:41:50): every sequence b is scored by the
 // cross-entropy of the positions its mask selects (the ending's tokens): their sum, their
