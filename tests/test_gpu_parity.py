@@ -174,6 +174,23 @@ def test_accumulation_matches_big_batch_oracle():
     _grads_cosine(st, ref_g)
 
 
+@pytest.mark.parametrize("T", [100, 37])
+def test_ragged_context_two_layers_bf16(T):
+    """124M widths (head size 64, the LDS-streamed attention kernels) with 2 layers and a
+    context that is not a multiple of 64: the last query and key blocks have waves wholly past
+    the sequence end, which run the masked computation and store nothing."""
+    note(f"124M ragged T={T} L=2 bf16 B=2")
+    ov = (("n_layer", 2), ("seq_len", T))
+    params, batches, ref_loss, ref_g, _ = oracle_step("gpt2_step", ov, 2, 1, True, False)
+    w = synthetic.workload("gpt2_step", **dict(ov))
+    st = make_step(w, "bf16", max_batch=2)
+    st.set_params(params)
+    loss, _ = st.forward(*batches[0])
+    assert abs(loss - ref_loss) <= 2e-2
+    st.backward(1.0, False)
+    _grads_cosine(st, ref_g)
+
+
 def test_xl_shape_two_layers_bf16():
     """1558M widths (C=1600, 25 heads, MLP 6400) with 2 layers, one sequence of 1024."""
     note("xl-shape L=2 bf16 B=1")

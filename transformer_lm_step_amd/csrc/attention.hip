@@ -628,7 +628,12 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
         dma_wait_barrier();
         if (c + 1 < nchunk) issue(c + 1);
         const int k0 = c * 64;
-        if (!wave_live || k0 > qw0 + QW - 1) continue;
+        // With one 16-query block per wave every wave needs every chunk up to the diagonal; a
+        // wave past the sequence end computes on zero queries and stores nothing. Skipping it
+        // here would make the compiler copy the accumulators on every iteration.
+        if constexpr (QB > 1) {
+            if (!wave_live || k0 > qw0 + QW - 1) continue;
+        }
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
         floatx4 s[4][QB];
@@ -772,7 +777,11 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
         dma_wait_barrier();
         if (qc + 1 < nqc) issue(qc + 1);
         const int q0 = qc * 64;
-        if (!wave_live || q0 + 63 < kw0) continue;
+        // as in the forward: with one 16-key block per wave no wave skips a chunk except past
+        // the sequence end, where it computes masked zeros and stores nothing
+        if constexpr (KBW > 1) {
+            if (!wave_live || q0 + 63 < kw0) continue;
+        }
         const char* sQ = smem + ((qc - qc0) & 1) * STAGE;
         const char* sO = sQ + TS_BYTES;
         const float* sL = (const float*)(sQ + 2 * TS_BYTES);
@@ -928,7 +937,9 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         dma_wait_barrier();
         if (c + 1 < nchunk) issue(c + 1);
         const int k0 = c * 64;
-        if (!wave_live || k0 > qw0 + QW - 1) continue;
+        if constexpr (QBW > 1) {   // see the forward
+            if (!wave_live || k0 > qw0 + QW - 1) continue;
+        }
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
         floatx4 s[4][QBW], dp[4][QBW];
