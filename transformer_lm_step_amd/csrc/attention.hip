@@ -603,15 +603,20 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
         for (int ks = 0; ks < 2; ++ks)
             qf[qb][ks] = q < T_ ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
     }
-    floatx4 o[4][QB];
-    float mrun[QB], lrun[QB];
+    // o: the output rows, unnormalized; lacc: the softmax denominators, accumulated by the
+    // same products as o with a fragment of ones in place of V^T (every entry of lacc[qb] is
+    // then the sum over the keys so far of query column (lane & 15)); mref: the reference
+    // maxima the exponentials are taken against
+    floatx4 o[4][QB], lacc[QB];
+    float mref[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        mrun[qb] = -INFINITY;
-        lrun[qb] = 0.f;
+        lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        mref[qb] = -INFINITY;
     }
+    const bf16x8 ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 
     const int kend = min(q0 + QBLK, T_);
     const int nchunk = (kend + 63) / 64;
@@ -669,29 +674,33 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
                     mx = fmaxf(mx, v);
                 }
             mx = group4_max(mx) * sc;
-            const float mnew = fmaxf(mrun[qb], mx);
-            const float msafe = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = exp2_raw(mrun[qb] - msafe);
-            float ls = 0.f;
+            // Lazy rescaling: the reference maximum moves (and o and the denominators are
+            // rescaled) only when some query of the wave has a score more than 2^8 above it,
+            // so the exponentials stay <= 256 and the normalization o / l, which shares the
+            // reference, is unchanged. The first chunk always sets it (mref = -inf).
+            if (__builtin_amdgcn_ballot_w64(mx > mref[qb] + 8.f)) {
+                const float mnew = fmaxf(mref[qb], mx);
+                const float alpha = exp2_raw(mref[qb] - (mnew == -INFINITY ? 0.f : mnew));
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d][qb] *= alpha;
+                lacc[qb] *= alpha;
+                mref[qb] = mnew;
+            }
+            const float msafe = mref[qb] == -INFINITY ? 0.f : mref[qb];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = exp2_raw(fmaf(s[kb][qb][i], sc, -msafe));
-                    s[kb][qb][i] = p;
-                    ls += p;
-                }
-            lrun[qb] = lrun[qb] * alpha + ls;
-            mrun[qb] = mnew;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) o[d][qb] *= alpha;
+                for (int i = 0; i < 4; ++i) s[kb][qb][i] = exp2_raw(fmaf(s[kb][qb][i], sc, -msafe));
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             bf16x8 pf[QB];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) pf[qb] = frag_from_acc<bf16>(s[2 * st][qb], s[2 * st + 1][qb]);
+            for (int qb = 0; qb < QB; ++qb) {
+                pf[qb] = frag_from_acc<bf16>(s[2 * st][qb], s[2 * st + 1][qb]);
+                mma8(lacc[qb], ones, pf[qb]);
+            }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const bf16x8 vf = ts_tr(sV, d * 16, 32 * st, 32 * st + 16, lane);
@@ -705,13 +714,13 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = qw0 + qb * 16 + col;
-        const float ltot = group4_sum(lrun[qb]);
+        const float ltot = lacc[qb][0];
         if (q >= T_) continue;
         const float inv = 1.0f / ltot;
         bf16* yr = y + ((int64_t)b * T_ + q) * C + h * HS;
 #pragma unroll
         for (int d = 0; d < 4; ++d) store4v<bf16>(yr + d * 16 + g * 4, o[d][qb], inv);
-        if (g == 0) lse[(int64_t)bh * T_ + q] = (mrun[qb] + log2f(ltot)) * kLn2;
+        if (g == 0) lse[(int64_t)bh * T_ + q] = (mref[qb] + log2f(ltot)) * kLn2;
     }
 }
 
@@ -720,7 +729,7 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
 template <int KBW>
 __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
                                                                     const bf16* __restrict__ dy,
-                                                                    const float* __restrict__ lse,
+                                                                    const float* __restrict__ lse2,
                                                                     const float* __restrict__ D,
                                                                     bf16* __restrict__ dqkv, int T_, int H, float sc,
                                                                     float scale) {
@@ -734,7 +743,7 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
     const int64_t ld = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T_ * ld;
     const bf16* dyb = dy + (int64_t)b * T_ * C;
-    const float* lse_bh = lse + (int64_t)bh * T_;
+    const float* lse_bh = lse2 + (int64_t)bh * T_;   // base-2 log-sum-exp
     const float* D_bh = D + (int64_t)bh * T_;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -814,14 +823,16 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
                 for (int i = 0; i < 4; ++i) {
                     const int ql = qb * 16 + g * 4 + i;
                     const int q = q0 + ql;
-                    const float L = sL[ql] * kLog2e, Dq = sD[ql];
+                    const float L = sL[ql], Dq = sD[ql];
 #pragma unroll
                     for (int kb = 0; kb < KBW; ++kb) {
                         const int key = kw0 + kb * 16 + col;
-                        float p = exp2_raw(fmaf(s[qb][kb][i], sc, -L));
-                        if constexpr (decltype(masked)::value) {
-                            if (!(key <= q && q < T_)) p = 0.f;
-                        }
+                        float a = fmaf(s[qb][kb][i], sc, -L);
+                        // masked entries get -inf added before the exponential (exp2(-inf) = 0):
+                        // a select between two constants, which the compiler keeps branch-free
+                        // (a select of the loaded value itself it turns into a branch per entry)
+                        if constexpr (decltype(masked)::value) a += ((key <= q) & (q < T_)) ? 0.f : -INFINITY;
+                        const float p = exp2_raw(a);
                         s[qb][kb][i] = p;
                         dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
                     }
@@ -914,7 +925,12 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         dsum += __shfl_xor(dsum, 32);
         L[qb] = ok ? lse[(int64_t)bh * T_ + q] * kLog2e : 0.f;
         Dq[qb] = ok ? dsum : 0.f;
-        if (ok && g == 0) D[(int64_t)bh * T_ + q] = dsum;   // for the dK/dV kernel, which runs next
+        // for the dK/dV kernel, which runs next: D, and after all B*H*T of them the log-sum-exp
+        // already in base 2 (one multiply per query here instead of one per score there)
+        if (ok && g == 0) {
+            D[(int64_t)bh * T_ + q] = dsum;
+            D[(int64_t)gridDim.y * T_ + (int64_t)bh * T_ + q] = L[qb];
+        }
     }
     floatx4 dq[4][QBW];
 #pragma unroll
@@ -971,10 +987,9 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = k0 + kb * 16 + g * 4 + i;
-                        float p = exp2_raw(fmaf(s[kb][qb][i], sc, -L[qb]));
-                        if constexpr (decltype(masked)::value) {
-                            if (!(key <= q && key < T_)) p = 0.f;
-                        }
+                        float a = fmaf(s[kb][qb][i], sc, -L[qb]);
+                        if constexpr (decltype(masked)::value) a += ((key <= q) & (key < T_)) ? 0.f : -INFINITY;  // as in dK/dV
+                        const float p = exp2_raw(a);
                         dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
                     }
                 }
@@ -1054,7 +1069,7 @@ static hipError_t bwd_launch(const void* qkv, const void* y, const void* dy, con
         if (e != hipSuccess) return e;
         const dim3 gk((T_ + 64 * ATT_DKV_KB - 1) / (64 * ATT_DKV_KB), B * H);
         attn_bwd_dkv_ts_kernel<ATT_DKV_KB><<<gk, dim3(A_THREADS), ts_dkv_lds(), s>>>(
-            (const bf16*)qkv, (const bf16*)dy, lse, (const float*)D, (bf16*)dqkv, T_, H, sc, scale);
+            (const bf16*)qkv, (const bf16*)dy, D + n, (const float*)D, (bf16*)dqkv, T_, H, sc, scale);
         return hipGetLastError();
     }
     attn_bwd_pre_kernel<T, HS><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>((const T*)y, (const T*)dy, D,

@@ -215,7 +215,7 @@ Plan make_plan(const gpt2_config* c) {
     P.datt = take(BT * C * es);
     P.dqkv = take(BT * 3 * C * es);
     P.du = take(BT * F * es);
-    P.Dbuf = take(BT * H * 4);
+    P.Dbuf = take(2 * BT * H * 4);   // attention backward: D, then the base-2 log-sum-exp
     size_t sk = 0;
     const int shapes[4][2] = {{(int)(3 * C), (int)C}, {(int)C, (int)C}, {(int)F, (int)C}, {(int)C, (int)F}};
     for (auto& s : shapes) {

@@ -122,7 +122,8 @@ hipError_t fill(float* p, int64_t n, float v, hipStream_t s);
 // qkv(T) [B*T, 3C] (q | k | v, head h = columns h*hs..), y(T) [B*T, C], lse fp32 [B*H*T]
 hipError_t attention_forward(const void* qkv, void* y, float* lse, int B, int T, int H, int hs,
                              int is_bf16, hipStream_t s);
-// dy(T) [B*T, C], D scratch fp32 [B*H*T], dqkv(T) [B*T, 3C]
+// dy(T) [B*T, C], D scratch fp32 [2*B*H*T] (the softmax-gradient term per query, then the
+// log-sum-exp in base 2 for the key-block kernel), dqkv(T) [B*T, 3C]
 hipError_t attention_backward(const void* qkv, const void* y, const void* dy, const float* lse,
                               float* D, void* dqkv, int B, int T, int H, int hs, int is_bf16,
                               hipStream_t s);
