@@ -167,6 +167,9 @@ struct Plan {
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
     size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, dqkv, du, Dbuf;
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
+    // LayerNorm backward partials: one set per LayerNorm (ln_f, then ln_2 and ln_1 of each layer
+    // from the last), reduced together after the backward; the sets' gradient offsets
+    size_t lnset_stride, lnscr, lnoff;
     size_t mask, rowd;   // evaluation: copied mask, per-sequence double sums and counts
 };
 
@@ -224,7 +227,11 @@ Plan make_plan(const gpt2_config* c) {
     }
     P.splitk = take(sk ? sk : 256);
     P.rspart = take((size_t)16 * std::max(3 * C, F) * 4);   // <= 16 splits x the widest bias
-    P.lnpart = take((size_t)layernorm_backward_blocks((int)BT) * 3 * C * 4);
+    const int nln = 2 * c->n_layer + 1;
+    P.lnset_stride = (size_t)layernorm_backward_blocks((int)BT) * 3 * C;
+    P.lnpart = take(nln * P.lnset_stride * 4);
+    P.lnscr = take((size_t)sum_sets_scratch_floats(nln, (int)(3 * C)) * 4);
+    P.lnoff = take((size_t)2 * nln * 8);
     P.cspart = take((size_t)colsum_partial_floats((int)BT, (int)std::max(3 * C, F)) * 4);
     P.sumscr = take((size_t)sum_scratch_floats((int)std::max(3 * C, F)) * 4);
     P.normpart = take((size_t)norm_blocks() * 4);
@@ -431,6 +438,22 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
     if (e == hipSuccess) e = hipMemsetAsync(h->at<float>(h->P.m), 0, N * 4, h->stream);
     if (e == hipSuccess) e = hipMemsetAsync(h->at<float>(h->P.v), 0, N * 4, h->stream);
     if (e == hipSuccess && h->bf16) e = refresh_shadow(h->params(), h->at<char>(h->P.shadow), h->L.decay_end, h->stream);
+    if (e == hipSuccess) {
+        // gradient offsets of the LayerNorm partial sets, in the order the backward fills them:
+        // weight and bias (adjacent in the arena), then the bias of the projection whose residual
+        // add feeds the LayerNorm (none for ln_f)
+        const int nl = cfg->n_layer, nln = 2 * nl + 1;
+        std::vector<int64_t> off(2 * nln);
+        off[0] = h->L.lnf_w;
+        off[nln] = -1;
+        for (int l = nl - 1, i = 1; l >= 0; --l, i += 2) {
+            off[i] = h->L.ln2_w[l];
+            off[nln + i] = h->L.b_pr[l];
+            off[i + 1] = h->L.ln1_w[l];
+            off[nln + i + 1] = h->L.b_o[l];
+        }
+        e = hipMemcpy(h->at<int64_t>(h->P.lnoff), off.data(), off.size() * 8, hipMemcpyHostToDevice);
+    }
     if (e != hipSuccess) { delete h; return set_error(GPT2_EHIP, "init: %s", hipGetErrorString(e)); }
     *out = h;
     return GPT2_OK;
@@ -767,6 +790,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     // bf16 input gradient of the following product, cast to fp32 where LayerNorm runs
     char* dln = h->at<char>(P.dln);
     float* lnpart = h->at<float>(P.lnpart);
+    int lnset = 0;   // the next LayerNorm partial set
     float* cspart = h->at<float>(P.cspart);
     float* sumscr = h->at<float>(P.sumscr);
     void* skpart = h->at<char>(P.splitk);
@@ -774,17 +798,12 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
 
     // LayerNorm backward; with bias_off >= 0 the incoming residual gradient's column sum
     // (gathered by the same kernel) is the bias gradient of the projection at that offset
-    auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
-                      int64_t bias_off) -> int {
-        TRY(run(h, "layernorm_bwd", [&] {
-            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, accum_dres, lnpart, lnblk, BT, C, bf, s);
-        }));
-        // LayerNorm weight and bias gradients are adjacent in the arena; the third partial
-        // (column sums of the incoming residual gradient) is the projection bias gradient
-        if (bias_off < 0)
-            return run(h, "ln_param_grad", [&] { return sum_partials(lnpart, lnblk, 2 * C, 3 * C, grd + w_off, acc, sumscr, s); });
-        return run(h, "ln_param_grad", [&] {
-            return sum_partials2(lnpart, lnblk, 3 * C, 3 * C, grd + w_off, 2 * C, grd + bias_off, acc, sumscr, s);
+    // (the weight, bias and projection-bias gradients come from the partial sets after the last
+    // LayerNorm, in one reduction; the sets' order is the one the offsets table was built in)
+    auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres) -> int {
+        float* part = lnpart + (size_t)lnset++ * P.lnset_stride;
+        return run(h, "layernorm_bwd", [&] {
+            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, accum_dres, part, lnblk, BT, C, bf, s);
         });
     };
     // weight gradient dW (+)= dy^T x; with bias_off >= 0 also the bias gradient db (+)= colsum(dy),
@@ -820,7 +839,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.epi = EPI_F32; g.C = grd + L.wte; g.ldc = C; g.alpha = grad_scale; g.beta = acc;
         TRY(run(h, "gemm_lm_head_dw", [&] { return gemm(g, bf, s); }));
     }
-    TRY(ln_bwd(h->at<char>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0, -1));
+    TRY(ln_bwd(h->at<char>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0));
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
@@ -843,7 +862,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
-        TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1, L.b_pr[l]));
+        TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1));
         // x_mid = x_in + y Wo^T + bo
         TRY(dw(dres, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
         {
@@ -868,8 +887,15 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the attn.c_proj bias gradient)
-        TRY(ln_bwd(h->at<char>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1, L.b_o[l]));
+        TRY(ln_bwd(h->at<char>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1));
     }
+    // LayerNorm weight and bias gradients, and the projection bias gradients (column sums of the
+    // residual gradient entering each ln_2 / ln_1), from every set at once
+    TRY(run(h, "ln_param_grad", [&] {
+        const int64_t* off = h->at<int64_t>(P.lnoff);
+        return sum_partials_sets(lnpart, lnset, (int64_t)P.lnset_stride, lnblk, 3 * C, 3 * C, grd, off, 2 * C,
+                                 off + (2 * c.n_layer + 1), acc, h->at<float>(P.lnscr), s);
+    }));
     // embeddings: token rows scatter-add on top of the lm_head gradient, position rows
     if (!acc && T < c.block_size)
         HIPTRY(fill(grd + L.wpe + (int64_t)T * C, (int64_t)(c.block_size - T) * C, 0.f, s), "zero wpe tail");

@@ -73,6 +73,15 @@ int sum_scratch_floats(int n);
 // the same with two destinations: columns [0, n1) into out1, [n1, n) into out2
 hipError_t sum_partials2(const float* partial, int nblk, int n, int64_t stride, float* out1, int n1, float* out2,
                          int accumulate, float* scratch, hipStream_t s);
+// sum_partials2 over nset partial sets of the same shape in one pass (set i at partial +
+// i*set_stride): columns [0, n1) of set i into base + off1[i], [n1, n) into base + off2[i]
+// (skipped when off2[i] < 0); off1, off2 are device arrays of nset offsets (floats); the
+// per-column order, and so every result, is sum_partials2's. scratch holds
+// sum_sets_scratch_floats(nset, n) floats.
+hipError_t sum_partials_sets(const float* partial, int nset, int64_t set_stride, int nblk, int n, int64_t stride,
+                             float* base, const int64_t* off1, int n1, const int64_t* off2, int accumulate,
+                             float* scratch, hipStream_t s);
+int sum_sets_scratch_floats(int nset, int n);
 // column sums of a [rows, n] matrix (storage T or f32) into out[n] (+)=, deterministic
 hipError_t colsum(const void* x, int x_is_f32, int is_bf16, int rows, int n, float* partial,
                   float* out, int accumulate, float* scratch, hipStream_t s);

@@ -242,9 +242,14 @@ hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, 
 constexpr int SUM_SLICES = 16;
 int sum_scratch_floats(int n) { return SUM_SLICES * n; }
 
+// blockIdx.z selects one of several partial sets of the same shape (set_stride floats apart),
+// each with its own SUM_SLICES x n block of scratch
 __global__ void __launch_bounds__(256) colred1_kernel(const float* __restrict__ partial, int np, int n,
-                                                      int64_t stride, float* __restrict__ scratch) {
+                                                      int64_t stride, float* __restrict__ scratch,
+                                                      int64_t set_stride) {
     __shared__ float red[4][64];
+    partial += (int64_t)blockIdx.z * set_stride;
+    scratch += (int64_t)blockIdx.z * SUM_SLICES * n;
     const int col = blockIdx.x * 64 + (threadIdx.x & 63), grp = threadIdx.x >> 6;
     const int per = (np + SUM_SLICES - 1) / SUM_SLICES;
     const int p0 = blockIdx.y * per;
@@ -281,7 +286,7 @@ __global__ void __launch_bounds__(256) colred2_kernel(const float* __restrict__ 
 hipError_t sum_partials2(const float* partial, int np, int n, int64_t stride, float* out1, int n1, float* out2,
                          int accumulate, float* scratch, hipStream_t s) {
     hipLaunchKernelGGL(colred1_kernel, dim3((n + 63) / 64, SUM_SLICES), dim3(256), 0, s, partial, np, n, stride,
-                       scratch);
+                       scratch, (int64_t)0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(colred2_kernel, dim3((n + 255) / 256), dim3(256), 0, s, scratch, n, out1, n1, out2, accumulate);
@@ -291,6 +296,38 @@ hipError_t sum_partials2(const float* partial, int np, int n, int64_t stride, fl
 hipError_t sum_partials(const float* partial, int np, int n, int64_t stride, float* out, int accumulate,
                         float* scratch, hipStream_t s) {
     return sum_partials2(partial, np, n, stride, out, n, nullptr, accumulate, scratch, s);
+}
+
+// Second stage for several sets at once (blockIdx.y = set): columns [0, n1) go to
+// base[off1[set] + col], columns [n1, n) to base[off2[set] + col - n1], or nowhere when
+// off2[set] < 0.
+__global__ void __launch_bounds__(256) colred2_sets_kernel(const float* __restrict__ scratch, int n,
+                                                           float* __restrict__ base, const int64_t* __restrict__ off1,
+                                                           int n1, const int64_t* __restrict__ off2, int accumulate) {
+    const int col = blockIdx.x * 256 + threadIdx.x, set = blockIdx.y;
+    if (col >= n) return;
+    if (col >= n1 && off2[set] < 0) return;
+    const float* sc = scratch + (int64_t)set * SUM_SLICES * n;
+    float v = 0.f;
+#pragma unroll
+    for (int z = 0; z < SUM_SLICES; ++z) v += sc[(int64_t)z * n + col];
+    float* o = col < n1 ? base + off1[set] + col : base + off2[set] + (col - n1);
+    *o = accumulate ? *o + v : v;
+}
+
+int sum_sets_scratch_floats(int nset, int n) { return nset * SUM_SLICES * n; }
+
+hipError_t sum_partials_sets(const float* partial, int nset, int64_t set_stride, int np, int n, int64_t stride,
+                             float* base, const int64_t* off1, int n1, const int64_t* off2, int accumulate,
+                             float* scratch, hipStream_t s) {
+    if (nset < 1) return hipSuccess;
+    hipLaunchKernelGGL(colred1_kernel, dim3((n + 63) / 64, SUM_SLICES, nset), dim3(256), 0, s, partial, np, n, stride,
+                       scratch, set_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(colred2_sets_kernel, dim3((n + 255) / 256, nset), dim3(256), 0, s, scratch, n, base, off1, n1,
+                       off2, accumulate);
+    return hipGetLastError();
 }
 
 // column sums of x [rows, n]: stage 1 writes one partial row per row-slice, stage 2 is
