@@ -118,10 +118,66 @@ static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const T* x, cons
     return hipGetLastError();
 }
 
+// bf16 rows of C = 256 * NC: one half-wave (32 lanes) per row, NC 16-byte chunks per lane, so
+// a wave keeps two rows' loads in flight with half the load instructions. Same arithmetic as
+// the kernel above (mean, then the centered variance, each summed over the row in fp32).
+template <int NC>
+__global__ void __launch_bounds__(256) layernorm_forward_half_kernel(const bf16* __restrict__ x,
+                                                                     const float* __restrict__ w,
+                                                                     const float* __restrict__ b,
+                                                                     bf16* __restrict__ out, float* __restrict__ mean,
+                                                                     float* __restrict__ rstd, int rows, int C) {
+    const int l = threadIdx.x & 31;
+    const int row = blockIdx.x * 8 + (threadIdx.x >> 5);
+    const bool live = row < rows;
+    const bf16* xr = x + (int64_t)(live ? row : rows - 1) * C;
+    float v[NC][8];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const uint4 raw = ld16(xr + 8 * (l + 32 * j));
+        const bf16* e = (const bf16*)&raw;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { v[j][q] = (float)e[q]; s += v[j][q]; }
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o);
+    const float mu = s / (float)C;
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) { const float d = v[j][q] - mu; s2 += d * d; }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) s2 += __shfl_xor(s2, o);
+    const float r = 1.0f / sqrtf(s2 / (float)C + LN_EPS);
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = 8 * (l + 32 * j);
+        const float4 w0 = *(const float4*)(w + c), w1 = *(const float4*)(w + c + 4);
+        const float4 b0 = *(const float4*)(b + c), b1 = *(const float4*)(b + c + 4);
+        const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        bf16x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (bf16)((v[j][q] - mu) * r * ww[q] + bb[q]);
+        *(bf16x8*)(out + (int64_t)row * C + c) = o;
+    }
+    if (l == 0) { mean[row] = mu; rstd[row] = r; }
+}
+
 hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int is_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
     dim3 g((rows + 3) / 4);
+    if (is_bf16 && (C == 512 || C == 768 || C == 1024) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+        const dim3 g8((rows + 7) / 8);
+        if (C == 512) hipLaunchKernelGGL(layernorm_forward_half_kernel<2>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+        else if (C == 768) hipLaunchKernelGGL(layernorm_forward_half_kernel<3>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+        else hipLaunchKernelGGL(layernorm_forward_half_kernel<4>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+        return hipGetLastError();
+    }
     if (is_bf16) return ln_fwd_launch<bf16>(C / 4, g, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
     return ln_fwd_launch<float>(C / 4, g, s, (const float*)x, w, b, (float*)out, mean, rstd, rows, C);
 }
