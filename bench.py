@@ -163,7 +163,7 @@ TRAFFIC_CLASSES = {
     "cross_entropy": ("cross_entropy_tiled_kernel", None),
     "adamw": ("adamw_kernel", None),
     "attn_fwd": ("attn_fwd_ts_kernel", None),
-    "layernorm_fwd": ("layernorm_forward_kernel", None),
+    "layernorm_fwd": ("layernorm_forward_half_kernel", None),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
