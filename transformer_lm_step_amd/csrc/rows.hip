@@ -544,13 +544,16 @@ __global__ void __launch_bounds__(256) cross_entropy_tiled_kernel(bf16* __restri
     const float inv_n = 1.0f / (float)rows;
     const float lse2 = lse * 1.4426950408889634f;
     const int nvec = Vp / 8;
-    // CE_U chunks per thread and trip, all loaded before any is used (more bytes in flight)
+    // CE_U chunks per thread and trip, all loaded before any is used (more bytes in flight).
+    // The logits are read once and dz is read next by the products, from HBM either way (1.6 GB
+    // at B=16): non-temporal accesses keep both out of the caches (this pass 0.69 -> 0.63 ms).
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     constexpr int CE_U = 4;
     for (int v0 = threadIdx.x; v0 < nvec; v0 += 256 * CE_U) {
         uint4 raw[CE_U];
 #pragma unroll
         for (int u = 0; u < CE_U; ++u)
-            if (v0 + 256 * u < nvec) raw[u] = ld16(zr + (v0 + 256 * u) * 8);
+            if (v0 + 256 * u < nvec) raw[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)(zr + (v0 + 256 * u) * 8)));
 #pragma unroll
         for (int u = 0; u < CE_U; ++u) {
             const int v = v0 + 256 * u;
@@ -569,7 +572,7 @@ __global__ void __launch_bounds__(256) cross_entropy_tiled_kernel(bf16* __restri
                     const float p = __builtin_amdgcn_exp2f(vals[q] * 1.4426950408889634f - lse2);
                     e[q] = (bf16)((p - (v * 8 + q == y ? 1.f : 0.f)) * inv_n);
                 }
-                st16(zr + v * 8, raw[u]);
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4, raw[u]), (u32x4*)(zr + v * 8));
             }
         }
     }
