@@ -516,6 +516,13 @@ DEV bf16x8 to_bf16x8(const float (&v)[8]) {
 // epi4 on 8 consecutive columns n..n+7 (a: the first 4 values, b: the next 4, with alpha and
 // the bias applied); `in` is the 8 residual values or saved pre-activations (GELU derivative)
 // on the vector path
+
+// 16-byte store that bypasses the caches (for outputs read again only much later or from HBM
+// anyway)
+DEV void st16_nt(void* p, const bf16x8& v) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
+}
 template <int EPI, bool CHECK = true>
 DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b, const typename EpiIn8<EPI>::T& in) {
     if (CHECK && m >= p.M) return;
@@ -527,7 +534,9 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
 #pragma unroll
             for (int q = 0; q < 8; ++q) r[q] = v[q] * gelu_grad_f((float)in[q]);
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
-        } else if constexpr (EPI == EPI_BIAS_T || EPI == EPI_LOGITS) {
+        } else if constexpr (EPI == EPI_LOGITS) {
+            st16_nt((bf16*)p.C + o, to_bf16x8(v));
+        } else if constexpr (EPI == EPI_BIAS_T) {
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(v);
         } else if constexpr (EPI == EPI_BIAS_RESID) {
 #pragma unroll
