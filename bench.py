@@ -1,15 +1,19 @@
 """Benchmark of the GPT-2 training step on one MI355X.
 
 One timed step = forward with loss + backward + clip/AdamW of GPT-2 124M at B=16, T=1024 in
-bf16 mode (the "gpt2_step" workload; other workloads with --workload). Inputs are seeded
-synthetic Zipf(1.1) token batches already resident in device memory; parameters follow the
-GPT-2 initialization. Prints one JSON line.
+bf16 mode (the "gpt2_step" workload; other workloads with --workload). bf16 mode is the
+autocast recipe: bf16 product and attention operands, an fp32 residual stream and gradient
+(--dtype bf16_res16 times the variant that stores those in bf16 too; the default run also
+times it briefly and reports it under "variant_bf16_res16", never as `value`). Inputs are
+seeded synthetic Zipf(1.1) token batches already resident in device memory; parameters
+follow the GPT-2 initialization. Prints one JSON line.
 
   value       tokens/s of the whole job (one GPU)
   mfu         tokens/s * (6N + 6*L*T*C) / dense bf16 MFMA peak (2.5166e15 FLOP/s)
-  roofline    the kernel class with the largest share of step time, timed live with HIP
-              events on the library's stream during the timed steps: algorithmic FLOPs or
-              bytes per launch / mean launch time, against the MI355X peak
+  roofline    the kernel class with the largest share of step time (every class, single- or
+              multi-shape), timed live with HIP events on the library's stream during the
+              timed steps: algorithmic FLOPs or bytes per launch (the class's total per step
+              over its launches per step) / mean launch time, against the MI355X peak
   kernels     ms per step of every kernel class (same live timing)
   cpu_baseline  the CPU oracle (float32 numpy) on one sequence of the same
               model, forward + backward + AdamW, on this host's cores
@@ -36,12 +40,16 @@ def model_flops_per_token(w, n_params, mode="train"):
     return f // 3 if mode in ("eval", "decode") else f     # forward only: 2N + 2LTC
 
 
-def class_costs(w, B, n_params, n_decay, mode="train"):
+def class_costs(w, B, n_params, n_decay, mode="train", res16=False):
     """Algorithmic cost of each kernel class per step: ('flop', total) or ('byte', total).
     A step is w.micro_steps forward/backward passes of B sequences and one optimizer update
-    (mode "eval": one forward-only scoring pass, whose cross-entropy reads the logits once)."""
+    (mode "eval": one forward-only scoring pass, whose cross-entropy reads the logits once).
+    res16: the residual stream and its gradient are bf16 (else fp32, with a bf16 copy of the
+    gradient written for the products)."""
     BT, C, F, Vp, L, T, H = B * w.seq_len, w.n_embd, w.mlp_hidden, w.padded_vocab_size, w.n_layer, w.seq_len, w.n_head
-    es = 2  # bf16 storage
+    es = 2  # bf16 storage of operands and activations
+    er = 2 if res16 else 4  # residual stream and its gradient
+    cp = 0 if res16 else 2  # bf16 copy of an fp32 residual gradient
     k = w.micro_steps
     attn_fwd = 2 * 2 * B * H * (T * (T + 1) / 2) * (C // H)            # QK^T and PV, causal half
     per_micro = {
@@ -56,15 +64,15 @@ def class_costs(w, B, n_params, n_decay, mode="train"):
         "gemm_dw": ("flop", 2 * BT * C * (3 * C + C + F + F) * L),
         "attn_fwd": ("flop", attn_fwd * L),
         "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
-        # the residual stream and the LayerNorm output in the storage type, mean and rstd
-        "layernorm_fwd": ("byte", (2 * L + 1) * (2 * BT * C * es + 8 * BT)),
-        # x, dh and the residual gradient written (storage type), mean and rstd; all but the
-        # final LayerNorm's also read the incoming residual gradient
-        "layernorm_bwd": ("byte", (2 * L + 1) * (3 * BT * C * es + 8 * BT) + 2 * L * BT * C * es),
+        # the residual stream read, the bf16 LayerNorm output written, mean and rstd
+        "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * (er + es) + 8 * BT)),
+        # dh (bf16) and x read, the residual gradient (and its bf16 copy) written, mean and rstd;
+        # all but the final LayerNorm's also read the incoming residual gradient
+        "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * (es + 2 * er + cp) + 8 * BT) + 2 * L * BT * C * er),
         # the per-row, per-192-column-tile softmax statistics the logits product stores; training
         # also reads the logits once and writes their gradient over them
         "cross_entropy": ("byte", BT * (Vp // 192) * 8 + (0 if mode == "eval" else 2 * BT * Vp * es)),
-        "embed_fwd": ("byte", BT * C * (4 + 4 + es)),   # fp32 wte and wpe rows, x in the storage type
+        "embed_fwd": ("byte", BT * C * (4 + 4 + er)),   # fp32 wte and wpe rows, x in the residual type
     }
     if mode == "decode":
         # one new position per sequence: the products stream their bf16 weights (B rows are
@@ -225,44 +233,19 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
     print(json.dumps(rec, indent=1))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2_step")
-    ap.add_argument("--mode", choices=("train", "eval", "decode"), default="train",
-                    help="eval: time forward-only scoring (gpt2_evaluate, the validation-loss form) of "
-                         "one micro-batch instead of the training step; decode: time key/value-cache "
-                         "decoding steps with top-50 sampling of the workload's B sequences after an "
-                         "8-token prompt (one step = one new token per sequence)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
-                    help="after timing, run device copies of BYTES bytes (counter calibration)")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="build profiles/traffic.json from two rocprofv3 --pmc counter traces and exit")
-    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
-    args = ap.parse_args()
-    if args.traffic_from:
-        traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_bytes,
-                     os.path.join(ROOT, "profiles", "traffic.json"))
-        return
-    if args.gpus != 1:
-        print(f"bench.py: the GPT-2 step library runs on one GPU; --gpus {args.gpus} is not supported "
-              "(data-parallel sharding over several GPUs is not implemented)", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=True):
+    """Create a handle for workload w in `dtype`, run `warmup` untimed steps, a per-class timing
+    pass, then `steps` timed steps (the dominant class keeps its HIP events). Returns a dict of
+    the measurements; the handle is destroyed before returning."""
     import torch
 
     import synthetic
     import transformer_lm_step_amd as G
 
-    w = synthetic.workload(args.workload)
     B, T = w.batch, w.seq_len
+    res16 = dtype == "bf16_res16"
     cfg = G.make_config(w.n_layer, w.n_head, w.n_embd, w.block_size, w.vocab_size, w.padded_vocab_size, B,
-                        w.dtype)
+                        dtype if w.dtype == "bf16" else w.dtype)
     st = G.GPT2Step(cfg, seed=w.seed_base + 1000)
     n_params = st.n_params
     n_decay = G.gpt2_decay_end(cfg)
@@ -279,7 +262,7 @@ def main():
 
     if args.mode == "decode":
         prompt_len = 8
-        n_dec = args.warmup + max(1, min(5, args.steps)) + args.steps
+        n_dec = warmup + max(1, min(5, steps)) + steps
         if prompt_len + n_dec > T:
             raise SystemExit(f"bench.py: {prompt_len} + {n_dec} decoding positions exceed block_size {T}")
         gen = torch.Generator().manual_seed(w.seed_base + 3000)
@@ -309,89 +292,148 @@ def main():
         step_no[0] += 1
         G.gpt2_adamw_step(h, w.lr, 0.9, 0.95, 1e-8, 0.1, 1.0, step_no[0], d_norm.data_ptr())
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # per-class live timing over a separate pass to find the dominant class
     kernels = {}
-    if not args.no_kernel_timing:
+    if kernel_timing:
+        nrep = max(1, min(5, steps))
         G.gpt2_timing_begin(h, None)
-        for _ in range(max(1, min(5, args.steps))):
+        for _ in range(nrep):
             step()
         G.gpt2_timing_end(h)
-        nrep = max(1, min(5, args.steps))
         for c in G.kernel_classes():
             ms, n = G.gpt2_timing_get(h, c)
             if n:
                 kernels[c] = {"ms_per_step": ms / nrep, "launches_per_step": n / nrep}
-    costs = class_costs(w, B, n_params, n_decay, args.mode)
-    single = [c for c in ("gemm_lm_head", "gemm_lm_head_dx", "gemm_lm_head_dw", "gemm_fc", "gemm_qkv",
-                          "gemm_attn_proj", "gemm_mlp_proj", "attn_fwd", "cross_entropy", "adamw",
-                          "layernorm_fwd", "topk_sample") if c in kernels and c in costs]
-    dominant = max(single, key=lambda c: kernels[c]["ms_per_step"]) if single else None
+    costs = class_costs(w, B, n_params, n_decay, args.mode, res16)
+    cands = [c for c in kernels if c in costs]
+    dominant = max(cands, key=lambda c: kernels[c]["ms_per_step"]) if (cands and roofline) else None
 
     # timed region: the dominant class keeps its HIP events (on the library's stream)
     if dominant:
         G.gpt2_timing_begin(h, dominant)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    roofline = None
+    roof = None
     if dominant:
         G.gpt2_timing_end(h)
         ms, n = G.gpt2_timing_get(h, dominant)
         kind, total = costs[dominant]
-        per_launch = total / (n / args.steps) if n else 0
+        per_launch = total / (n / steps) if n else 0
         avg_s = ms / 1e3 / n
         if kind == "flop":
             achieved, peak, unit, bound = per_launch / avg_s / 1e12, PEAK_BF16 / 1e12, "TFLOP/s", "mfma"
         else:
             achieved, peak, unit, bound = per_launch / avg_s / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
-        roofline = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": round(peak, 1),
-                    "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic_for(dominant),
-                    "launch_ms": round(ms / n, 4), "per_launch": per_launch,
-                    "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
-    if args.mode != "train":
-        k = 1
-    loss = float(d_loss[:k].sum().item()) / k if args.mode != "decode" else None
-    ms_step = el / args.steps * 1e3
-    tokens = B * T * k if args.mode != "decode" else B
-    value = tokens / (el / args.steps)
-    fpt = model_flops_per_token(w, n_params, args.mode)
-    mfu = value * fpt / PEAK_BF16
+        roof = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": round(peak, 1),
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic_for(dominant) if not res16 else None,
+                "launch_ms": round(ms / n, 4), "launches_per_step": n / steps, "per_launch": per_launch,
+                "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
+    kk = k if args.mode == "train" else 1
+    loss = float(d_loss[:kk].sum().item()) / kk if args.mode != "decode" else None
+    tokens = B * T * kk if args.mode != "decode" else B
     for c, d in kernels.items():
         if c in costs:
             kind, total = costs[c]
             rate = total / (d["ms_per_step"] / 1e3)
             d["achieved"] = round(rate / (1e12 if kind == "flop" else 1e9), 2)
             d["unit"] = "TFLOP/s" if kind == "flop" else "GB/s"
+    st.close()
+    del st
+    torch.cuda.synchronize()
+    return {"el": el, "ms_step": el / steps * 1e3, "value": tokens / (el / steps), "loss": loss,
+            "roofline": roof, "kernels": kernels, "n_params": n_params, "k": kk}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_step")
+    ap.add_argument("--dtype", choices=("bf16", "bf16_res16"), default="bf16",
+                    help="bf16: the autocast recipe (fp32 residual stream and gradient), timed for `value`; "
+                         "bf16_res16: the variant with a bf16 residual stream and gradient")
+    ap.add_argument("--no-variant", action="store_true",
+                    help="skip the short timing of the bf16_res16 variant after the main measurement")
+    ap.add_argument("--mode", choices=("train", "eval", "decode"), default="train",
+                    help="eval: time forward-only scoring (gpt2_evaluate, the validation-loss form) of "
+                         "one micro-batch instead of the training step; decode: time key/value-cache "
+                         "decoding steps with top-50 sampling of the workload's B sequences after an "
+                         "8-token prompt (one step = one new token per sequence)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
+                    help="after timing, run device copies of BYTES bytes (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="build profiles/traffic.json from two rocprofv3 --pmc counter traces and exit")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_bytes,
+                     os.path.join(ROOT, "profiles", "traffic.json"))
+        return
+    if args.gpus != 1:
+        print(f"bench.py: the GPT-2 step library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(data-parallel sharding over several GPUs is not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synthetic
+
+    w = synthetic.workload(args.workload)
+    B, T = w.batch, w.seq_len
+    r = run_workload(args, w, args.dtype, args.steps, args.warmup, kernel_timing=not args.no_kernel_timing)
+    k = r["k"]
+    fpt = model_flops_per_token(w, r["n_params"], args.mode)
+    mfu = r["value"] * fpt / PEAK_BF16
+    dtype_name = {"bf16": "bf16", "bf16_res16": "bf16 (bf16 residual stream)"}[args.dtype] \
+        if w.dtype == "bf16" else "f32"
     out = {
         "metric": ("training tokens/sec and MFU, GPT-2 124M B=16 T=1024 bf16, 1 MI355X"
                    if args.workload == "gpt2_step" else f"training tokens/sec, {args.workload}")
         if args.mode == "train" else (f"evaluation tokens/sec (forward-only scoring), {args.workload}"
                                       if args.mode == "eval" else
                                       f"decoded tokens/sec (key/value cache, top-50 sampling), {args.workload}"),
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "value": round(r["value"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype_name, "data": "synthetic",
         "config": {"workload": f"{w.name}: GPT-2 L={w.n_layer} H={w.n_head} C={w.n_embd}, B={B}, T={T}, "
                                f"vocab {w.vocab_size} padded to {w.padded_vocab_size}, "
                                + (f"{k} micro-step(s) + AdamW per step" if args.mode == "train"
                                   else "one forward-only scoring pass (no backward, no update) per step"
                                   if args.mode == "eval" else
                                   f"one decoding step (one new token for each of B sequences, positions "
-                                  f"8..{8 + args.warmup + max(1, min(5, args.steps)) + args.steps - 1}) per step"),
+                                  f"8..{8 + args.warmup + max(1, min(5, args.steps)) + args.steps - 1}) per step")
+                               + ("; residual stream and its gradient fp32, product operands bf16"
+                                  if args.dtype == "bf16" and w.dtype == "bf16" else
+                                  "; residual stream and its gradient bf16" if w.dtype == "bf16" else ""),
                    "global_batch": B * k, "seq_len": T, "parallelism": "single GPU"},
         "mfu": round(mfu, 4), "model_flops_per_token": fpt, "peak_flops": PEAK_BF16,
-        "loss": round(loss, 5) if loss is not None else None, "roofline": roofline, "kernels": kernels,
+        "loss": round(r["loss"], 5) if r["loss"] is not None else None, "roofline": r["roofline"],
+        "kernels": r["kernels"],
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    if (args.mode == "train" and args.dtype == "bf16" and w.dtype == "bf16" and not args.no_variant):
+        # the narrower-storage variant, timed briefly on a handle of its own (never `value`)
+        v = run_workload(args, w, "bf16_res16", max(5, args.steps // 2), 2, kernel_timing=False, roofline=False)
+        out["variant_bf16_res16"] = {
+            "dtype": "bf16 (bf16 residual stream)", "value": round(v["value"], 1), "unit": "tokens/s",
+            "ms_per_step": round(v["ms_step"], 3), "mfu": round(v["value"] * fpt / PEAK_BF16, 4),
+            "steps": max(5, args.steps // 2), "warmup": 2,
+            "note": "residual stream and its gradient stored in bf16: narrower than the autocast recipe"}
     if args.copy_calib:
+        dev = torch.device("cuda:0")
         src = torch.empty(args.copy_calib, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -401,7 +443,6 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.mode)
     print(json.dumps(out))
-    st.close()
 
 
 if __name__ == "__main__":

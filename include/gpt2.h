@@ -40,12 +40,21 @@ extern "C" {
 #define GPT2_ESTATE (-2) /* call out of order, e.g. backward without a forward that had targets */
 #define GPT2_EHIP (-3)   /* a HIP runtime call or kernel launch failed; the message names it */
 
-/* Arithmetic modes. GPT2_FP32: every tensor fp32, products on fp32 MFMA (a check mode).
- * GPT2_BF16: matrix-product and attention operands bf16 with fp32 accumulation; residual
- * stream, LayerNorm statistics, softmax and loss math, master weights, gradients and AdamW
- * moments stay fp32 (the autocast recipe of chapter 1:36:50-1:48:25 of the lecture notes). */
+/* Arithmetic modes (what each stores; every accumulation is fp32 in all three):
+ * GPT2_FP32        every tensor fp32, products on fp32 MFMA (a check mode).
+ * GPT2_BF16        the autocast recipe of chapter 1:36:50-1:48:25 of the lecture notes:
+ *                  product and attention operands bf16 (bf16 copies of the 2-D weights; LayerNorm
+ *                  outputs, q|k|v, attention output, GELU input and output, logits and their
+ *                  gradient, and every activation gradient that feeds a product); the residual
+ *                  stream (embedding sum and every residual add) and its gradient fp32, with a
+ *                  bf16 copy of that gradient as the products' operand; LayerNorm statistics,
+ *                  softmax and loss math, master weights, gradients and AdamW moments fp32.
+ * GPT2_BF16_RES16  GPT2_BF16 with the residual stream and its gradient also stored in bf16
+ *                  (narrower than the autocast recipe; fewer bytes per LayerNorm and residual add).
+ * fp32 -> bf16 conversions round to nearest even. */
 #define GPT2_FP32 0
 #define GPT2_BF16 1
+#define GPT2_BF16_RES16 2
 
 /* Model and capacity. The counting and layout calls need only positive sizes, n_embd a
  * multiple of n_head and padded_vocab_size >= vocab_size. Sizing the workspace and creating
@@ -62,7 +71,7 @@ typedef struct gpt2_config {
     int32_t vocab_size;        /* V: token ids lie in [0, V) */
     int32_t padded_vocab_size; /* Vp: rows of wte and width of the softmax */
     int32_t max_batch;
-    int32_t dtype;             /* GPT2_FP32 or GPT2_BF16 */
+    int32_t dtype;             /* GPT2_FP32, GPT2_BF16 or GPT2_BF16_RES16 */
 } gpt2_config;
 
 typedef struct gpt2 gpt2_t;
@@ -244,7 +253,8 @@ int gpt2_timing_end(gpt2_t* h);
 int gpt2_timing_get(gpt2_t* h, const char* name, double* total_ms, int64_t* launches);
 const char* gpt2_kernel_class(int32_t i);
 
-/* Copy a saved activation of the last forward for inspection: which = "x_in", "h1", "qkv",
+/* Copy a saved activation of the last forward for inspection: which = "x_in" (the residual
+ * stream entering layer `layer`; layer = n_layer is ln_f's input), "h1", "qkv",
  * "att", "lse", "h2", "u", "a", "x_out", "hf" (layer ignored for the last two) or "dz"
  * (after a forward with targets: the cross-entropy gradient (softmax - onehot)/(B*T),
  * unscaled). Values are converted to fp32 into d_dst (device), which must hold

@@ -1,7 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle on the same seeded inputs.
 
 Bars: fp32 check mode, per-tensor max|d|/max|ref| <= 1e-4 for logits, loss and gradients;
-bf16 mode, |loss - ref| <= 2e-2 and per-tensor gradient cosine >= 0.999 (float64 metrics).
+bf16 modes, |loss - ref| <= 2e-2 and per-tensor gradient cosine >= 0.999 (float64 metrics).
+"bf16" is the autocast recipe (fp32 residual stream and gradient); "bf16_res16" also stores
+the residual stream and its gradient in bf16.
 The oracle runs in float64. Sizes span several tiles and ragged tails; the 124M, 1558M-shaped
 and accumulation workloads run at their real widths, with fewer layers or sequences where the
 oracle would otherwise take minutes (the kernels and launch shapes per layer are the same).
@@ -105,11 +107,15 @@ def test_tiny_fp32_accumulate_flag():
     _grads_fp32_check(st, ref_g)
 
 
-def test_tiny_bf16_matches_oracle():
-    note("tiny bf16")
+BF16_MODES = ["bf16", "bf16_res16"]
+
+
+@pytest.mark.parametrize("mode", BF16_MODES)
+def test_tiny_bf16_matches_oracle(mode):
+    note(f"tiny {mode}")
     params, batches, ref_loss, ref_g, _ = oracle_step("tiny", (), 4, 1, True, False)
     w = synthetic.workload("tiny")
-    st = make_step(w, "bf16")
+    st = make_step(w, mode)
     st.set_params(params)
     x, y = batches[0]
     loss, _ = st.forward(x, y)
@@ -144,11 +150,12 @@ def test_124m_forward_bf16_loss_b4():
     assert abs(loss - float(out["loss"])) <= 2e-2, (loss, out["loss"])
 
 
-def test_124m_step_bf16_gradients_b2():
-    note("124M bf16 step B=2")
+@pytest.mark.parametrize("mode", BF16_MODES)
+def test_124m_step_bf16_gradients_b2(mode):
+    note(f"124M {mode} step B=2")
     params, batches, ref_loss, ref_g, _ = oracle_step("gpt2_step", (), 2, 1, True, False)
     w = synthetic.workload("gpt2_step")
-    st = make_step(w, "bf16", max_batch=2)
+    st = make_step(w, mode, max_batch=2)
     st.set_params(params)
     loss, _ = st.forward(*batches[0])
     assert abs(loss - ref_loss) <= 2e-2
@@ -191,17 +198,63 @@ def test_ragged_context_two_layers_bf16(T):
     _grads_cosine(st, ref_g)
 
 
-def test_xl_shape_two_layers_bf16():
+@pytest.mark.parametrize("mode", BF16_MODES)
+def test_xl_shape_two_layers_bf16(mode):
     """1558M widths (C=1600, 25 heads, MLP 6400) with 2 layers, one sequence of 1024."""
-    note("xl-shape L=2 bf16 B=1")
+    note(f"xl-shape L=2 {mode} B=1")
     params, batches, ref_loss, ref_g, _ = oracle_step("gpt2_xl", (("n_layer", 2),), 1, 1, True, False)
     w = synthetic.workload("gpt2_xl", n_layer=2)
-    st = make_step(w, "bf16", max_batch=1)
+    st = make_step(w, mode, max_batch=1)
     st.set_params(params)
     loss, _ = st.forward(*batches[0])
     assert abs(loss - ref_loss) <= 2e-2
     st.backward(1.0, False)
     _grads_cosine(st, ref_g)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", BF16_MODES)
+def test_step_b16_two_layers_full_gradients(mode):
+    """The benchmark's launch shapes against the oracle: B=16, T=1024 (16,384 rows) at the
+    124M widths with 2 layers. At this row count every N=768 product (the projections'
+    forwards, every input-gradient product with N=768, the lm_head input gradient) and the
+    vocabulary product take 128x192 tiles, as in the timed step. Loss and every gradient."""
+    note(f"124M {mode} B=16 L=2 full gradients")
+    ov = (("n_layer", 2),)
+    params, batches, ref_loss, ref_g, _ = oracle_step("gpt2_step", ov, 16, 1, True, False)
+    w = synthetic.workload("gpt2_step", n_layer=2)
+    st = make_step(w, mode)
+    st.set_params(params)
+    loss, _ = st.forward(*batches[0])
+    assert abs(loss - ref_loss) <= 2e-2, (loss, ref_loss)
+    st.backward(1.0, False)
+    _grads_cosine(st, ref_g)
+    st.close()
+
+
+@pytest.mark.parametrize("mode,T", [("fp32", 2048), ("bf16_res16", 2048), ("fp32", 1900)])
+def test_embedding_backward_chunked(mode, T):
+    """More rows than one sort chunk of the embedding backward (9 sequences of T tokens:
+    more than 16,384 rows, so the ids are sorted in two chunks and the second chunk's sums add
+    onto the first's): tiny widths with block_size T, every gradient against the oracle
+    (fp32 check mode 1e-4; the bf16 residual-gradient mode by cosine)."""
+    note(f"chunked embedding backward {mode} B=9 T={T}")
+    w = synthetic.workload("tiny", block_size=T, seq_len=T, batch=9)
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    p64 = f64(params)
+    out = O.forward(p64, w.n_layer, w.n_head, x, y, want_logits=False)
+    ref_g = O.backward(p64, w.n_layer, w.n_head, out["cache"], 1.0)
+    st = make_step(w, mode)
+    st.set_params(params)
+    loss, _ = st.forward(x, y)
+    st.backward(1.0, False)
+    if mode == "fp32":
+        assert abs(loss - out["loss"]) <= 1e-4 * abs(out["loss"])
+        _grads_fp32_check(st, ref_g)
+    else:
+        assert abs(loss - out["loss"]) <= 2e-2
+        _grads_cosine(st, ref_g)
 
 
 # ------------------------------------------------------------------ full-size invariants
@@ -219,7 +272,8 @@ def test_full_step_b16_invariants():
     b = 5
     ref = O.forward(f64(params), w.n_layer, w.n_head, x[b:b + 1], y[b:b + 1], want_cache=False)
     lg = logits[b].cpu().numpy()
-    assert cosine(lg, ref["logits"][0]) >= 0.999
+    worst = min(cosine(lg[t], ref["logits"][0, t]) for t in range(w.seq_len))
+    assert worst >= 0.999, worst
     z = ref["logits"][0]
     closed = math.log(w.padded_vocab_size) + z.var(axis=-1).mean() / 2
     assert abs(loss - closed) <= 0.05
@@ -294,6 +348,62 @@ def test_full_ctx2048_b32_invariants():
     assert torch.equal(lrest, logits2[b + 1:])
 
 
+@pytest.mark.timeout(900)
+def test_xl_full_size_invariants():
+    """The 1558M-shaped micro-step at its real size (48 layers, 25 heads, C=1600, B=4,
+    T=1024, bf16): every position of a sampled sequence's logits against the oracle, that
+    sequence's mean loss against the oracle's, the batch loss within 0.5 of ln(V), bitwise
+    determinism of the backward, bitwise causality.
+
+    The Gaussian-logit closed form ln(Vp) + var(z)/2 that the 124M tests use is not a gate
+    here: it assumes each target's logit has mean zero, but with Zipf-distributed tokens the
+    48 layers carry a component along the embeddings of frequent tokens (which are also
+    frequent targets), so the target logit has a positive mean (+0.16 on the sampled sequence in the
+    oracle, whose log-sum-exp does follow the closed form) and the loss sits 0.1-0.2 below it."""
+    note("xl bf16 full L=48 B=4")
+    w = synthetic.workload("gpt2_xl")
+    params = synthetic.init_params(w)
+    (x, y), = synthetic.micro_batches(w, 1)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    loss, logits = st.forward(x, y, want_logits=True)
+    assert math.isfinite(loss)
+    b = 2
+    note("xl oracle forward of one sequence")
+    ref = O.forward(f64(params), w.n_layer, w.n_head, x[b:b + 1], y[b:b + 1], want_cache=False)
+    del params
+    lg = logits[b].cpu().numpy()
+    z = ref["logits"][0]
+    worst = min(cosine(lg[t], z[t]) for t in range(w.seq_len))
+    assert worst >= 0.999, worst
+    assert abs(loss - math.log(w.vocab_size)) <= 0.5, loss
+    _, row_mean, tot = st.evaluate(x, y)
+    assert tot == loss
+    assert abs(row_mean[b] - float(ref["loss"])) <= 2e-2, (row_mean[b], ref["loss"])
+    note("xl backward determinism")
+    st.forward(x, y)
+    st.backward(1.0, False)
+    g1 = torch.empty(st.n_params, dtype=torch.float32, device="cuda")
+    G.gpt2_get_grads(st.h, g1.data_ptr(), 1)
+    assert torch.isfinite(g1).all()
+    st.forward(x, y)
+    st.backward(1.0, False)
+    g2 = torch.empty_like(g1)
+    G.gpt2_get_grads(st.h, g2.data_ptr(), 1)
+    assert torch.equal(g1, g2), "backward is not bitwise deterministic"
+    del g1, g2
+    note("xl causality")
+    x2 = x.copy()
+    t = 700
+    x2[b, t + 1] = (x2[b, t + 1] + 7) % w.vocab_size
+    _, logits2 = st.forward(x2, y, want_logits=True, want_loss=False)
+    assert torch.equal(logits[b, :t + 1], logits2[b, :t + 1])
+    assert not torch.equal(logits[b, t + 1:], logits2[b, t + 1:])
+    assert torch.equal(logits[:b], logits2[:b])
+    del logits, logits2
+    st.close()
+
+
 def _state(st):
     p = torch.empty(st.n_params, dtype=torch.float32, device="cuda")
     m, v = torch.empty_like(p), torch.empty_like(p)
@@ -360,6 +470,57 @@ def test_checkpoint_resume_bitwise(tmp_path):
     with pytest.raises(ValueError):
         ck.load(e, path)
     e.close()
+
+
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_checkpoint_resume_matches_oracle_adamw(tmp_path, mode):
+    """The oracle's leg of a resume: a state saved after two optimizer steps is read back with
+    allow_pickle=False into the oracle's tensors; both sides take the same gradients (set into
+    the resumed handle) and one more step at t = saved t + 1 from the restored params, m and v.
+    Parameters, both moments and the norm agree at the AdamW bar, so a convention that save
+    and load share (the step count, the order of the moments, the decayed prefix) cannot hide."""
+    from transformer_lm_step_amd import checkpoint as ck
+    note(f"checkpoint resume vs oracle AdamW {mode}")
+    w = synthetic.workload("tiny")
+    params = synthetic.init_params(w, randomize_affine=True)
+    batches = synthetic.micro_batches(w, 2)
+    a = make_step(w, mode)
+    a.set_params(params)
+    for s_ in range(2):
+        a.forward(*batches[s_])
+        a.backward(1.0, False)
+        a.adamw_step(1e-3 * (s_ + 1), t=s_ + 1)
+    path = str(tmp_path / "state.npz")
+    ck.save(a, path, adam_t=2, data_pos=2)
+    a.close()
+
+    b = make_step(w, mode, seed=5)
+    got = ck.load(b, path)
+    assert got["adam_t"] == 2
+    rng = np.random.default_rng(17)
+    grads = {k: (rng.standard_normal(v.shape) * 0.5).astype(np.float32) for k, v in params.items()}
+    gt = torch.from_numpy(b.pack(grads)).cuda()
+    G.gpt2_set_grads(b.h, gt.data_ptr(), 1)
+    t = got["adam_t"] + 1
+    lr = 2.5e-3
+    norm = b.adamw_step(lr, t=t)
+
+    state = ck.read_state(path)
+    p = f64(b.unpack(state["params"]))
+    m = f64(b.unpack(state["m"]))
+    v = f64(b.unpack(state["v"]))
+    assert any(np.abs(m[k]).max() > 0 for k in m), "saved moments are empty"
+    ref_norm = O.optimizer_step(p, f64(grads), m, v, t, lr)
+    assert norm == pytest.approx(ref_norm, rel=1e-5)
+    gp = b.params()
+    mm = torch.empty(b.n_params, dtype=torch.float32, device="cuda")
+    vv = torch.empty_like(mm)
+    G.gpt2_get_moments(b.h, mm.data_ptr(), vv.data_ptr(), 1)
+    gm, gv = b.unpack(mm.cpu().numpy()), b.unpack(vv.cpu().numpy())
+    for k in p:
+        assert np.abs(gp[k] - p[k]).max() <= 1e-6 * max(np.abs(p[k]).max(), 1e-3), k
+        assert rel_max(gm[k], m[k]) <= 1e-5 and rel_max(gv[k], v[k]) <= 1e-5, k
+    b.close()
 
 
 def test_evaluate_tiny_fp32_matches_oracle():
@@ -476,16 +637,17 @@ def _decode(st, params, w, prompt, total, k, rng, check_logits):
     return seq
 
 
-def test_few_rows_bf16_forward():
+@pytest.mark.parametrize("mode", BF16_MODES)
+def test_few_rows_bf16_forward(mode):
     """A forward of only 16 rows (B=2, T=8) at the 124M widths with 2 layers, bf16: the
     products take the few-row path (every forward epilogue: bias, residual, GELU, and the
     50304-column lm_head); logits (cosine >= 0.999) and loss (bf16 bar) against the oracle."""
-    note("few rows bf16 B=2 T=8")
+    note(f"few rows {mode} B=2 T=8")
     w = synthetic.workload("gpt2_step", n_layer=2, batch=2, seq_len=8)
     params = synthetic.init_params(w, randomize_affine=True)
     (x, y), = synthetic.micro_batches(w, 1)
     ref = O.forward(f64(params), w.n_layer, w.n_head, x, y, want_cache=False)
-    st = make_step(w, "bf16")
+    st = make_step(w, mode)
     st.set_params(params)
     loss, logits = st.forward(x, y, want_logits=True)
     assert abs(loss - ref["loss"]) <= 2e-2

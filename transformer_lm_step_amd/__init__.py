@@ -6,7 +6,7 @@ memory and streams; :class:`GPT2Step` is a convenience holder that allocates the
 as a torch tensor and passes raw pointers.
 
 Importing this package loads the library and raises if it has not been built
-(``python -m transformer_lm_step_amd.build``). There is no fallback implementation.
+(``python transformer_lm_step_amd/build.py``). There is no fallback implementation.
 """
 from __future__ import annotations
 
@@ -18,7 +18,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpt2_step.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EHIP = 0, -1, -2, -3
-GPT2_FP32, GPT2_BF16 = 0, 1
+GPT2_FP32, GPT2_BF16, GPT2_BF16_RES16 = 0, 1, 2
+# dtype names accepted by make_config: the C ABI's three arithmetic modes
+DTYPES = {"fp32": GPT2_FP32, "bf16": GPT2_BF16, "bf16_res16": GPT2_BF16_RES16}
 
 
 class gpt2_config(ctypes.Structure):
@@ -34,7 +36,7 @@ class GPT2Error(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m transformer_lm_step_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python transformer_lm_step_amd/build.py`")
 # torch ships its own HIP runtime with the same soname as the system one. Loading torch first
 # makes the library bind to that already-loaded runtime, so one process never holds two.
 import torch  # noqa: E402,F401
@@ -104,7 +106,7 @@ def make_config(n_layer, n_head, n_embd, block_size, vocab_size, padded_vocab_si
                 dtype="bf16", mlp_hidden=None) -> gpt2_config:
     return gpt2_config(n_layer, n_head, n_embd, 4 * n_embd if mlp_hidden is None else mlp_hidden,
                        block_size, vocab_size, padded_vocab_size, max_batch,
-                       GPT2_BF16 if dtype in ("bf16", GPT2_BF16) else GPT2_FP32)
+                       dtype if isinstance(dtype, int) else DTYPES[dtype])
 
 
 # ---------------------------------------------------------------- C ABI, same names

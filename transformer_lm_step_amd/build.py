@@ -2,7 +2,7 @@
 
 Every ``csrc/*.hip`` file is compiled by hipcc (in parallel) and linked into one shared
 library next to this file. Packed fp32 instructions are disabled in the device code.
-Usage: ``python -m transformer_lm_step_amd.build`` (or ``build()`` from Python).
+Usage: ``python transformer_lm_step_amd/build.py`` (or ``build()`` from Python).
 """
 from __future__ import annotations
 

@@ -175,7 +175,7 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
         const int n = nw + j * 16 + (lane & 15);
         const bool nok = !CHECK || n < p.N;
         float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU)
+        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
             bias = (p.bias && nok) ? p.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -188,6 +188,8 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                 extra[r] = 0.f;
                 if constexpr (EPI == EPI_BIAS_RESID) {
                     if (ok) extra[r] = to_f<T>(((const T*)p.resid)[(int64_t)m * p.ldr + n]);
+                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                    if (ok) extra[r] = ((const float*)p.resid)[(int64_t)m * p.ldr + n];
                 } else if constexpr (EPI == EPI_GELU_BWD) {
                     if (ok) extra[r] = to_f<T>(((const T*)p.aux)[(int64_t)m * p.ldaux + n]);
                 } else if constexpr (EPI == EPI_F32) {
@@ -204,6 +206,8 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                     ((T*)p.C)[o] = from_f<T>(p.alpha * v + bias);
                 } else if constexpr (EPI == EPI_BIAS_RESID) {
                     ((T*)p.C)[o] = from_f<T>(extra[r] + v + bias);
+                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+                    ((float*)p.C)[o] = extra[r] + v + bias;
                 } else if constexpr (EPI == EPI_BIAS_GELU) {
                     const T u = from_f<T>(v + bias);
                     ((T*)p.C)[o] = u;
@@ -391,13 +395,14 @@ template <> struct EpiIn<EPI_GELU_BWD> { typedef bf16x4 T; };
 template <> struct EpiIn<EPI_BIAS_RESID> { typedef bf16x4 T; };
 template <int EPI>
 DEV bool epi_reads(const GemmArgs& p) {
-    return EPI == EPI_BIAS_RESID || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
+    return EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
 }
 // 1 if the 4 columns n..n+3 of row m take the vector path
 DEV bool epi_vec(const GemmArgs& p, int m, int n) { return m < p.M && p.vec && n + 3 < p.N; }
 template <int EPI>
 DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
     if constexpr (EPI == EPI_BIAS_RESID) return *(const bf16x4*)((const bf16*)p.resid + (int64_t)m * p.ldr + n);
+    else if constexpr (EPI == EPI_BIAS_RESID_F32) return *(const float4*)((const float*)p.resid + (int64_t)m * p.ldr + n);
     else if constexpr (EPI == EPI_GELU_BWD) return *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
     else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
 }
@@ -410,7 +415,8 @@ template <int EPI>
 constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_F32; }
 template <int EPI>
 constexpr bool epi_bias() {
-    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU;
+    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 ||
+           EPI == EPI_BIAS_GELU;
 }
 // bias of columns n..n+3 (0 past the matrix edge or without a bias)
 DEV float4 bias4(const GemmArgs& p, int n) {
@@ -461,6 +467,9 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
             const bf16x4 a = in;
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
                                                    v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
+        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+            const float4 rr = in;
+            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]);
         } else if constexpr (EPI == EPI_F32) {
             float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
             if (p.beta) old = in;
@@ -479,6 +488,8 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
             ((bf16*)p.C)[e] = (bf16)v[r];
         } else if constexpr (EPI == EPI_BIAS_RESID) {
             ((bf16*)p.C)[e] = (bf16)((float)((const bf16*)p.resid)[(int64_t)m * p.ldr + nn] + v[r]);
+        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
+            ((float*)p.C)[e] = ((const float*)p.resid)[(int64_t)m * p.ldr + nn] + v[r];
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             const bf16 u = (bf16)v[r];
             ((bf16*)p.C)[e] = u;
@@ -658,7 +669,7 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     half(std::integral_constant<int, 0>{});
     half(std::integral_constant<int, 1>{});
 }
-// fp32 outputs (gradient output, split-K partials): 4-column chunks (already
+// fp32 outputs (gradient output, split-K partials, the fp32 residual add): 4-column chunks (already
 // 16-byte accesses), alpha and the bias applied per chunk by epi4. Split-K partials of
 // a tile inside the matrix skip the per-chunk checks. (Applying alpha and the bias ahead of
 // epi4, as the bf16 form does, measured 9-12% slower here.)
@@ -989,7 +1000,8 @@ static bool skinny_ok(const GemmDesc& d, int nsplit) {
     constexpr int E = 16 / sizeof(T);
     if (d.M > SK_MAX_M || d.a_layout != 0 || d.b_layout != 0 || nsplit != 1 || d.rowsum) return false;
     if (d.N > 16384) return false;   // very wide products (the vocabulary) fill the GPU on the tiled path
-    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID && d.epi != EPI_BIAS_GELU) return false;
+    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID && d.epi != EPI_BIAS_RESID_F32 && d.epi != EPI_BIAS_GELU)
+        return false;
     if (d.K % E || d.lda % E || d.ldb % E) return false;
     return (((uintptr_t)d.A | (uintptr_t)d.B) & 15) == 0;
 }
@@ -999,6 +1011,7 @@ static hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
     if (epi == EPI_BIAS_T) gemm_skinny_kernel<T, EPI_BIAS_T><<<grid, blk, 0, s>>>(a);
     else if (epi == EPI_BIAS_RESID) gemm_skinny_kernel<T, EPI_BIAS_RESID><<<grid, blk, 0, s>>>(a);
+    else if (epi == EPI_BIAS_RESID_F32) gemm_skinny_kernel<T, EPI_BIAS_RESID_F32><<<grid, blk, 0, s>>>(a);
     else gemm_skinny_kernel<T, EPI_BIAS_GELU><<<grid, blk, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1065,6 +1078,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(0, 0, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_LOGITS)
             MM_CASE_WIDE(0, 0, EPI_BIAS_RESID)
+            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE_WIDE(0, 1, EPI_F32)
             MM_CASE_WIDE(0, 1, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_BIAS_GELU)
@@ -1073,6 +1087,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(1, 1, EPI_F32)
             MM_CASE(0, 0, EPI_BIAS_T)
             MM_CASE(0, 0, EPI_BIAS_RESID)
+            MM_CASE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE(0, 0, EPI_BIAS_GELU)
             MM_CASE(0, 1, EPI_GELU_BWD)
             MM_CASE(0, 1, EPI_F32)
@@ -1090,6 +1105,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_tiled<T, AL, BL, EP>(a, nsplit, bm, bn, s); else
     GEMM_CASE(0, 0, EPI_BIAS_T)
     GEMM_CASE(0, 0, EPI_BIAS_RESID)
+    GEMM_CASE(0, 0, EPI_BIAS_RESID_F32)
     GEMM_CASE(0, 0, EPI_BIAS_GELU)
     GEMM_CASE(0, 1, EPI_GELU_BWD)
     GEMM_CASE(0, 1, EPI_F32)
@@ -1156,6 +1172,7 @@ static void set_lds_mm() {
 
 void gemm_setup() {
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_LOGITS, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 192>();
+    set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();
@@ -1168,6 +1185,7 @@ void gemm_setup() {
     (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_F32, 128, 128, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 128>();
+    set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();
     set_lds_mm<0, 1, EPI_PARTIAL, 128, 128>(); set_lds_mm<1, 1, EPI_F32, 128, 128>();
@@ -1175,6 +1193,7 @@ void gemm_setup() {
     // allow the dynamic LDS size (above the 64 KiB default) for every instantiation
 #define SETUP_T(T)                                                                                          \
     set_lds_all<T, 0, 0, EPI_BIAS_T>(); set_lds_all<T, 0, 0, EPI_BIAS_RESID>();                        \
+    set_lds_all<T, 0, 0, EPI_BIAS_RESID_F32>();                                                             \
     set_lds_all<T, 0, 0, EPI_BIAS_GELU>(); set_lds_all<T, 0, 1, EPI_GELU_BWD>();                           \
     set_lds_all<T, 0, 1, EPI_F32>(); set_lds_all<T, 0, 1, EPI_BIAS_T>(); set_lds_all<T, 1, 1, EPI_F32>(); \
     set_lds_all<T, 1, 1, EPI_PARTIAL>(); set_lds_all<T, 0, 1, EPI_PARTIAL>();

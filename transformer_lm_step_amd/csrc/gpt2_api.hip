@@ -41,7 +41,8 @@ bool config_ok(const gpt2_config* c, std::string* why, bool strict = true) {
         return bad("config fields must be positive");
     if (c->n_embd % c->n_head) return bad("n_embd must be a multiple of n_head");
     if (c->padded_vocab_size < c->vocab_size) return bad("padded_vocab_size must be >= vocab_size");
-    if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16) return bad("dtype must be GPT2_FP32 or GPT2_BF16");
+    if (c->dtype != GPT2_FP32 && c->dtype != GPT2_BF16 && c->dtype != GPT2_BF16_RES16)
+        return bad("dtype must be GPT2_FP32, GPT2_BF16 or GPT2_BF16_RES16");
     if (!strict) return true;
     const int hs = c->n_embd / c->n_head;
     if (hs != 64 && hs != 32) return bad("head size n_embd/n_head must be 32 or 64");
@@ -165,7 +166,7 @@ struct Plan {
     // offsets in bytes
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
-    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, dqkv, du, Dbuf;
+    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dres16, dln, datt, dqkv, du, Dbuf;
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
     // LayerNorm backward partials: one set per LayerNorm (ln_f, then ln_2 and ln_1 of each layer
     // from the last), reduced together after the backward; the sets' gradient offsets
@@ -176,8 +177,9 @@ struct Plan {
 Plan make_plan(const gpt2_config* c) {
     Plan P;
     const Layout L = make_layout(c);
-    const bool bf = c->dtype == GPT2_BF16;
-    const size_t es = bf ? 2 : 4;
+    const bool bf = c->dtype != GPT2_FP32;
+    const size_t es = bf ? 2 : 4;                                  // operands and activations
+    const size_t er = c->dtype == GPT2_BF16_RES16 ? 2 : 4;         // residual stream and its gradient
     const int64_t BT = (int64_t)c->max_batch * c->block_size;
     const int64_t C = c->n_embd, F = c->mlp_hidden, Vp = c->padded_vocab_size, H = c->n_head;
     size_t o = 0;
@@ -189,9 +191,9 @@ Plan make_plan(const gpt2_config* c) {
     P.shadow = bf ? take(L.decay_end * 2) : 0;
     P.idx = take(BT * 4);
     P.tgt = take(BT * 4);
-    for (int l = 0; l <= c->n_layer; ++l) P.x_in.push_back(take(BT * C * es));
+    for (int l = 0; l <= c->n_layer; ++l) P.x_in.push_back(take(BT * C * er));
     for (int l = 0; l < c->n_layer; ++l) {
-        P.x_mid.push_back(take(BT * C * es));
+        P.x_mid.push_back(take(BT * C * er));
         P.h1.push_back(take(BT * C * es));
         P.mean1.push_back(take(BT * 4));
         P.rstd1.push_back(take(BT * 4));
@@ -213,7 +215,9 @@ Plan make_plan(const gpt2_config* c) {
     P.loss = take(256);
     P.mask = take(BT);
     P.rowd = take((size_t)c->max_batch * 2 * 8);
-    P.dres = take(BT * C * es);
+    P.dres = take(BT * C * er);
+    // bf16 copy of an fp32 residual gradient: the A operand of the products that take it
+    P.dres16 = (bf && er == 4) ? take(BT * C * 2) : 0;
     P.dln = take(BT * C * es);
     P.datt = take(BT * C * es);
     P.dqkv = take(BT * 3 * C * es);
@@ -255,7 +259,8 @@ struct gpt2 {
     char* ws = nullptr;
     hipStream_t stream = nullptr;
     int dev = 0;
-    bool bf16 = false;
+    bool bf16 = false;    // product and attention operands, activations: bf16 (else fp32)
+    bool res16 = false;   // residual stream and its gradient: bf16 (else fp32)
     // state of the last forward
     bool have_fwd = false;
     int B = 0, T = 0;
@@ -405,7 +410,8 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
     }
     h->ws = (char*)d_ws;
     h->stream = (hipStream_t)stream;
-    h->bf16 = cfg->dtype == GPT2_BF16;
+    h->bf16 = cfg->dtype != GPT2_FP32;
+    h->res16 = cfg->dtype == GPT2_BF16_RES16;
     (void)hipGetDevice(&h->dev);
     if (!g_setup_done) {
         gemm_setup();
@@ -520,17 +526,19 @@ extern "C" float* gpt2_grads_device(gpt2_t* h) { return h ? h->grads() : nullptr
 static int forward_trunk(gpt2_t* h, int B, int T) {
     const gpt2_config& c = h->cfg;
     const int BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
-    const int bf = h->bf16;
+    const int bf = h->bf16, r16 = h->res16;
+    // residual add: in the storage type, or into the fp32 stream from bf16 operands
+    const int epi_res = (bf && !r16) ? EPI_BIAS_RESID_F32 : EPI_BIAS_RESID;
     const Layout& L = h->L;
     const Plan& P = h->P;
     float* prm = h->params();
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
-    TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<char>(P.x_in[0]), B, T, C, bf, s); }));
+    TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<char>(P.x_in[0]), B, T, C, r16, s); }));
     for (int l = 0; l < c.n_layer; ++l) {
         TRY(run(h, "layernorm_fwd", [&] {
             return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
-                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), BT, C, bf, s);
+                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), BT, C, r16, bf, s);
         }));
         GemmDesc g;
         g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
@@ -545,12 +553,12 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = BT; g.N = C; g.K = C;
-        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.epi = epi_res; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
         g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
             return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
-                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), BT, C, bf, s);
+                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), BT, C, r16, bf, s);
         }));
         g = GemmDesc();
         g.A = h->at<char>(P.h2[l]); g.lda = C;
@@ -562,13 +570,13 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = BT; g.N = C; g.K = F;
-        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.epi = epi_res; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
         g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
     }
     TRY(run(h, "layernorm_fwd", [&] {
         return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
-                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), BT, C, bf, s);
+                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), BT, C, r16, bf, s);
     }));
     {
         GemmDesc g;
@@ -694,7 +702,8 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         return set_error(GPT2_EINVAL, "top_k=%d outside [1, %d]", top_k, GPT2_TOPK_MAX);
     if (d_next && !d_uniform) return set_error(GPT2_EINVAL, "drawing the next token needs d_uniform");
     const int C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
-    const int bf = h->bf16;
+    const int bf = h->bf16, r16 = h->res16;
+    const int epi_res = (bf && !r16) ? EPI_BIAS_RESID_F32 : EPI_BIAS_RESID;
     const size_t es = bf ? 2 : 4;
     const Layout& L = h->L;
     const Plan& P = h->P;
@@ -704,12 +713,12 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
     HIPTRY(hipMemcpyAsync(idx, d_tokens, (size_t)B * 4, hipMemcpyDeviceToDevice, s), "copy tokens");
     h->dec_B = 0;   // until this step has been enqueued completely
     TRY(run(h, "embed_fwd", [&] {
-        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, bf, s);
+        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, r16, s);
     }));
     for (int l = 0; l < c.n_layer; ++l) {
         TRY(run(h, "layernorm_fwd", [&] {
             return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
-                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), B, C, bf, s);
+                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), B, C, r16, bf, s);
         }));
         GemmDesc g;
         g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
@@ -725,12 +734,12 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = B; g.N = C; g.K = C;
-        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
+        g.epi = epi_res; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
         g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
             return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
-                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), B, C, bf, s);
+                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), B, C, r16, bf, s);
         }));
         g = GemmDesc();
         g.A = h->at<char>(P.h2[l]); g.lda = C;
@@ -742,13 +751,13 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = B; g.N = C; g.K = F;
-        g.epi = EPI_BIAS_RESID; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
+        g.epi = epi_res; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
         g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
     }
     TRY(run(h, "layernorm_fwd", [&] {
         return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
-                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), B, C, bf, s);
+                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), B, C, r16, bf, s);
     }));
     {
         GemmDesc g;
@@ -777,15 +786,18 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     const gpt2_config& c = h->cfg;
     const int B = h->B, T = h->T, BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size;
     const int H = c.n_head, hs = C / H;
-    const int bf = h->bf16;
+    const int bf = h->bf16, r16 = h->res16;
     const int acc = accumulate ? 1 : 0;
     const Layout& L = h->L;
     const Plan& P = h->P;
     float* grd = h->grads();
     float* prm = h->params();
     hipStream_t s = h->stream;
-    // gradient of the residual stream, in the storage type (like every activation gradient)
+    // gradient of the residual stream, in the residual stream's type; the products take it as
+    // bf16 (under the autocast recipe the gradient reaching a bf16 product output is cast down)
     char* dres = h->at<char>(P.dres);
+    char* dres16 = P.dres16 ? h->at<char>(P.dres16) : nullptr;
+    char* dres_op = dres16 ? dres16 : dres;
     // gradient of a LayerNorm's output, in the storage type: under the autocast recipe it is the
     // bf16 input gradient of the following product, cast to fp32 where LayerNorm runs
     char* dln = h->at<char>(P.dln);
@@ -803,7 +815,8 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres) -> int {
         float* part = lnpart + (size_t)lnset++ * P.lnset_stride;
         return run(h, "layernorm_bwd", [&] {
-            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, accum_dres, part, lnblk, BT, C, bf, s);
+            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres16, accum_dres, part, lnblk, BT, C, bf,
+                                      r16, s);
         });
     };
     // weight gradient dW (+)= dy^T x; with bias_off >= 0 also the bias gradient db (+)= colsum(dy),
@@ -843,10 +856,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
-        TRY(dw(dres, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
+        TRY(dw(dres_op, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
         {
             GemmDesc g;
-            g.A = dres; g.lda = C; g.a_layout = 0;
+            g.A = dres_op; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_pr[l]); g.ldb = F; g.b_layout = 1;
             g.M = BT; g.N = F; g.K = C;
             g.epi = EPI_GELU_BWD; g.C = h->at<char>(P.du); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
@@ -864,10 +877,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
         TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1));
         // x_mid = x_in + y Wo^T + bo
-        TRY(dw(dres, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
+        TRY(dw(dres_op, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
         {
             GemmDesc g;
-            g.A = dres; g.lda = C; g.a_layout = 0;
+            g.A = dres_op; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_o[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = C;
             g.epi = EPI_BIAS_T; g.C = h->at<char>(P.datt); g.ldc = C; g.alpha = 1.f;
@@ -900,7 +913,7 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     if (!acc && T < c.block_size)
         HIPTRY(fill(grd + L.wpe + (int64_t)T * C, (int64_t)(c.block_size - T) * C, 0.f, s), "zero wpe tail");
     TRY(run(h, "embed_bwd", [&] {
-        return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc, bf,
+        return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc, r16,
                               h->at<char>(P.ebscratch), s);
     }));
     return GPT2_OK;
@@ -976,8 +989,8 @@ extern "C" int gpt2_debug_tensor(gpt2_t* h, const char* which, int32_t layer, fl
     int64_t n = 0;
     bool f32 = false;
     std::string w = which;
-    if (w == "x_in" && layer >= 0 && layer <= c.n_layer) { off = P.x_in[layer]; n = BT * C; }
-    else if (w == "x_out") { off = P.x_in[c.n_layer]; n = BT * C; }
+    if (w == "x_in" && layer >= 0 && layer <= c.n_layer) { off = P.x_in[layer]; n = BT * C; f32 = !h->res16; }
+    else if (w == "x_out") { off = P.x_in[c.n_layer]; n = BT * C; f32 = !h->res16; }
     else if (w == "hf") { off = P.hf; n = BT * C; }
     else if (w == "dz") { off = P.logits; n = BT * c.padded_vocab_size; }
     else if (lay && w == "h1") { off = P.h1[layer]; n = BT * C; }

@@ -9,7 +9,7 @@ namespace gpt2k {
 // ------------------------------------------------------------------ GEMM
 enum Epi {
     EPI_BIAS_T = 0,          // C(T)   = alpha*acc + bias[n]           (bias may be null)
-    EPI_BIAS_RESID = 1,      // C(T)   = resid(T)[m][n] + acc + bias[n]
+    EPI_BIAS_RESID = 1,      // C(T)   = resid(T)[m][n] + acc + bias[n]   (residual stream in the storage type)
     EPI_BIAS_GELU = 2,       // C(T)   = u = acc + bias[n];  C2(T) = gelu_tanh(u)
     EPI_GELU_BWD = 3,        // C(T)   = acc * gelu_tanh'(aux[m][n])
     EPI_F32 = 4,             // C(f32) = (beta ? C : 0) + alpha*acc
@@ -17,6 +17,7 @@ enum Epi {
     EPI_LOGITS = 6,          // C(bf16) = alpha*acc + bias[n], and C2 (fp32 pairs) = for every row m
                              // and 192-column tile t: (max, sum exp(z - max)) of that row's
                              // bf16-rounded outputs in the tile, at C2[2 * (m * tiles + t)]
+    EPI_BIAS_RESID_F32 = 7,  // C(f32) = resid(f32)[m][n] + acc + bias[n]  (fp32 residual stream, bf16 operands)
 };
 
 struct GemmDesc {
@@ -27,7 +28,7 @@ struct GemmDesc {
     void* C = nullptr; int64_t ldc = 0;
     void* C2 = nullptr;
     const float* bias = nullptr;
-    const void* resid = nullptr; int64_t ldr = 0;   // storage type
+    const void* resid = nullptr; int64_t ldr = 0;   // storage type (fp32 for EPI_BIAS_RESID_F32)
     const void* aux = nullptr; int64_t ldaux = 0;
     float alpha = 1.f;
     int beta = 0;
@@ -52,18 +53,20 @@ void gemm_setup();
 size_t gemm_lds_bytes();
 
 // ------------------------------------------------------------------ elementwise / rows
-// x(T) [B*T, C] = wte[idx] + wpe[t] (the residual stream is in the storage type)
+// x [B*T, C] = wte[idx] + wpe[t], x in bf16 if x_bf16 else fp32 (the residual stream's type)
 hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, void* x, int B, int T,
-                         int C, int is_bf16, hipStream_t s);
-// LayerNorm forward: out(T) = (x(T) - mean) * rstd * w + b ; saves mean, rstd (fp32)
+                         int C, int x_bf16, hipStream_t s);
+// LayerNorm forward: out = (x - mean) * rstd * w + b ; saves mean, rstd (fp32). x is bf16 if
+// x_bf16 (the bf16 residual stream) else fp32; out is bf16 if out_bf16 else fp32.
 hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
-                             float* rstd, int rows, int C, int is_bf16, hipStream_t s);
+                             float* rstd, int rows, int C, int x_bf16, int out_bf16, hipStream_t s);
 // LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; partial[blk][0:C] = sum dh*xhat,
 // [C:2C] = sum dh, [2C:3C] = sum of the incoming dres (zero without accumulate) over the
-// block's rows. dh, x and the residual gradient dres are in the storage type T.
+// block's rows. dh is bf16 if dh_bf16 else fp32; x and dres are bf16 if res_bf16 else fp32;
+// dres16 (nullable) receives a bf16 copy of the new dres.
 hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, const float* rstd,
-                              const float* w, void* dres, int accumulate_dres,
-                              float* partial, int nblk, int rows, int C, int is_bf16, hipStream_t s);
+                              const float* w, void* dres, void* dres16, int accumulate_dres,
+                              float* partial, int nblk, int rows, int C, int dh_bf16, int res_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);
 // out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order); scratch holds
 // sum_scratch_floats(n) floats
@@ -108,7 +111,7 @@ hipError_t convert_to_f32(const void* src, float* dst, int64_t n, int is_bf16, h
 hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s);
 
 // embedding backward (deterministic): dwte[idx[r]] += dx[r] in ascending r, dwpe[t] (+)= sum_b dx[b,t];
-// dx in the storage type (bf16 if is_bf16, else fp32)
+// dx (the residual stream's gradient) is bf16 if is_bf16, else fp32
 size_t embed_backward_scratch_bytes(int rows, int C);
 void rows_setup();
 hipError_t embed_backward(const int32_t* idx, const void* dx, float* dwte, float* dwpe, int B, int T,

@@ -62,23 +62,25 @@ hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe,
 constexpr int LN_NV = 8;
 constexpr float LN_EPS = 1e-5f;
 
-// NV = float4 per lane needed for C (C <= 256 * NV): the row is held in registers sized to C
-template <typename T, int NV>
-__global__ void __launch_bounds__(256) layernorm_forward_kernel(const T* __restrict__ x, const float* __restrict__ w,
-                                                                const float* __restrict__ b, T* __restrict__ out,
+// NV = float4 per lane needed for C (C <= 256 * NV): the row is held in registers sized to C.
+// TX: type of the residual stream x (fp32, or bf16 in the bf16-residual mode); TO: type of the
+// normalized output (the operand type of the product that follows).
+template <typename TX, typename TO, int NV>
+__global__ void __launch_bounds__(256) layernorm_forward_kernel(const TX* __restrict__ x, const float* __restrict__ w,
+                                                                const float* __restrict__ b, TO* __restrict__ out,
                                                                 float* __restrict__ mean, float* __restrict__ rstd,
                                                                 int rows, int C) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const int nv = C >> 2;
-    const T* xr = x + (int64_t)row * C;
+    const TX* xr = x + (int64_t)row * C;
     float4 v[NV];
     float s = 0.f;
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int c = lane + 64 * j;
-        v[j] = c < nv ? load4<T>(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j] = c < nv ? load4<TX>(xr + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
         s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
     }
     const float mu = wave_sum(s) / (float)C;
@@ -98,17 +100,17 @@ __global__ void __launch_bounds__(256) layernorm_forward_kernel(const T* __restr
         const int c = lane + 64 * j;
         if (c < nv) {
             const float4 ww = ((const float4*)w)[c], bb = ((const float4*)b)[c];
-            store4<T>(out + (int64_t)row * C + 4 * c, (v[j].x - mu) * r * ww.x + bb.x, (v[j].y - mu) * r * ww.y + bb.y,
-                      (v[j].z - mu) * r * ww.z + bb.z, (v[j].w - mu) * r * ww.w + bb.w);
+            store4<TO>(out + (int64_t)row * C + 4 * c, (v[j].x - mu) * r * ww.x + bb.x, (v[j].y - mu) * r * ww.y + bb.y,
+                       (v[j].z - mu) * r * ww.z + bb.z, (v[j].w - mu) * r * ww.w + bb.w);
         }
     }
     if (lane == 0) { mean[row] = mu; rstd[row] = r; }
 }
 
-template <typename T>
-static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const T* x, const float* w, const float* b, T* out,
+template <typename TX, typename TO>
+static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const TX* x, const float* w, const float* b, TO* out,
                                 float* mean, float* rstd, int rows, int C) {
-#define LNF(NV) hipLaunchKernelGGL((layernorm_forward_kernel<T, NV>), g, dim3(256), 0, s, x, w, b, out, mean, rstd, rows, C)
+#define LNF(NV) hipLaunchKernelGGL((layernorm_forward_kernel<TX, TO, NV>), g, dim3(256), 0, s, x, w, b, out, mean, rstd, rows, C)
     if (nv4 <= 64) LNF(1);
     else if (nv4 <= 128) LNF(2);
     else if (nv4 <= 192) LNF(3);
@@ -168,18 +170,20 @@ __global__ void __launch_bounds__(256) layernorm_forward_half_kernel(const bf16*
 }
 
 hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
-                             float* rstd, int rows, int C, int is_bf16, hipStream_t s) {
+                             float* rstd, int rows, int C, int x_bf16, int out_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
+    if (x_bf16 && !out_bf16) return hipErrorInvalidValue;
     dim3 g((rows + 3) / 4);
-    if (is_bf16 && (C == 512 || C == 768 || C == 1024) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    if (x_bf16 && (C == 512 || C == 768 || C == 1024) && ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 15) == 0) {
         const dim3 g8((rows + 7) / 8);
         if (C == 512) hipLaunchKernelGGL(layernorm_forward_half_kernel<2>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
         else if (C == 768) hipLaunchKernelGGL(layernorm_forward_half_kernel<3>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
         else hipLaunchKernelGGL(layernorm_forward_half_kernel<4>, g8, dim3(256), 0, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
         return hipGetLastError();
     }
-    if (is_bf16) return ln_fwd_launch<bf16>(C / 4, g, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
-    return ln_fwd_launch<float>(C / 4, g, s, (const float*)x, w, b, (float*)out, mean, rstd, rows, C);
+    if (x_bf16) return ln_fwd_launch<bf16, bf16>(C / 4, g, s, (const bf16*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+    if (out_bf16) return ln_fwd_launch<float, bf16>(C / 4, g, s, (const float*)x, w, b, (bf16*)out, mean, rstd, rows, C);
+    return ln_fwd_launch<float, float>(C / 4, g, s, (const float*)x, w, b, (float*)out, mean, rstd, rows, C);
 }
 
 // Backward through y = xhat*w + b, xhat = (x - mean)*rstd:
@@ -193,11 +197,14 @@ hipError_t layernorm_forward(const void* x, const float* w, const float* b, void
 constexpr int LNB_ROWS = 4;
 int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 * LNB_ROWS); }
 
-// NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers
-template <typename T, int NV>
+// NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers.
+// TD: type of dh (the operand type); TX: type of x and of the residual gradient dres (fp32, or
+// bf16 in the bf16-residual mode). With dres16 non-null, the new dres is also stored as bf16
+// (the A operand of the products that take the residual gradient).
+template <typename TD, typename TX, int NV>
 __global__ void __launch_bounds__(256) layernorm_backward_kernel(
-    const T* __restrict__ dh, const T* __restrict__ x, const float* __restrict__ mean,
-    const float* __restrict__ rstd, const float* __restrict__ w, T* __restrict__ dres,
+    const TD* __restrict__ dh, const TX* __restrict__ x, const float* __restrict__ mean,
+    const float* __restrict__ rstd, const float* __restrict__ w, TX* __restrict__ dres, bf16* __restrict__ dres16,
     int accumulate, float* __restrict__ partial, int rows, int C) {
     extern __shared__ float sred[];  // [4][3C]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -212,9 +219,9 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     const int r0 = (blockIdx.x * 4 + wave) * LNB_ROWS;
     for (int row = r0; row < r0 + LNB_ROWS && row < rows; ++row) {
         const float mu = mean[row], r = rstd[row];
-        const T* dr = dh + (int64_t)row * C;
-        const T* xr = x + (int64_t)row * C;
-        T* o = dres + (int64_t)row * C;
+        const TD* dr = dh + (int64_t)row * C;
+        const TX* xr = x + (int64_t)row * C;
+        TX* o = dres + (int64_t)row * C;
         float4 xh[NV], dxh[NV], old[NV];
         float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -222,8 +229,8 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
             const int c = lane + 64 * j;
             xh[j] = dxh[j] = old[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (c < nv) {
-                const float4 d = load4<T>(dr + 4 * c), xx = load4<T>(xr + 4 * c);
-                if (accumulate) old[j] = load4<T>(o + 4 * c);
+                const float4 d = load4<TD>(dr + 4 * c), xx = load4<TX>(xr + 4 * c);
+                if (accumulate) old[j] = load4<TX>(o + 4 * c);
                 xh[j] = make_float4((xx.x - mu) * r, (xx.y - mu) * r, (xx.z - mu) * r, (xx.w - mu) * r);
                 dxh[j] = make_float4(d.x * wv[j].x, d.y * wv[j].y, d.z * wv[j].z, d.w * wv[j].w);
                 s1 += (dxh[j].x + dxh[j].y) + (dxh[j].z + dxh[j].w);
@@ -242,7 +249,8 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
                                              old[j].y + r * (dxh[j].y - m1 - xh[j].y * m2),
                                              old[j].z + r * (dxh[j].z - m1 - xh[j].z * m2),
                                              old[j].w + r * (dxh[j].w - m1 - xh[j].w * m2));
-                store4<T>(o + 4 * c, g.x, g.y, g.z, g.w);
+                store4<TX>(o + 4 * c, g.x, g.y, g.z, g.w);
+                if (dres16) store4<bf16>(dres16 + (int64_t)row * C + 4 * c, g.x, g.y, g.z, g.w);
             }
         }
     }
@@ -263,12 +271,12 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     }
 }
 
-template <typename T>
-static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const T* dh, const T* x,
-                                const float* mean, const float* rstd, const float* w, T* dres, int acc,
+template <typename TD, typename TX>
+static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, const TD* dh, const TX* x,
+                                const float* mean, const float* rstd, const float* w, TX* dres, bf16* dres16, int acc,
                                 float* partial, int rows, int C) {
-#define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<T, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
-                                   dres, acc, partial, rows, C)
+#define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<TD, TX, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
+                                   dres, dres16, acc, partial, rows, C)
     if (nv4 <= 64) LNB(1);
     else if (nv4 <= 128) LNB(2);
     else if (nv4 <= 192) LNB(3);
@@ -279,15 +287,19 @@ static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, cons
 }
 
 hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, const float* rstd,
-                              const float* w, void* dres, int accumulate_dres, float* partial,
-                              int nblk, int rows, int C, int is_bf16, hipStream_t s) {
+                              const float* w, void* dres, void* dres16, int accumulate_dres, float* partial,
+                              int nblk, int rows, int C, int dh_bf16, int res_bf16, hipStream_t s) {
     if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
+    if (res_bf16 && !dh_bf16) return hipErrorInvalidValue;
     const size_t lds = 12 * (size_t)C * sizeof(float);
-    if (is_bf16)
-        return ln_bwd_launch<bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, (const bf16*)x, mean, rstd, w,
-                                   (bf16*)dres, accumulate_dres, partial, rows, C);
-    return ln_bwd_launch<float>(C / 4, dim3(nblk), lds, s, (const float*)dh, (const float*)x, mean, rstd, w,
-                                (float*)dres, accumulate_dres, partial, rows, C);
+    if (res_bf16)
+        return ln_bwd_launch<bf16, bf16>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, (const bf16*)x, mean, rstd, w,
+                                         (bf16*)dres, (bf16*)dres16, accumulate_dres, partial, rows, C);
+    if (dh_bf16)
+        return ln_bwd_launch<bf16, float>(C / 4, dim3(nblk), lds, s, (const bf16*)dh, (const float*)x, mean, rstd, w,
+                                          (float*)dres, (bf16*)dres16, accumulate_dres, partial, rows, C);
+    return ln_bwd_launch<float, float>(C / 4, dim3(nblk), lds, s, (const float*)dh, (const float*)x, mean, rstd, w,
+                                       (float*)dres, (bf16*)dres16, accumulate_dres, partial, rows, C);
 }
 
 // Column sums of partial [np, n] (row stride `stride`), deterministic, in two launches:
