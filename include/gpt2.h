@@ -175,6 +175,24 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int3
 int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask, int32_t B,
                   int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss);
 
+/* For callers that cannot allocate device memory or use a workspace-backed scratch between
+ * calls (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): gpt2_evaluate with the same arguments, results and errors, whose own scratch
+ * (the per-position losses, the mask copy and the per-sequence double sums) lives in a
+ * fixed device array of the library instead of the handle's workspace. The array is
+ * GPT2_NOALLOC_MAX_SEQ * 16 + GPT2_NOALLOC_MAX_ROWS * 5 bytes (1.3 MiB); each GPU the library
+ * runs on holds one copy until the process ends. Calls with B > GPT2_NOALLOC_MAX_SEQ or
+ * B*T > GPT2_NOALLOC_MAX_ROWS fail with GPT2_EINVAL before anything is enqueued. Every call
+ * on a GPU shares that GPU's array (it keeps the last call's contents; every value a call
+ * reads is written by that call first), so calls that overlap on one GPU -- from two handles
+ * on different streams, or two threads -- race and must be serialized by the caller. The
+ * handle's activations are used as by gpt2_evaluate. Nothing here allocates: no hipMalloc,
+ * hipFree or allocating library routine. */
+#define GPT2_NOALLOC_MAX_SEQ 4096
+#define GPT2_NOALLOC_MAX_ROWS 262144
+int gpt2_evaluate_noalloc(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask,
+                          int32_t B, int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss);
+
 /* ---------------------------------------------------------------- incremental decoding */
 
 /* Sampling as the lecture notes do it (chapter 0:28:07-0:41:44 and the sampling code of

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt2_step.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EHIP = 0, -1, -2, -3
 GPT2_FP32, GPT2_BF16, GPT2_BF16_RES16 = 0, 1, 2
+GPT2_NOALLOC_MAX_SEQ, GPT2_NOALLOC_MAX_ROWS = 4096, 262144
 # dtype names accepted by make_config: the C ABI's three arithmetic modes
 DTYPES = {"fp32": GPT2_FP32, "bf16": GPT2_BF16, "bf16_res16": GPT2_BF16_RES16}
 
@@ -62,6 +63,7 @@ _SIGS = {
     "gpt2_set_grads": (ctypes.c_int, [_P, _P, ctypes.c_int]),
     "gpt2_get_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     "gpt2_evaluate": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "gpt2_evaluate_noalloc": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_reset": (ctypes.c_int, [_P, ctypes.c_int32]),
     "gpt2_decode_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "gpt2_decode_position": (ctypes.c_int32, [_P]),
@@ -200,6 +202,11 @@ def gpt2_forward(h, d_idx, d_targets, B, T, d_logits=None, d_loss=None, want_hos
 
 def gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum=None, d_row_mean=None, d_loss=None) -> None:
     _check(_lib.gpt2_evaluate(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss))
+
+
+def gpt2_evaluate_noalloc(h, d_idx, d_targets, d_mask, B, T, d_row_sum=None, d_row_mean=None,
+                          d_loss=None) -> None:
+    _check(_lib.gpt2_evaluate_noalloc(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss))
 
 
 def gpt2_decode_reset(h, B: int) -> None:

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -267,6 +268,8 @@ struct gpt2 {
     int lm_tiles = 0;   // > 0: the logits product also stored per-tile softmax statistics
     // incremental decoding: sequences in the key/value cache (0: no cache) and their length
     int dec_B = 0, dec_pos = 0;
+    // device address of this GPU's allocation-free evaluation scratch (the static array below)
+    char* na_scratch = nullptr;
     // timing
     bool timing = false;
     std::string filter;
@@ -331,6 +334,37 @@ int run(gpt2_t* h, const char* cls, Fn&& fn) {
 
 bool g_setup_done = false;
 
+}  // namespace
+
+// =================================================================== allocation-free scratch
+// The scratch of gpt2_evaluate_noalloc: per-sequence double sums and counts, the per-position
+// losses and the mask copy, in one file-scope device array that each GPU holds for the life of
+// the process. In host code `scratch` names a host-side stand-in, so kernels and copies take
+// the device address hipGetSymbolAddress returns for it, looked up once per device.
+constexpr size_t NA_ROWD_BYTES = (size_t)GPT2_NOALLOC_MAX_SEQ * 2 * sizeof(double);
+constexpr size_t NA_LOSS_BYTES = (size_t)GPT2_NOALLOC_MAX_ROWS * sizeof(float);
+constexpr size_t NA_MASK_BYTES = (size_t)GPT2_NOALLOC_MAX_ROWS;
+constexpr size_t NA_BYTES = NA_ROWD_BYTES + NA_LOSS_BYTES + NA_MASK_BYTES;
+static_assert(NA_ROWD_BYTES % 256 == 0 && NA_LOSS_BYTES % 256 == 0, "aligned sub-buffers");
+static __device__ __align__(256) char scratch[NA_BYTES];
+
+namespace {
+std::mutex g_na_mu;
+std::map<int, char*> g_na_ptr;   // device -> address of its copy of `scratch`
+
+// the device address of `scratch` on device `dev` (which must be the current device)
+int noalloc_scratch(int dev, char** out) {
+    std::lock_guard<std::mutex> lk(g_na_mu);
+    auto it = g_na_ptr.find(dev);
+    if (it != g_na_ptr.end()) { *out = it->second; return GPT2_OK; }
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+        return set_error(GPT2_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_na_ptr[dev] = (char*)p;
+    *out = (char*)p;
+    return GPT2_OK;
+}
 }  // namespace
 
 // =================================================================== sizing
@@ -419,6 +453,11 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
         rows_setup();
         decode_setup();
         g_setup_done = true;
+    }
+    {
+        // this device's allocation-free scratch (the handle's device is current here)
+        const int r = noalloc_scratch(h->dev, &h->na_scratch);
+        if (r != GPT2_OK) { delete h; return r; }
     }
     // parameters per the GPT-2 initialization, gradients and moments zero
     const int n = gpt2_num_tensors(cfg);
@@ -644,34 +683,62 @@ extern "C" int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_ta
 }
 
 // =================================================================== evaluation
-extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask,
-                             int32_t B, int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss) {
-    if (!h || !d_idx || !d_targets) return set_error(GPT2_EINVAL, "null argument");
-    const gpt2_config& c = h->cfg;
-    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
-    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
+// Forward-only scoring with its scratch (per-position losses, mask copy, per-sequence double
+// sums and counts) at the given device addresses.
+static int evaluate_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask, int32_t B,
+                         int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss, float* loss_rows,
+                         uint8_t* mask_copy, double* rowd) {
     h->have_fwd = false;   // the activations are overwritten and no gradient of the loss is formed
     h->dec_B = 0;
-    const int BT = B * T, Vp = c.padded_vocab_size;
-    const int bf = h->bf16;
+    const int BT = B * T;
     const Plan& P = h->P;
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
     int32_t* tgt = h->at<int32_t>(P.tgt);
-    uint8_t* mask = d_mask ? h->at<uint8_t>(P.mask) : nullptr;
+    uint8_t* mask = d_mask ? mask_copy : nullptr;
     HIPTRY(hipMemcpyAsync(idx, d_idx, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy idx");
     HIPTRY(hipMemcpyAsync(tgt, d_targets, (size_t)BT * 4, hipMemcpyDeviceToDevice, s), "copy targets");
     if (d_mask) HIPTRY(hipMemcpyAsync(mask, d_mask, (size_t)BT, hipMemcpyDeviceToDevice, s), "copy mask");
     TRY(forward_trunk(h, B, T));
-    float* loss_rows = h->at<float>(P.loss_rows);
     TRY(loss_rows_after_trunk(h, BT, loss_rows, nullptr, /*write_grad=*/0));
     // without a mask the batch mean is the training forward's loss, reduced the same way
     TRY(run(h, "eval_rows", [&] {
-        return masked_row_loss(loss_rows, mask, B, T, h->at<double>(P.rowd), d_row_sum, d_row_mean,
-                               mask ? d_loss : nullptr, s);
+        return masked_row_loss(loss_rows, mask, B, T, rowd, d_row_sum, d_row_mean, mask ? d_loss : nullptr, s);
     }));
     if (d_loss && !mask) TRY(run(h, "loss_mean", [&] { return mean_reduce(loss_rows, BT, d_loss, s); }));
     return GPT2_OK;
+}
+
+static int evaluate_args_ok(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int32_t B, int32_t T) {
+    if (!h || !d_idx || !d_targets) return set_error(GPT2_EINVAL, "null argument");
+    const gpt2_config& c = h->cfg;
+    if (B < 1 || B > c.max_batch) return set_error(GPT2_EINVAL, "B=%d outside [1, max_batch=%d]", B, c.max_batch);
+    if (T < 1 || T > c.block_size) return set_error(GPT2_EINVAL, "T=%d outside [1, block_size=%d]", T, c.block_size);
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_evaluate(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask,
+                             int32_t B, int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss) {
+    TRY(evaluate_args_ok(h, d_idx, d_targets, B, T));
+    const Plan& P = h->P;
+    return evaluate_impl(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss, h->at<float>(P.loss_rows),
+                         h->at<uint8_t>(P.mask), h->at<double>(P.rowd));
+}
+
+extern "C" int gpt2_evaluate_noalloc(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, const uint8_t* d_mask,
+                                     int32_t B, int32_t T, float* d_row_sum, float* d_row_mean, float* d_loss) {
+    TRY(evaluate_args_ok(h, d_idx, d_targets, B, T));
+    if (B > GPT2_NOALLOC_MAX_SEQ)
+        return set_error(GPT2_EINVAL, "B=%d exceeds the allocation-free scratch (at most %d sequences)", B,
+                         GPT2_NOALLOC_MAX_SEQ);
+    if ((int64_t)B * T > GPT2_NOALLOC_MAX_ROWS)
+        return set_error(GPT2_EINVAL, "B*T=%lld exceeds the allocation-free scratch (at most %d positions)",
+                         (long long)B * T, GPT2_NOALLOC_MAX_ROWS);
+    if (!h->na_scratch) return set_error(GPT2_ESTATE, "no allocation-free scratch on this handle's device");
+    char* base = h->na_scratch;
+    return evaluate_impl(h, d_idx, d_targets, d_mask, B, T, d_row_sum, d_row_mean, d_loss,
+                         (float*)(base + NA_ROWD_BYTES), (uint8_t*)(base + NA_ROWD_BYTES + NA_LOSS_BYTES),
+                         (double*)base);
 }
 
 // =================================================================== incremental decoding
