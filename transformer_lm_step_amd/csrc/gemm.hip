@@ -44,6 +44,7 @@ struct GemmArgs {
     int beta;                   // 1: add into the fp32 output
     int64_t part_stride;        // split-K partial stride (elements)
     float* rowsum_part;         // [nsplit][M] row sums of A (a_layout 1), or null
+    float* rowsum_out;          // with one split: the row sums of A written (beta: added) here directly
     int vec;                    // 1: full tiles may use 8/16-byte epilogue accesses
     int vec8;                   // 1: also 8-element (16-byte bf16) epilogue accesses
 };
@@ -748,22 +749,20 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
     }
 }
 
-template <int ALAY, int BLAY, int EPI, int BM, int BN, bool ROWSUM = false>
-// Bounds of one workgroup per CU: the compiler then keeps the accumulators in AGPRs and uses the
-// VGPRs for deeper load scheduling (measured 10-15% faster than a two-workgroup bound). Every
-// instantiation stays at or below 256 registers in total, so two workgroups still share a CU.
-// (The row-sum variant needs the explicit two-workgroup bound to stay within 256 registers.)
-__global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmArgs p) {
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
+// One output tile of the LDS-streamed path: workgroup `pid` of `nwg` over the tiles of p, K
+// split `split` (a plain launch passes blockIdx.x, gridDim.x, blockIdx.y; a grouped launch its
+// product's own numbering).
+template <int ALAY, int BLAY, int EPI, int BM, int BN, bool ROWSUM>
+DEV void mm_tile(const GemmArgs& p, int pid, int nwg, int split, char* smem) {
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
     const int num_m = (p.M + BM - 1) / BM, num_n = (p.N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, num_m, num_n, tm, tn);
+    tile_coords(pid, nwg, num_m, num_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int kbeg = blockIdx.y * p.ksplit_len;
+    const int kbeg = split * p.ksplit_len;
     const int nt = min(p.ksplit_len, p.K - kbeg) / MM_BK;
 
     uint32_t offA[BM / 32], offB[BN / 32];
@@ -787,7 +786,7 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
     floatx4 rs[ROWSUM ? FM : 1];
 #pragma unroll
     for (int i = 0; i < (ROWSUM ? FM : 1); ++i) rs[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const bool do_rs = ROWSUM && tn == 0 && wn == 0;
+    const bool do_rs = ROWSUM && (p.rowsum_part || p.rowsum_out) && tn == 0 && wn == 0;
 
     if (nt > 0) {
         mm_issue<BM>(baseA, offA, lds0, wave);
@@ -834,11 +833,47 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
                 const int m = m0 + wm * TM + 16 * i + (lane & 15);
-                if (lane < 16 && m < p.M) p.rowsum_part[(int64_t)blockIdx.y * p.M + m] = rs[i][0];
+                if (lane < 16 && m < p.M) {
+                    if (p.rowsum_out) p.rowsum_out[m] = p.beta ? p.rowsum_out[m] + rs[i][0] : rs[i][0];
+                    else p.rowsum_part[(int64_t)split * p.M + m] = rs[i][0];
+                }
             }
         }
     }
     store_staged<EPI, FM, FN, BN>(p, acc, smem, m0, n0, wm, wn, lane, tid);
+}
+
+// Bounds of one workgroup per CU: the compiler then keeps the accumulators in AGPRs and uses the
+// VGPRs for deeper load scheduling (measured 10-15% faster than a two-workgroup bound). Every
+// instantiation stays at or below 256 registers in total, so two workgroups still share a CU.
+// (The row-sum variant needs the explicit two-workgroup bound to stay within 256 registers.)
+template <int ALAY, int BLAY, int EPI, int BM, int BN, bool ROWSUM = false>
+__global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmArgs p) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    mm_tile<ALAY, BLAY, EPI, BM, BN, ROWSUM>(p, blockIdx.x, gridDim.x, blockIdx.y, smem);
+}
+
+// Grouped weight-gradient products: workgroup w runs tile w - tile0 of the product whose range
+// [tile0, tile0 + ntiles) holds w (found by a binary search over the sorted ranges); every
+// product takes the whole K, so there are no split-K partials.
+template <int BN>
+__global__ void __launch_bounds__(GTHREADS, 2) gemm_mm_group_kernel(GemmArgs base, const GroupProb* __restrict__ probs,
+                                                                    int nprob) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int w = blockIdx.x;
+    int lo = 0, hi = nprob - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (probs[mid].tile0 <= w) lo = mid;
+        else hi = mid - 1;
+    }
+    const GroupProb g = probs[lo];
+    GemmArgs p = base;
+    p.A = g.A; p.B = g.B; p.C = g.C; p.lda = g.lda; p.ldb = g.ldb; p.ldc = g.ldc;
+    p.M = g.M; p.N = g.N;
+    p.rowsum_part = nullptr;
+    p.rowsum_out = g.rowsum;
+    mm_tile<1, 1, EPI_F32, 128, BN, true>(p, w - g.tile0, g.ntiles, 0, smem);
 }
 
 template <int BM, int BN>
@@ -858,6 +893,35 @@ static hipError_t launch_mm(const GemmArgs& a, int nsplit, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+static bool mm_ok(const GemmDesc& d, int ksplit_len);
+
+int gemm_group_tiles(int M, int N, int bn) { return ((M + 127) / 128) * ((N + bn - 1) / bn); }
+
+bool gemm_group_ok(const GroupProb& g, int K) {
+    auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    GemmDesc d;
+    d.A = g.A; d.lda = g.lda; d.a_layout = 1;
+    d.B = g.B; d.ldb = g.ldb; d.b_layout = 1;
+    d.M = g.M; d.N = g.N; d.K = K;
+    return mm_ok(d, K) && g.ldc % 4 == 0 && al(g.C) && (!g.rowsum || al(g.rowsum));
+}
+
+hipError_t gemm_grouped(const GroupProb* d_probs, int nprob, int total_tiles, int K, float alpha, int beta, int bn,
+                        hipStream_t s) {
+    if (nprob < 1 || total_tiles < 1 || K % MM_BK || (bn != 128 && bn != 192)) return hipErrorInvalidValue;
+    GemmArgs a{};
+    a.K = K;
+    a.ksplit_len = K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.vec = 1;
+    if (bn == 192)
+        gemm_mm_group_kernel<192><<<dim3(total_tiles), dim3(GTHREADS), mm_lds_bytes<128, 192>(), s>>>(a, d_probs, nprob);
+    else
+        gemm_mm_group_kernel<128><<<dim3(total_tiles), dim3(GTHREADS), mm_lds_bytes<128, 128>(), s>>>(a, d_probs, nprob);
+    return hipGetLastError();
+}
 
 // out[m][n] = (beta ? out : 0) + alpha * sum_z part[z][m][n], z in order (deterministic).
 // Workgroups past the matrix (when rs_out is set) reduce the row-sum partials the same way:
@@ -1024,6 +1088,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     a.C = d.C; a.ldc = d.ldc; a.C2 = d.C2; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
     a.aux = d.aux; a.ldaux = d.ldaux; a.alpha = d.alpha; a.beta = d.beta;
     a.rowsum_part = nullptr;
+    a.rowsum_out = nullptr;
     constexpr int BK = 128 / sizeof(T);
     int nsplit = d.nsplit < 1 ? 1 : d.nsplit;
     const int ktiles = (d.K + BK - 1) / BK;
@@ -1184,6 +1249,10 @@ void gemm_setup() {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
     (void)hipFuncSetAttribute((const void*)gemm_mm_kernel<1, 1, EPI_F32, 128, 128, true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mm_lds_bytes<128, 128>());
+    (void)hipFuncSetAttribute((const void*)gemm_mm_group_kernel<192>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)mm_lds_bytes<128, 192>());
+    (void)hipFuncSetAttribute((const void*)gemm_mm_group_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)mm_lds_bytes<128, 128>());
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();

@@ -167,7 +167,13 @@ struct Plan {
     // offsets in bytes
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
-    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dres16, dln, datt, dqkv, du, Dbuf;
+    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, Dbuf;
+    // output gradients that feed products: per layer in the bf16 modes (kept for the grouped
+    // weight-gradient launch at the end of the backward), one shared buffer in fp32 mode
+    std::vector<size_t> du, dqkv;
+    // bf16 copies of the residual gradient at each layer's output and after its attention
+    std::vector<size_t> d16o, d16m;
+    size_t gprob;          // GroupProb table of the grouped weight-gradient launch (4 per layer)
     size_t splitk, rspart, lnpart, cspart, sumscr, normpart, normcoef, ebscratch;
     // LayerNorm backward partials: one set per LayerNorm (ln_f, then ln_2 and ln_1 of each layer
     // from the last), reduced together after the backward; the sets' gradient offsets
@@ -217,12 +223,18 @@ Plan make_plan(const gpt2_config* c) {
     P.mask = take(BT);
     P.rowd = take((size_t)c->max_batch * 2 * 8);
     P.dres = take(BT * C * er);
-    // bf16 copy of an fp32 residual gradient: the A operand of the products that take it
-    P.dres16 = (bf && er == 4) ? take(BT * C * 2) : 0;
     P.dln = take(BT * C * es);
     P.datt = take(BT * C * es);
-    P.dqkv = take(BT * 3 * C * es);
-    P.du = take(BT * F * es);
+    for (int l = 0; l < (bf ? c->n_layer : 1); ++l) {
+        P.dqkv.push_back(take(BT * 3 * C * es));
+        P.du.push_back(take(BT * F * es));
+    }
+    if (bf)
+        for (int l = 0; l < c->n_layer; ++l) {
+            P.d16o.push_back(take(BT * C * 2));
+            P.d16m.push_back(take(BT * C * 2));
+        }
+    P.gprob = take((size_t)4 * c->n_layer * sizeof(GroupProb));
     P.Dbuf = take(2 * BT * H * 4);   // attention backward: D, then the base-2 log-sum-exp
     size_t sk = 0;
     const int shapes[4][2] = {{(int)(3 * C), (int)C}, {(int)C, (int)C}, {(int)F, (int)C}, {(int)C, (int)F}};
@@ -270,6 +282,10 @@ struct gpt2 {
     int dec_B = 0, dec_pos = 0;
     // device address of this GPU's allocation-free evaluation scratch (the static array below)
     char* na_scratch = nullptr;
+    // grouped weight-gradient launch: usable (bf16, shapes the LDS-streamed path takes), its
+    // tile width and total workgroups
+    bool group_ok = false;
+    int group_bn = 128, group_tiles = 0;
     // timing
     bool timing = false;
     std::string filter;
@@ -498,6 +514,42 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
             off[nln + i + 1] = h->L.b_o[l];
         }
         e = hipMemcpy(h->at<int64_t>(h->P.lnoff), off.data(), off.size() * 8, hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess && h->bf16) {
+        // the weight-gradient products of every layer, for one grouped launch after the backward:
+        // mlp.c_proj (A = residual gradient at the layer output, B = a), mlp.c_fc (du, h2; bias
+        // = row sums of du), attn.c_proj (residual gradient after attention, y), attn.c_attn
+        // (dqkv, h1; bias = row sums of dqkv)
+        const Layout& L = h->L;
+        const Plan& P = h->P;
+        float* grd = h->grads();
+        const int C = cfg->n_embd, F = cfg->mlp_hidden;
+        const int bn = (C % 192 == 0 && F % 192 == 0) ? 192 : 128;
+        std::vector<GroupProb> pr;
+        bool ok = true;
+        int tile0 = 0;
+        for (int l = cfg->n_layer - 1; l >= 0; --l) {
+            auto add = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t woff, int M, int N,
+                           int64_t boff) {
+                GroupProb g{};
+                g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+                g.C = grd + woff; g.ldc = N; g.M = M; g.N = N;
+                g.rowsum = boff >= 0 ? grd + boff : nullptr;
+                g.tile0 = tile0;
+                g.ntiles = gemm_group_tiles(M, N, bn);
+                tile0 += g.ntiles;
+                ok = ok && gemm_group_ok(g, 64);
+                pr.push_back(g);
+            };
+            add(h->at<char>(P.d16o[l]), C, h->at<char>(P.a[l]), F, L.w_pr[l], C, F, -1);
+            add(h->at<char>(P.du[l]), F, h->at<char>(P.h2[l]), C, L.w_fc[l], F, C, L.b_fc[l]);
+            add(h->at<char>(P.d16m[l]), C, h->at<char>(P.att[l]), C, L.w_o[l], C, C, -1);
+            add(h->at<char>(P.dqkv[l]), 3 * C, h->at<char>(P.h1[l]), C, L.w_qkv[l], 3 * C, C, L.b_qkv[l]);
+        }
+        h->group_ok = ok;
+        h->group_bn = bn;
+        h->group_tiles = tile0;
+        e = hipMemcpy(h->at<GroupProb>(P.gprob), pr.data(), pr.size() * sizeof(GroupProb), hipMemcpyHostToDevice);
     }
     if (e != hipSuccess) { delete h; return set_error(GPT2_EHIP, "init: %s", hipGetErrorString(e)); }
     *out = h;
@@ -863,8 +915,15 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     // gradient of the residual stream, in the residual stream's type; the products take it as
     // bf16 (under the autocast recipe the gradient reaching a bf16 product output is cast down)
     char* dres = h->at<char>(P.dres);
-    char* dres16 = P.dres16 ? h->at<char>(P.dres16) : nullptr;
-    char* dres_op = dres16 ? dres16 : dres;
+    // bf16 copies of the residual gradient, one per point where a product takes it (fp32 mode:
+    // the products take the fp32 gradient itself)
+    auto d16_out = [&](int l) -> char* { return bf ? h->at<char>(P.d16o[l]) : dres; };
+    auto d16_mid = [&](int l) -> char* { return bf ? h->at<char>(P.d16m[l]) : dres; };
+    auto du_of = [&](int l) -> char* { return h->at<char>(P.du[bf ? l : 0]); };
+    auto dqkv_of = [&](int l) -> char* { return h->at<char>(P.dqkv[bf ? l : 0]); };
+    // every weight gradient of the blocks in one grouped launch after the layer loop (whole-K
+    // products, no split-K), where the shapes allow it; otherwise per layer with split-K
+    const bool grouped = h->group_ok && BT % 64 == 0;
     // gradient of a LayerNorm's output, in the storage type: under the autocast recipe it is the
     // bf16 input gradient of the following product, cast to fp32 where LayerNorm runs
     char* dln = h->at<char>(P.dln);
@@ -879,10 +938,12 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     // (gathered by the same kernel) is the bias gradient of the projection at that offset
     // (the weight, bias and projection-bias gradients come from the partial sets after the last
     // LayerNorm, in one reduction; the sets' order is the one the offsets table was built in)
-    auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres) -> int {
+    // (copy16: where the bf16 copy of the new residual gradient goes, or null)
+    auto ln_bwd = [&](const void* x, const float* mean, const float* rstd, int64_t w_off, int accum_dres,
+                      char* copy16) -> int {
         float* part = lnpart + (size_t)lnset++ * P.lnset_stride;
         return run(h, "layernorm_bwd", [&] {
-            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, dres16, accum_dres, part, lnblk, BT, C, bf,
+            return layernorm_backward(dln, x, mean, rstd, prm + w_off, dres, copy16, accum_dres, part, lnblk, BT, C, bf,
                                       r16, s);
         });
     };
@@ -919,35 +980,39 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         g.epi = EPI_F32; g.C = grd + L.wte; g.ldc = C; g.alpha = grad_scale; g.beta = acc;
         TRY(run(h, "gemm_lm_head_dw", [&] { return gemm(g, bf, s); }));
     }
-    TRY(ln_bwd(h->at<char>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0));
+    TRY(ln_bwd(h->at<char>(P.x_in[c.n_layer]), h->at<float>(P.meanf), h->at<float>(P.rstdf), L.lnf_w, 0,
+               bf ? d16_out(c.n_layer - 1) : nullptr));
 
     for (int l = c.n_layer - 1; l >= 0; --l) {
         // x_out = x_mid + a Wpr^T + bpr
-        TRY(dw(dres_op, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
+        char* g_out = d16_out(l);
+        if (!grouped) TRY(dw(g_out, C, h->at<char>(P.a[l]), F, C, F, L.w_pr[l]));
         {
             GemmDesc g;
-            g.A = dres_op; g.lda = C; g.a_layout = 0;
+            g.A = g_out; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_pr[l]); g.ldb = F; g.b_layout = 1;
             g.M = BT; g.N = F; g.K = C;
-            g.epi = EPI_GELU_BWD; g.C = h->at<char>(P.du); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
+            g.epi = EPI_GELU_BWD; g.C = du_of(l); g.ldc = F; g.aux = h->at<char>(P.u[l]); g.ldaux = F;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
-        TRY(dw(h->at<char>(P.du), F, h->at<char>(P.h2[l]), C, F, C, L.w_fc[l], L.b_fc[l]));
+        if (!grouped) TRY(dw(du_of(l), F, h->at<char>(P.h2[l]), C, F, C, L.w_fc[l], L.b_fc[l]));
         {
             GemmDesc g;
-            g.A = h->at<char>(P.du); g.lda = F; g.a_layout = 0;
+            g.A = du_of(l); g.lda = F; g.a_layout = 0;
             g.B = h->wop(L.w_fc[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = F;
             g.epi = EPI_BIAS_T; g.C = dln; g.ldc = C; g.alpha = 1.f;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the mlp.c_proj bias gradient)
-        TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1));
+        TRY(ln_bwd(h->at<char>(P.x_mid[l]), h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), L.ln2_w[l], 1,
+                   bf ? d16_mid(l) : nullptr));
         // x_mid = x_in + y Wo^T + bo
-        TRY(dw(dres_op, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
+        char* g_mid = d16_mid(l);
+        if (!grouped) TRY(dw(g_mid, C, h->at<char>(P.att[l]), C, C, C, L.w_o[l]));
         {
             GemmDesc g;
-            g.A = dres_op; g.lda = C; g.a_layout = 0;
+            g.A = g_mid; g.lda = C; g.a_layout = 0;
             g.B = h->wop(L.w_o[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = C;
             g.epi = EPI_BIAS_T; g.C = h->at<char>(P.datt); g.ldc = C; g.alpha = 1.f;
@@ -955,20 +1020,25 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
         }
         TRY(run(h, "attn_bwd", [&] {
             return attention_backward(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), h->at<char>(P.datt),
-                                      h->at<float>(P.lse[l]), h->at<float>(P.Dbuf), h->at<char>(P.dqkv), B, T, H, hs, bf, s);
+                                      h->at<float>(P.lse[l]), h->at<float>(P.Dbuf), dqkv_of(l), B, T, H, hs, bf, s);
         }));
-        TRY(dw(h->at<char>(P.dqkv), 3 * C, h->at<char>(P.h1[l]), C, 3 * C, C, L.w_qkv[l], L.b_qkv[l]));
+        if (!grouped) TRY(dw(dqkv_of(l), 3 * C, h->at<char>(P.h1[l]), C, 3 * C, C, L.w_qkv[l], L.b_qkv[l]));
         {
             GemmDesc g;
-            g.A = h->at<char>(P.dqkv); g.lda = 3 * C; g.a_layout = 0;
+            g.A = dqkv_of(l); g.lda = 3 * C; g.a_layout = 0;
             g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 1;
             g.M = BT; g.N = C; g.K = 3 * C;
             g.epi = EPI_BIAS_T; g.C = dln; g.ldc = C; g.alpha = 1.f;
             TRY(run(h, "gemm_dx", [&] { return gemm(g, bf, s); }));
         }
         // (the column sum of the incoming dres is the attn.c_proj bias gradient)
-        TRY(ln_bwd(h->at<char>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1));
+        TRY(ln_bwd(h->at<char>(P.x_in[l]), h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), L.ln1_w[l], 1,
+                   (bf && l > 0) ? d16_out(l - 1) : nullptr));
     }
+    if (grouped)
+        TRY(run(h, "gemm_dw", [&] {
+            return gemm_grouped(h->at<GroupProb>(P.gprob), 4 * c.n_layer, h->group_tiles, BT, 1.f, acc, h->group_bn, s);
+        }));
     // LayerNorm weight and bias gradients, and the projection bias gradients (column sums of the
     // residual gradient entering each ln_2 / ln_1), from every set at once
     TRY(run(h, "ln_param_grad", [&] {

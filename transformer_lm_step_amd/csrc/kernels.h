@@ -49,6 +49,24 @@ int gemm_logits_tiles(const GemmDesc& d, int is_bf16);
 // 1 if gemm() computes d.rowsum itself (LDS-streamed bf16 path), 0 if the caller must
 int gemm_fuses_rowsum(const GemmDesc& d, int is_bf16);
 void gemm_pick_tile(int M, int N, int nsplit, int is_bf16, int* bm, int* bn);
+
+// Grouped weight-gradient products (bf16 operands, LDS-streamed path): product i computes
+//   C_i[m][n] = (beta ? C_i : 0) + alpha * sum_k A_i[k*lda_i + m] * B_i[k*ldb_i + n]
+// over the shared K (dW = dY^T X with K = tokens), and with rowsum_i non-null also
+//   rowsum_i[m] = (beta ? rowsum_i : 0) + sum_k A_i[k*lda_i + m]      (the bias gradient).
+// One launch of 128 x bn tiles; the products' tile ranges [tile0, tile0 + ntiles) are
+// consecutive and ascending (ntiles = gemm_group_tiles(M, N, bn)). Every output element is
+// one workgroup's fixed-order sum over K (deterministic, no split-K).
+struct GroupProb {
+    const void* A; const void* B; float* C; float* rowsum;
+    int64_t lda, ldb, ldc;
+    int M, N;
+    int tile0, ntiles;
+};
+int gemm_group_tiles(int M, int N, int bn);
+bool gemm_group_ok(const GroupProb& g, int K);   // the LDS-streamed path's shape rules hold
+hipError_t gemm_grouped(const GroupProb* d_probs, int nprob, int total_tiles, int K, float alpha, int beta, int bn,
+                        hipStream_t s);
 void gemm_setup();
 size_t gemm_lds_bytes();
 
