@@ -15,7 +15,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgpt2_step.so")
+# the in-tree build, or another build of the same library named by GPT2_STEP_LIB
+LIB_PATH = os.environ.get("GPT2_STEP_LIB") or os.path.join(_HERE, "libgpt2_step.so")
 
 GPT2_OK, GPT2_EINVAL, GPT2_ESTATE, GPT2_EHIP = 0, -1, -2, -3
 GPT2_FP32, GPT2_BF16, GPT2_BF16_RES16 = 0, 1, 2
