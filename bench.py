@@ -64,8 +64,10 @@ def class_costs(w, B, n_params, n_decay, mode="train", res16=False):
         "gemm_dw": ("flop", 2 * BT * C * (3 * C + C + F + F) * L),
         "attn_fwd": ("flop", attn_fwd * L),
         "attn_bwd": ("flop", 2.5 * attn_fwd * L),   # dV, dP, dK, dQ plus the S recompute
-        # the residual stream read, the bf16 LayerNorm output written, mean and rstd
-        "layernorm_fwd": ("byte", (2 * L + 1) * (BT * C * (er + es) + 8 * BT)),
+        # the first LayerNorm reads the residual stream and writes its bf16 output; the other 2L
+        # add the projection output (bf16) to the stream first: the old stream and y read, the
+        # new stream and the bf16 output written; mean and rstd
+        "layernorm_fwd": ("byte", BT * C * (er + es) + 2 * L * BT * C * (2 * er + 2 * es) + (2 * L + 1) * 8 * BT),
         # dh (bf16) and x read, the residual gradient (and its bf16 copy) written, mean and rstd;
         # all but the final LayerNorm's also read the incoming residual gradient
         "layernorm_bwd": ("byte", (2 * L + 1) * (BT * C * (es + 2 * er + cp) + 8 * BT) + 2 * L * BT * C * er),

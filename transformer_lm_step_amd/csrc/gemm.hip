@@ -38,7 +38,6 @@ struct GemmArgs {
     void* C; int64_t ldc;       // main output (storage type or fp32, per epilogue)
     void* C2;                   // second output (GELU activation)
     const float* bias;
-    const void* resid; int64_t ldr;   // residual input (storage type)
     const void* aux; int64_t ldaux;   // pre-activation u for the GELU derivative
     float alpha;
     int beta;                   // 1: add into the fp32 output
@@ -176,7 +175,7 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
         const int n = nw + j * 16 + (lane & 15);
         const bool nok = !CHECK || n < p.N;
         float bias = 0.f;
-        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_BIAS_GELU)
+        if constexpr (EPI == EPI_BIAS_T || EPI == EPI_BIAS_GELU)
             bias = (p.bias && nok) ? p.bias[n] : 0.f;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -187,11 +186,7 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                 const int m = mb + r;
                 const bool ok = !CHECK || (nok && m < p.M);
                 extra[r] = 0.f;
-                if constexpr (EPI == EPI_BIAS_RESID) {
-                    if (ok) extra[r] = to_f<T>(((const T*)p.resid)[(int64_t)m * p.ldr + n]);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    if (ok) extra[r] = ((const float*)p.resid)[(int64_t)m * p.ldr + n];
-                } else if constexpr (EPI == EPI_GELU_BWD) {
+                if constexpr (EPI == EPI_GELU_BWD) {
                     if (ok) extra[r] = to_f<T>(((const T*)p.aux)[(int64_t)m * p.ldaux + n]);
                 } else if constexpr (EPI == EPI_F32) {
                     if (ok && p.beta) extra[r] = ((const float*)p.C)[(int64_t)m * p.ldc + n];
@@ -205,10 +200,6 @@ DEV void store_body(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
                 const int64_t o = (int64_t)m * p.ldc + n;
                 if constexpr (EPI == EPI_BIAS_T) {
                     ((T*)p.C)[o] = from_f<T>(p.alpha * v + bias);
-                } else if constexpr (EPI == EPI_BIAS_RESID) {
-                    ((T*)p.C)[o] = from_f<T>(extra[r] + v + bias);
-                } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-                    ((float*)p.C)[o] = extra[r] + v + bias;
                 } else if constexpr (EPI == EPI_BIAS_GELU) {
                     const T u = from_f<T>(v + bias);
                     ((T*)p.C)[o] = u;
@@ -393,18 +384,15 @@ DEV bf16x4 to_bf16x4(float a, float b, float c, float d) {
 // loads of a whole staged half are in flight together instead of one after each store.
 template <int EPI> struct EpiIn { typedef float4 T; };
 template <> struct EpiIn<EPI_GELU_BWD> { typedef bf16x4 T; };
-template <> struct EpiIn<EPI_BIAS_RESID> { typedef bf16x4 T; };
 template <int EPI>
 DEV bool epi_reads(const GemmArgs& p) {
-    return EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 || EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
+    return EPI == EPI_GELU_BWD || (EPI == EPI_F32 && p.beta);
 }
 // 1 if the 4 columns n..n+3 of row m take the vector path
 DEV bool epi_vec(const GemmArgs& p, int m, int n) { return m < p.M && p.vec && n + 3 < p.N; }
 template <int EPI>
 DEV typename EpiIn<EPI>::T epi_load(const GemmArgs& p, int m, int n) {
-    if constexpr (EPI == EPI_BIAS_RESID) return *(const bf16x4*)((const bf16*)p.resid + (int64_t)m * p.ldr + n);
-    else if constexpr (EPI == EPI_BIAS_RESID_F32) return *(const float4*)((const float*)p.resid + (int64_t)m * p.ldr + n);
-    else if constexpr (EPI == EPI_GELU_BWD) return *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
+    if constexpr (EPI == EPI_GELU_BWD) return *(const bf16x4*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
     else return *(const float4*)((const float*)p.C + (int64_t)m * p.ldc + n);
 }
 
@@ -416,8 +404,7 @@ template <int EPI>
 constexpr bool epi_alpha() { return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_F32; }
 template <int EPI>
 constexpr bool epi_bias() {
-    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_RESID_F32 ||
-           EPI == EPI_BIAS_GELU;
+    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_GELU;
 }
 // bias of columns n..n+3 (0 past the matrix edge or without a bias)
 DEV float4 bias4(const GemmArgs& p, int n) {
@@ -455,10 +442,6 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
     if (!CHECK || (p.vec && n + 3 < p.N)) {
         if constexpr (EPI == EPI_BIAS_T) {
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == EPI_BIAS_RESID) {
-            const bf16x4 rr = in;
-            *(bf16x4*)((bf16*)p.C + o) = to_bf16x4((float)rr[0] + v[0], (float)rr[1] + v[1], (float)rr[2] + v[2],
-                                                   (float)rr[3] + v[3]);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             const bf16x4 u = to_bf16x4(v[0], v[1], v[2], v[3]);
             *(bf16x4*)((bf16*)p.C + o) = u;
@@ -468,9 +451,6 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
             const bf16x4 a = in;
             *(bf16x4*)((bf16*)p.C + o) = to_bf16x4(v[0] * gelu_grad_f((float)a[0]), v[1] * gelu_grad_f((float)a[1]),
                                                    v[2] * gelu_grad_f((float)a[2]), v[3] * gelu_grad_f((float)a[3]));
-        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            const float4 rr = in;
-            *(float4*)((float*)p.C + o) = make_float4(rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]);
         } else if constexpr (EPI == EPI_F32) {
             float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
             if (p.beta) old = in;
@@ -487,10 +467,6 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
         const int64_t e = o + r;
         if constexpr (EPI == EPI_BIAS_T) {
             ((bf16*)p.C)[e] = (bf16)v[r];
-        } else if constexpr (EPI == EPI_BIAS_RESID) {
-            ((bf16*)p.C)[e] = (bf16)((float)((const bf16*)p.resid)[(int64_t)m * p.ldr + nn] + v[r]);
-        } else if constexpr (EPI == EPI_BIAS_RESID_F32) {
-            ((float*)p.C)[e] = ((const float*)p.resid)[(int64_t)m * p.ldr + nn] + v[r];
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             const bf16 u = (bf16)v[r];
             ((bf16*)p.C)[e] = u;
@@ -511,12 +487,10 @@ DEV void epi4(const GemmArgs& p, int m, int n, const float4& v4, const typename 
 // 8-byte stores: the epilogue's store instructions, not its bytes, were what it waited on).
 template <int EPI>
 constexpr bool epi_wide() {
-    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_RESID || EPI == EPI_BIAS_GELU ||
-           EPI == EPI_GELU_BWD;
+    return EPI == EPI_BIAS_T || EPI == EPI_LOGITS || EPI == EPI_BIAS_GELU || EPI == EPI_GELU_BWD;
 }
 template <int EPI> struct EpiIn8 { typedef int T; };
 template <> struct EpiIn8<EPI_GELU_BWD> { typedef bf16x8 T; };
-template <> struct EpiIn8<EPI_BIAS_RESID> { typedef bf16x8 T; };
 DEV bool epi_vec8(const GemmArgs& p, int m, int n) { return m < p.M && p.vec8 && n + 7 < p.N; }
 
 DEV bf16x8 to_bf16x8(const float (&v)[8]) {
@@ -526,8 +500,8 @@ DEV bf16x8 to_bf16x8(const float (&v)[8]) {
     return o;
 }
 // epi4 on 8 consecutive columns n..n+7 (a: the first 4 values, b: the next 4, with alpha and
-// the bias applied); `in` is the 8 residual values or saved pre-activations (GELU derivative)
-// on the vector path
+// the bias applied); `in` is the 8 saved pre-activations of the GELU derivative on the vector
+// path
 
 // 16-byte store that bypasses the caches (for outputs read again only much later or from HBM
 // anyway)
@@ -550,10 +524,6 @@ DEV void epi8(const GemmArgs& p, int m, int n, const float4& a, const float4& b,
             st16_nt((bf16*)p.C + o, to_bf16x8(v));
         } else if constexpr (EPI == EPI_BIAS_T) {
             *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(v);
-        } else if constexpr (EPI == EPI_BIAS_RESID) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) r[q] = (float)in[q] + v[q];
-            *(bf16x8*)((bf16*)p.C + o) = to_bf16x8(r);
         } else {  // EPI_BIAS_GELU
             const bf16x8 u = to_bf16x8(v);
             *(bf16x8*)((bf16*)p.C + o) = u;
@@ -597,17 +567,12 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     auto half = [&](auto hc) {
         constexpr int h = decltype(hc)::value;
         In in[NIT];
-        if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_BIAS_RESID) {
+        if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int k = tid + it * GTHREADS, r = k / CPR, c = k - r * CPR;
                 const int m = m0 + 64 * h + r, n = n0 + 8 * c;
-                if (!CHK || epi_vec8(p, m, n)) {
-                    if constexpr (EPI == EPI_GELU_BWD)
-                        in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
-                    else
-                        in[it] = *(const bf16x8*)((const bf16*)p.resid + (int64_t)m * p.ldr + n);
-                }
+                if (!CHK || epi_vec8(p, m, n)) in[it] = *(const bf16x8*)((const bf16*)p.aux + (int64_t)m * p.ldaux + n);
             }
         }
         if (wm == h) {
@@ -670,7 +635,7 @@ DEV void store_staged_bf16(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char
     half(std::integral_constant<int, 0>{});
     half(std::integral_constant<int, 1>{});
 }
-// fp32 outputs (gradient output, split-K partials, the fp32 residual add): 4-column chunks (already
+// fp32 outputs (gradient output, split-K partials): 4-column chunks (already
 // 16-byte accesses), alpha and the bias applied per chunk by epi4. Split-K partials of
 // a tile inside the matrix skip the per-chunk checks. (Applying alpha and the bias ahead of
 // epi4, as the bf16 form does, measured 9-12% slower here.)
@@ -1064,8 +1029,7 @@ static bool skinny_ok(const GemmDesc& d, int nsplit) {
     constexpr int E = 16 / sizeof(T);
     if (d.M > SK_MAX_M || d.a_layout != 0 || d.b_layout != 0 || nsplit != 1 || d.rowsum) return false;
     if (d.N > 16384) return false;   // very wide products (the vocabulary) fill the GPU on the tiled path
-    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_RESID && d.epi != EPI_BIAS_RESID_F32 && d.epi != EPI_BIAS_GELU)
-        return false;
+    if (d.epi != EPI_BIAS_T && d.epi != EPI_BIAS_GELU) return false;
     if (d.K % E || d.lda % E || d.ldb % E) return false;
     return (((uintptr_t)d.A | (uintptr_t)d.B) & 15) == 0;
 }
@@ -1074,8 +1038,6 @@ template <typename T>
 static hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
     if (epi == EPI_BIAS_T) gemm_skinny_kernel<T, EPI_BIAS_T><<<grid, blk, 0, s>>>(a);
-    else if (epi == EPI_BIAS_RESID) gemm_skinny_kernel<T, EPI_BIAS_RESID><<<grid, blk, 0, s>>>(a);
-    else if (epi == EPI_BIAS_RESID_F32) gemm_skinny_kernel<T, EPI_BIAS_RESID_F32><<<grid, blk, 0, s>>>(a);
     else gemm_skinny_kernel<T, EPI_BIAS_GELU><<<grid, blk, 0, s>>>(a);
     return hipGetLastError();
 }
@@ -1085,7 +1047,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     GemmArgs a{};
     a.A = d.A; a.B = d.B; a.lda = d.lda; a.ldb = d.ldb;
     a.M = d.M; a.N = d.N; a.K = d.K;
-    a.C = d.C; a.ldc = d.ldc; a.C2 = d.C2; a.bias = d.bias; a.resid = d.resid; a.ldr = d.ldr;
+    a.C = d.C; a.ldc = d.ldc; a.C2 = d.C2; a.bias = d.bias;
     a.aux = d.aux; a.ldaux = d.ldaux; a.alpha = d.alpha; a.beta = d.beta;
     a.rowsum_part = nullptr;
     a.rowsum_out = nullptr;
@@ -1099,9 +1061,9 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     {
         // vector epilogue accesses need 4-element-aligned rows and 16-byte aligned bases
         auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
-        a.vec = d.ldc % 4 == 0 && d.ldr % 4 == 0 && d.ldaux % 4 == 0 && al(d.C) && al(d.C2) && al(d.bias) &&
-                al(d.resid) && al(d.aux) && al(d.partial);
-        a.vec8 = a.vec && d.ldc % 8 == 0 && d.ldaux % 8 == 0 && d.ldr % 8 == 0;
+        a.vec = d.ldc % 4 == 0 && d.ldaux % 4 == 0 && al(d.C) && al(d.C2) && al(d.bias) && al(d.aux) &&
+                al(d.partial);
+        a.vec8 = a.vec && d.ldc % 8 == 0 && d.ldaux % 8 == 0;
     }
     int epi = d.epi;
     if (epi == EPI_LOGITS && !gemm_logits_tiles(d, sizeof(T) == 2)) return hipErrorInvalidValue;
@@ -1142,8 +1104,6 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if (wide && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 192>(a, nsplit, s); else
             MM_CASE_WIDE(0, 0, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_LOGITS)
-            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID)
-            MM_CASE_WIDE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE_WIDE(0, 1, EPI_F32)
             MM_CASE_WIDE(0, 1, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_BIAS_GELU)
@@ -1151,8 +1111,6 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(1, 1, EPI_PARTIAL)
             MM_CASE_WIDE(1, 1, EPI_F32)
             MM_CASE(0, 0, EPI_BIAS_T)
-            MM_CASE(0, 0, EPI_BIAS_RESID)
-            MM_CASE(0, 0, EPI_BIAS_RESID_F32)
             MM_CASE(0, 0, EPI_BIAS_GELU)
             MM_CASE(0, 1, EPI_GELU_BWD)
             MM_CASE(0, 1, EPI_F32)
@@ -1169,8 +1127,6 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
 #define GEMM_CASE(AL, BL, EP) \
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_tiled<T, AL, BL, EP>(a, nsplit, bm, bn, s); else
     GEMM_CASE(0, 0, EPI_BIAS_T)
-    GEMM_CASE(0, 0, EPI_BIAS_RESID)
-    GEMM_CASE(0, 0, EPI_BIAS_RESID_F32)
     GEMM_CASE(0, 0, EPI_BIAS_GELU)
     GEMM_CASE(0, 1, EPI_GELU_BWD)
     GEMM_CASE(0, 1, EPI_F32)
@@ -1236,8 +1192,7 @@ static void set_lds_mm() {
 }
 
 void gemm_setup() {
-    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_LOGITS, 128, 192>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 192>();
-    set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 192>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_LOGITS, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 192>(); set_lds_mm<1, 1, EPI_F32, 128, 192>();
@@ -1253,16 +1208,14 @@ void gemm_setup() {
                               (int)mm_lds_bytes<128, 192>());
     (void)hipFuncSetAttribute((const void*)gemm_mm_group_kernel<128>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)mm_lds_bytes<128, 128>());
-    set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>(); set_lds_mm<0, 0, EPI_BIAS_RESID, 128, 128>();
-    set_lds_mm<0, 0, EPI_BIAS_RESID_F32, 128, 128>();
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 128>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 128>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 128>();
     set_lds_mm<0, 1, EPI_F32, 128, 128>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 128>();
     set_lds_mm<0, 1, EPI_PARTIAL, 128, 128>(); set_lds_mm<1, 1, EPI_F32, 128, 128>();
     set_lds_mm<1, 1, EPI_PARTIAL, 128, 128>();
     // allow the dynamic LDS size (above the 64 KiB default) for every instantiation
 #define SETUP_T(T)                                                                                          \
-    set_lds_all<T, 0, 0, EPI_BIAS_T>(); set_lds_all<T, 0, 0, EPI_BIAS_RESID>();                        \
-    set_lds_all<T, 0, 0, EPI_BIAS_RESID_F32>();                                                             \
+    set_lds_all<T, 0, 0, EPI_BIAS_T>();                                                                     \
     set_lds_all<T, 0, 0, EPI_BIAS_GELU>(); set_lds_all<T, 0, 1, EPI_GELU_BWD>();                           \
     set_lds_all<T, 0, 1, EPI_F32>(); set_lds_all<T, 0, 1, EPI_BIAS_T>(); set_lds_all<T, 1, 1, EPI_F32>(); \
     set_lds_all<T, 1, 1, EPI_PARTIAL>(); set_lds_all<T, 0, 1, EPI_PARTIAL>();

@@ -168,6 +168,7 @@ struct Plan {
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
     size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, Dbuf;
+    size_t yproj;          // a projection's output with its bias, before the residual add
     // output gradients that feed products: per layer in the bf16 modes (kept for the grouped
     // weight-gradient launch at the end of the backward), one shared buffer in fp32 mode
     std::vector<size_t> du, dqkv;
@@ -213,6 +214,7 @@ Plan make_plan(const gpt2_config* c) {
         P.u.push_back(take(BT * F * es));
         P.a.push_back(take(BT * F * es));
     }
+    P.yproj = take(BT * C * es);
     P.hf = take(BT * C * es);
     P.meanf = take(BT * 4);
     P.rstdf = take(BT * 4);
@@ -618,19 +620,18 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
     const gpt2_config& c = h->cfg;
     const int BT = B * T, C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
     const int bf = h->bf16, r16 = h->res16;
-    // residual add: in the storage type, or into the fp32 stream from bf16 operands
-    const int epi_res = (bf && !r16) ? EPI_BIAS_RESID_F32 : EPI_BIAS_RESID;
     const Layout& L = h->L;
     const Plan& P = h->P;
     float* prm = h->params();
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
+    char* y = h->at<char>(P.yproj);
     TRY(run(h, "embed_fwd", [&] { return embed_forward(idx, prm + L.wte, prm + L.wpe, h->at<char>(P.x_in[0]), B, T, C, r16, s); }));
+    TRY(run(h, "layernorm_fwd", [&] {
+        return layernorm_forward(h->at<char>(P.x_in[0]), prm + L.ln1_w[0], prm + L.ln1_b[0], h->at<char>(P.h1[0]),
+                                 h->at<float>(P.mean1[0]), h->at<float>(P.rstd1[0]), BT, C, r16, bf, s);
+    }));
     for (int l = 0; l < c.n_layer; ++l) {
-        TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
-                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), BT, C, r16, bf, s);
-        }));
         GemmDesc g;
         g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
         g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 0;
@@ -640,16 +641,17 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         TRY(run(h, "attn_fwd", [&] {
             return attention_forward(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), h->at<float>(P.lse[l]), B, T, H, hs, bf, s);
         }));
+        // x_mid = x_in + (y Wo^T + bo), then ln_2
         g = GemmDesc();
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = BT; g.N = C; g.K = C;
-        g.epi = epi_res; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
-        g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
+        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_o[l];
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
-                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), BT, C, r16, bf, s);
+            return add_layernorm_forward(h->at<char>(P.x_in[l]), y, h->at<char>(P.x_mid[l]), prm + L.ln2_w[l],
+                                         prm + L.ln2_b[l], h->at<char>(P.h2[l]), h->at<float>(P.mean2[l]),
+                                         h->at<float>(P.rstd2[l]), BT, C, r16, bf, s);
         }));
         g = GemmDesc();
         g.A = h->at<char>(P.h2[l]); g.lda = C;
@@ -657,18 +659,22 @@ static int forward_trunk(gpt2_t* h, int B, int T) {
         g.M = BT; g.N = F; g.K = C;
         g.epi = EPI_BIAS_GELU; g.C = h->at<char>(P.u[l]); g.C2 = h->at<char>(P.a[l]); g.ldc = F; g.bias = prm + L.b_fc[l];
         TRY(run(h, "gemm_fc", [&] { return gemm(g, bf, s); }));
+        // x_out = x_mid + (a Wpr^T + bpr), then the next layer's ln_1 (or ln_f)
         g = GemmDesc();
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = BT; g.N = C; g.K = F;
-        g.epi = epi_res; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
-        g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
+        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_pr[l];
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
+        const bool last = l + 1 == c.n_layer;
+        TRY(run(h, "layernorm_fwd", [&] {
+            return add_layernorm_forward(h->at<char>(P.x_mid[l]), y, h->at<char>(P.x_in[l + 1]),
+                                         prm + (last ? L.lnf_w : L.ln1_w[l + 1]), prm + (last ? L.lnf_b : L.ln1_b[l + 1]),
+                                         h->at<char>(last ? P.hf : P.h1[l + 1]),
+                                         h->at<float>(last ? P.meanf : P.mean1[l + 1]),
+                                         h->at<float>(last ? P.rstdf : P.rstd1[l + 1]), BT, C, r16, bf, s);
+        }));
     }
-    TRY(run(h, "layernorm_fwd", [&] {
-        return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
-                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), BT, C, r16, bf, s);
-    }));
     {
         GemmDesc g;
         g.A = h->at<char>(P.hf); g.lda = C;
@@ -822,23 +828,23 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
     if (d_next && !d_uniform) return set_error(GPT2_EINVAL, "drawing the next token needs d_uniform");
     const int C = c.n_embd, F = c.mlp_hidden, Vp = c.padded_vocab_size, H = c.n_head, hs = C / H;
     const int bf = h->bf16, r16 = h->res16;
-    const int epi_res = (bf && !r16) ? EPI_BIAS_RESID_F32 : EPI_BIAS_RESID;
     const size_t es = bf ? 2 : 4;
     const Layout& L = h->L;
     const Plan& P = h->P;
     float* prm = h->params();
     hipStream_t s = h->stream;
     int32_t* idx = h->at<int32_t>(P.idx);
+    char* y = h->at<char>(P.yproj);
     HIPTRY(hipMemcpyAsync(idx, d_tokens, (size_t)B * 4, hipMemcpyDeviceToDevice, s), "copy tokens");
     h->dec_B = 0;   // until this step has been enqueued completely
     TRY(run(h, "embed_fwd", [&] {
         return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, r16, s);
     }));
+    TRY(run(h, "layernorm_fwd", [&] {
+        return layernorm_forward(h->at<char>(P.x_in[0]), prm + L.ln1_w[0], prm + L.ln1_b[0], h->at<char>(P.h1[0]),
+                                 h->at<float>(P.mean1[0]), h->at<float>(P.rstd1[0]), B, C, r16, bf, s);
+    }));
     for (int l = 0; l < c.n_layer; ++l) {
-        TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<char>(P.x_in[l]), prm + L.ln1_w[l], prm + L.ln1_b[l], h->at<char>(P.h1[l]),
-                                     h->at<float>(P.mean1[l]), h->at<float>(P.rstd1[l]), B, C, r16, bf, s);
-        }));
         GemmDesc g;
         g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
         g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 0;
@@ -853,12 +859,12 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.att[l]); g.lda = C;
         g.B = h->wop(L.w_o[l]); g.ldb = C;
         g.M = B; g.N = C; g.K = C;
-        g.epi = epi_res; g.C = h->at<char>(P.x_mid[l]); g.ldc = C; g.bias = prm + L.b_o[l];
-        g.resid = h->at<char>(P.x_in[l]); g.ldr = C;
+        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_o[l];
         TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "layernorm_fwd", [&] {
-            return layernorm_forward(h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l], h->at<char>(P.h2[l]),
-                                     h->at<float>(P.mean2[l]), h->at<float>(P.rstd2[l]), B, C, r16, bf, s);
+            return add_layernorm_forward(h->at<char>(P.x_in[l]), y, h->at<char>(P.x_mid[l]), prm + L.ln2_w[l],
+                                         prm + L.ln2_b[l], h->at<char>(P.h2[l]), h->at<float>(P.mean2[l]),
+                                         h->at<float>(P.rstd2[l]), B, C, r16, bf, s);
         }));
         g = GemmDesc();
         g.A = h->at<char>(P.h2[l]); g.lda = C;
@@ -870,14 +876,17 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.A = h->at<char>(P.a[l]); g.lda = F;
         g.B = h->wop(L.w_pr[l]); g.ldb = F;
         g.M = B; g.N = C; g.K = F;
-        g.epi = epi_res; g.C = h->at<char>(P.x_in[l + 1]); g.ldc = C; g.bias = prm + L.b_pr[l];
-        g.resid = h->at<char>(P.x_mid[l]); g.ldr = C;
+        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_pr[l];
         TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
+        const bool last = l + 1 == c.n_layer;
+        TRY(run(h, "layernorm_fwd", [&] {
+            return add_layernorm_forward(h->at<char>(P.x_mid[l]), y, h->at<char>(P.x_in[l + 1]),
+                                         prm + (last ? L.lnf_w : L.ln1_w[l + 1]), prm + (last ? L.lnf_b : L.ln1_b[l + 1]),
+                                         h->at<char>(last ? P.hf : P.h1[l + 1]),
+                                         h->at<float>(last ? P.meanf : P.mean1[l + 1]),
+                                         h->at<float>(last ? P.rstdf : P.rstd1[l + 1]), B, C, r16, bf, s);
+        }));
     }
-    TRY(run(h, "layernorm_fwd", [&] {
-        return layernorm_forward(h->at<char>(P.x_in[c.n_layer]), prm + L.lnf_w, prm + L.lnf_b, h->at<char>(P.hf),
-                                 h->at<float>(P.meanf), h->at<float>(P.rstdf), B, C, r16, bf, s);
-    }));
     {
         GemmDesc g;
         g.A = h->at<char>(P.hf); g.lda = C;

@@ -9,7 +9,6 @@ namespace gpt2k {
 // ------------------------------------------------------------------ GEMM
 enum Epi {
     EPI_BIAS_T = 0,          // C(T)   = alpha*acc + bias[n]           (bias may be null)
-    EPI_BIAS_RESID = 1,      // C(T)   = resid(T)[m][n] + acc + bias[n]   (residual stream in the storage type)
     EPI_BIAS_GELU = 2,       // C(T)   = u = acc + bias[n];  C2(T) = gelu_tanh(u)
     EPI_GELU_BWD = 3,        // C(T)   = acc * gelu_tanh'(aux[m][n])
     EPI_F32 = 4,             // C(f32) = (beta ? C : 0) + alpha*acc
@@ -17,7 +16,6 @@ enum Epi {
     EPI_LOGITS = 6,          // C(bf16) = alpha*acc + bias[n], and C2 (fp32 pairs) = for every row m
                              // and 192-column tile t: (max, sum exp(z - max)) of that row's
                              // bf16-rounded outputs in the tile, at C2[2 * (m * tiles + t)]
-    EPI_BIAS_RESID_F32 = 7,  // C(f32) = resid(f32)[m][n] + acc + bias[n]  (fp32 residual stream, bf16 operands)
 };
 
 struct GemmDesc {
@@ -28,7 +26,6 @@ struct GemmDesc {
     void* C = nullptr; int64_t ldc = 0;
     void* C2 = nullptr;
     const float* bias = nullptr;
-    const void* resid = nullptr; int64_t ldr = 0;   // storage type (fp32 for EPI_BIAS_RESID_F32)
     const void* aux = nullptr; int64_t ldaux = 0;
     float alpha = 1.f;
     int beta = 0;
@@ -78,6 +75,12 @@ hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe,
 // x_bf16 (the bf16 residual stream) else fp32; out is bf16 if out_bf16 else fp32.
 hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
                              float* rstd, int rows, int C, int x_bf16, int out_bf16, hipStream_t s);
+// Residual add and LayerNorm: x_new = x_old + y (fp32 add, stored in the residual type: bf16
+// if x_bf16 else fp32), out = LayerNorm(x_new) with mean, rstd saved; y and out in the operand
+// type (bf16 if op_bf16 else fp32).
+hipError_t add_layernorm_forward(const void* x_old, const void* y, void* x_new, const float* w, const float* b,
+                                 void* out, float* mean, float* rstd, int rows, int C, int x_bf16, int op_bf16,
+                                 hipStream_t s);
 // LayerNorm backward: dres = (accumulate ? dres : 0) + dx ; partial[blk][0:C] = sum dh*xhat,
 // [C:2C] = sum dh, [2C:3C] = sum of the incoming dres (zero without accumulate) over the
 // block's rows. dh is bf16 if dh_bf16 else fp32; x and dres are bf16 if res_bf16 else fp32;

@@ -15,6 +15,12 @@ template <> DEV void store4<bf16>(bf16* p, float a, float b, float c, float d) {
     v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
     *(bf16x4*)p = v;
 }
+// 4 fp32 values as they read back after a store in type T (rounded to bf16 for bf16)
+template <typename T> DEV float4 load4_rounded(float a, float b, float c, float d);
+template <> DEV float4 load4_rounded<float>(float a, float b, float c, float d) { return make_float4(a, b, c, d); }
+template <> DEV float4 load4_rounded<bf16>(float a, float b, float c, float d) {
+    return make_float4((float)(bf16)a, (float)(bf16)b, (float)(bf16)c, (float)(bf16)d);
+}
 template <typename T> DEV float4 load4(const T* p);
 template <> DEV float4 load4<float>(const float* p) { return *(const float4*)p; }
 template <> DEV float4 load4<bf16>(const bf16* p) {
@@ -118,6 +124,87 @@ static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const TX* x, con
     else LNF(8);
 #undef LNF
     return hipGetLastError();
+}
+
+// Residual add fused with the LayerNorm that follows it: x_new = x_old + y, then the LayerNorm of
+// x_new. y is the projection's output with its bias (bf16 in the bf16 modes: the autocast recipe
+// rounds a product's output to bf16 before the fp32 residual add); the add is done in fp32 and
+// x_new is stored in the residual stream's type TX, and the statistics are taken on the stored
+// value. One wave per row, the row in registers.
+template <typename TX, typename TY, typename TO, int NV>
+__global__ void __launch_bounds__(256) add_layernorm_forward_kernel(
+    const TX* __restrict__ x_old, const TY* __restrict__ y, TX* __restrict__ x_new, const float* __restrict__ w,
+    const float* __restrict__ b, TO* __restrict__ out, float* __restrict__ mean, float* __restrict__ rstd, int rows,
+    int C) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int nv = C >> 2;
+    const int64_t ro = (int64_t)row * C;
+    float4 v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + 64 * j;
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < nv) {
+            const float4 a = load4<TX>(x_old + ro + 4 * c), d = load4<TY>(y + ro + 4 * c);
+            store4<TX>(x_new + ro + 4 * c, a.x + d.x, a.y + d.y, a.z + d.z, a.w + d.w);
+            v[j] = load4_rounded<TX>(a.x + d.x, a.y + d.y, a.z + d.z, a.w + d.w);
+        }
+        s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+    }
+    const float mu = wave_sum(s) / (float)C;
+    float s2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nv) {
+            const float a = v[j].x - mu, bb = v[j].y - mu, cc = v[j].z - mu, d = v[j].w - mu;
+            s2 += (a * a + bb * bb) + (cc * cc + d * d);
+        }
+    }
+    const float r = 1.0f / sqrtf(wave_sum(s2) / (float)C + LN_EPS);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nv) {
+            const float4 ww = ((const float4*)w)[c], bb = ((const float4*)b)[c];
+            store4<TO>(out + ro + 4 * c, (v[j].x - mu) * r * ww.x + bb.x, (v[j].y - mu) * r * ww.y + bb.y,
+                       (v[j].z - mu) * r * ww.z + bb.z, (v[j].w - mu) * r * ww.w + bb.w);
+        }
+    }
+    if (lane == 0) { mean[row] = mu; rstd[row] = r; }
+}
+
+template <typename TX, typename TY, typename TO>
+static hipError_t add_ln_launch(int nv4, dim3 g, hipStream_t s, const TX* xo, const TY* y, TX* xn, const float* w,
+                                const float* b, TO* out, float* mean, float* rstd, int rows, int C) {
+#define ALN(NV) hipLaunchKernelGGL((add_layernorm_forward_kernel<TX, TY, TO, NV>), g, dim3(256), 0, s, xo, y, xn, w, b, \
+                                   out, mean, rstd, rows, C)
+    if (nv4 <= 64) ALN(1);
+    else if (nv4 <= 128) ALN(2);
+    else if (nv4 <= 192) ALN(3);
+    else if (nv4 <= 256) ALN(4);
+    else ALN(8);
+#undef ALN
+    return hipGetLastError();
+}
+
+hipError_t add_layernorm_forward(const void* x_old, const void* y, void* x_new, const float* w, const float* b,
+                                 void* out, float* mean, float* rstd, int rows, int C, int x_bf16, int op_bf16,
+                                 hipStream_t s) {
+    if (C > 4 * 64 * LN_NV || (C & 3)) return hipErrorInvalidValue;
+    if (x_bf16 && !op_bf16) return hipErrorInvalidValue;
+    const dim3 g((rows + 3) / 4);
+    if (x_bf16)
+        return add_ln_launch<bf16, bf16, bf16>(C / 4, g, s, (const bf16*)x_old, (const bf16*)y, (bf16*)x_new, w, b,
+                                               (bf16*)out, mean, rstd, rows, C);
+    if (op_bf16)
+        return add_ln_launch<float, bf16, bf16>(C / 4, g, s, (const float*)x_old, (const bf16*)y, (float*)x_new, w, b,
+                                                (bf16*)out, mean, rstd, rows, C);
+    return add_ln_launch<float, float, float>(C / 4, g, s, (const float*)x_old, (const float*)y, (float*)x_new, w, b,
+                                              (float*)out, mean, rstd, rows, C);
 }
 
 // bf16 rows of C = 256 * NC: one half-wave (32 lanes) per row, NC 16-byte chunks per lane, so
