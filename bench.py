@@ -168,12 +168,17 @@ def traffic_for(kernel_class):
 TRAFFIC_CLASSES = {
     "gemm_fc": ("gemm_mm_kernel<0, 0, 2,", None),
     "gemm_lm_head": ("gemm_mm_kernel<0, 0, 6,", None),
-    "gemm_qkv": ("gemm_mm_kernel<0, 0, 0,", "min"),
+    "gemm_qkv": ("gemm_mm_kernel<0, 0, 0,", "max"),
     "gemm_lm_head_dw": ("gemm_mm_kernel<1, 1, 4,", None),
+    "gemm_dw": ("gemm_mm_group_kernel", None),
     "cross_entropy": ("cross_entropy_tiled_kernel", None),
     "adamw": ("adamw_kernel", None),
     "attn_fwd": ("attn_fwd_ts_kernel", None),
-    "layernorm_fwd": ("layernorm_forward_half_kernel", None),
+    "layernorm_fwd": ("add_layernorm_forward_kernel", None),
+    "layernorm_bwd": ("layernorm_backward_kernel", None),
+    # the block input gradients: every GELU-derivative launch and every plain input-gradient
+    # launch except the lm_head's (the first one after each cross-entropy launch)
+    "gemm_dx": (("gemm_mm_kernel<0, 1, 3,", "gemm_mm_kernel<0, 1, 0,"), "dx_blocks"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -210,6 +215,20 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
     sf, sw = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
 
     def select(per, meta, name, grid_rule):
+        if grid_rule == "dx_blocks":
+            out, after_ce = [], False
+            for d in sorted(per):
+                k = meta[d][0]
+                if "cross_entropy_tiled_kernel" in k:
+                    after_ce = True
+                elif name[1] in k:
+                    if after_ce:
+                        after_ce = False   # the lm_head input gradient
+                    else:
+                        out.append(d)
+                elif name[0] in k:
+                    out.append(d)
+            return out
         ds = [d for d in per if name in meta[d][0]]
         if grid_rule and ds:
             grids = sorted({meta[d][1] for d in ds})
@@ -235,7 +254,78 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
     print(json.dumps(rec, indent=1))
 
 
-def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=True):
+def symbol_costs(w, B, n_params, n_decay):
+    """Algorithmic work per step of each kernel symbol of the bf16 training step (fp32 residual
+    stream) at shapes where every product takes the LDS-streamed path: (name pattern, what it
+    runs, 'flop' or 'byte', total per step). Products sharing one instantiation are summed."""
+    BT, C, F, Vp, L, T, H = B * w.seq_len, w.n_embd, w.mlp_hidden, w.padded_vocab_size, w.n_layer, w.seq_len, w.n_head
+    af = 2 * 2 * B * H * (T * (T + 1) / 2) * (C // H) * L           # attention forward, causal half
+    cc = class_costs(w, B, n_params, n_decay)
+    return [
+        ("gemm_mm_group_kernel", "weight gradients of every block (grouped)", "flop",
+         2 * BT * C * (3 * C + C + F + F) * L),
+        ("gemm_mm_kernel<0, 1, 0,", "input gradients: lm_head, c_fc, attn c_proj, c_attn", "flop",
+         2 * BT * C * Vp + 2 * BT * C * (F + C + 3 * C) * L),
+        ("gemm_mm_kernel<0, 1, 3,", "mlp c_proj input gradient with GELU'", "flop", 2 * BT * F * C * L),
+        ("gemm_mm_kernel<0, 0, 0,", "forward: c_attn, attn c_proj, mlp c_proj", "flop", 2 * BT * C * (3 * C + C + F) * L),
+        ("gemm_mm_kernel<0, 0, 2,", "forward: c_fc with GELU", "flop", 2 * BT * F * C * L),
+        ("gemm_mm_kernel<0, 0, 6,", "lm_head logits + softmax statistics", "flop", 2 * BT * Vp * C),
+        ("gemm_mm_kernel<1, 1, 4,", "lm_head weight gradient", "flop", 2 * BT * Vp * C),
+        ("attn_fwd_ts_kernel", "attention forward", "flop", af),
+        # the backward's algorithmic work (dP, dV, dK, dQ and one recompute of S: 2.5x the forward),
+        # split as the two kernels divide it (each also recomputes S and dP, not counted twice)
+        ("attn_bwd_dkv_ts_kernel", "attention dK, dV", "flop", 1.5 * af),
+        ("attn_bwd_dq_ts_kernel", "attention dQ", "flop", 1.0 * af),
+        ("add_layernorm_forward_kernel", "residual add + LayerNorm forward (2L calls)", "byte",
+         2 * L * (BT * C * (2 * 4 + 2 * 2) + 8 * BT)),
+        ("layernorm_forward_kernel", "first LayerNorm forward", "byte", BT * C * (4 + 2) + 8 * BT),
+        ("layernorm_backward_kernel", "LayerNorm backward", "byte", cc["layernorm_bwd"][1]),
+        ("cross_entropy_tiled_kernel", "softmax cross-entropy", "byte", cc["cross_entropy"][1]),
+        ("adamw_kernel", "AdamW", "byte", cc["adamw"][1]),
+        ("norm_partial_kernel", "grad norm", "byte", cc["grad_norm"][1]),
+        ("embed_forward_kernel", "embedding forward", "byte", cc["embed_fwd"][1]),
+    ]
+
+
+def profile_table(stats_csv, steps):
+    """Markdown table of a rocprofv3 --stats kernel summary of `bench.py` (default workload): per
+    kernel symbol its time per step and, where its algorithmic work is known, its rate and
+    fraction of the MI355X peak (FLOP: dense bf16 MFMA; bytes: HBM)."""
+    import csv
+
+    import synthetic
+    w = synthetic.workload("gpt2_step")
+    n_params = 124475904
+    n_decay = 124354560
+    costs = symbol_costs(w, w.batch, n_params, n_decay)
+    rows = list(csv.DictReader(open(stats_csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows) / 1e6 / steps
+    print(f"| kernel symbol | what it runs | calls | avg us | ms/step | % of kernel time | work/step | rate | "
+          f"frac of peak |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        ms = float(r["TotalDurationNs"]) / 1e6 / steps
+        if ms < 0.004:
+            continue
+        name = r["Name"]
+        what, work, rate, frac = "", "", "", ""
+        for pat, desc, kind, tot in costs:
+            if pat in name:
+                what = desc
+                if kind == "flop":
+                    rt = tot / (ms / 1e3)
+                    work, rate, frac = f"{tot / 1e12:.3f} TFLOP", f"{rt / 1e12:.0f} TFLOP/s", f"{rt / PEAK_BF16:.3f}"
+                else:
+                    rt = tot / (ms / 1e3)
+                    work, rate, frac = f"{tot / 1e9:.3f} GB", f"{rt / 1e9:.0f} GB/s", f"{rt / PEAK_HBM:.3f}"
+                break
+        short = name if len(name) <= 70 else name[:67] + "..."
+        print(f"| `{short}` | {what} | {int(r['Calls'])} | {float(r['AverageNs']) / 1e3:.1f} | {ms:.3f} | "
+              f"{100 * ms / total:.1f} | {work} | {rate} | {frac} |")
+    print(f"\nTotal kernel time per step: {total:.2f} ms ({steps} steps in the trace).")
+
+
+def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=True, graph_steps=0):
     """Create a handle for workload w in `dtype`, run `warmup` untimed steps, a per-class timing
     pass, then `steps` timed steps (the dominant class keeps its HIP events). Returns a dict of
     the measurements; the handle is destroyed before returning."""
@@ -339,6 +429,28 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
                 "traffic": traffic_for(dominant) if not res16 else None,
                 "launch_ms": round(ms / n, 4), "launches_per_step": n / steps, "per_launch": per_launch,
                 "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
+    graph = None
+    if graph_steps and args.mode == "train":
+        # the same step captured once in a HIP graph and replayed (the AdamW step count and
+        # learning rate are the captured values on every replay: the same kernels and bytes)
+        orig = st.stream
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            G.gpt2_set_stream(h, torch.cuda.current_stream().cuda_stream)
+            step()
+        G.gpt2_set_stream(h, orig)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(graph_steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ge = time.perf_counter() - t1
+        graph = {"ms_per_step": round(ge / graph_steps * 1e3, 3), "steps": graph_steps,
+                 "value": round(B * T * k / (ge / graph_steps), 1)}
+        del g
     kk = k if args.mode == "train" else 1
     loss = float(d_loss[:kk].sum().item()) / kk if args.mode != "decode" else None
     tokens = B * T * kk if args.mode != "decode" else B
@@ -352,7 +464,7 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
     del st
     torch.cuda.synchronize()
     return {"el": el, "ms_step": el / steps * 1e3, "value": tokens / (el / steps), "loss": loss,
-            "roofline": roof, "kernels": kernels, "n_params": n_params, "k": kk}
+            "roofline": roof, "kernels": kernels, "n_params": n_params, "k": kk, "graph": graph}
 
 
 def main():
@@ -372,13 +484,21 @@ def main():
                          "decoding steps with top-50 sampling of the workload's B sequences after an "
                          "8-token prompt (one step = one new token per sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the short timing of the same step captured in a HIP graph and replayed")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
                     help="after timing, run device copies of BYTES bytes (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="build profiles/traffic.json from two rocprofv3 --pmc counter traces and exit")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--profile-table", nargs=2, metavar=("STATS_CSV", "STEPS"),
+                    help="print the per-symbol roofline table of a rocprofv3 --stats kernel summary of the "
+                         "default benchmark (STEPS: training steps in the trace) and exit")
     args = ap.parse_args()
+    if args.profile_table:
+        profile_table(args.profile_table[0], int(args.profile_table[1]))
+        return
     if args.traffic_from:
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_bytes,
                      os.path.join(ROOT, "profiles", "traffic.json"))
@@ -394,7 +514,8 @@ def main():
 
     w = synthetic.workload(args.workload)
     B, T = w.batch, w.seq_len
-    r = run_workload(args, w, args.dtype, args.steps, args.warmup, kernel_timing=not args.no_kernel_timing)
+    r = run_workload(args, w, args.dtype, args.steps, args.warmup, kernel_timing=not args.no_kernel_timing,
+                     graph_steps=0 if args.no_graph else max(5, args.steps // 2))
     k = r["k"]
     fpt = model_flops_per_token(w, r["n_params"], args.mode)
     mfu = r["value"] * fpt / PEAK_BF16
@@ -426,6 +547,9 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    if r["graph"]:
+        out["hip_graph"] = dict(r["graph"], note="the timed step captured once in a HIP graph and replayed; "
+                                                 "`value` is the eager launch sequence")
     if (args.mode == "train" and args.dtype == "bf16" and w.dtype == "bf16" and not args.no_variant):
         # the narrower-storage variant, timed briefly on a handle of its own (never `value`)
         v = run_workload(args, w, "bf16_res16", max(5, args.steps // 2), 2, kernel_timing=False, roofline=False)

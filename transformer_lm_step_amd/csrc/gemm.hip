@@ -54,14 +54,20 @@ constexpr size_t lds_bytes() { return 2 * (size_t)(BM + BN) * ROWB; }
 #ifndef GEMM_TILE_ORDER
 #define GEMM_TILE_ORDER 0
 #endif
-// workgroup id -> (tile_m, tile_n): XCD-contiguous ranges, then groups of GROUP_M tile rows
-DEV void tile_coords(int pid, int nwg, int num_m, int num_n, int& tm, int& tn) {
-    if (GEMM_TILE_ORDER == 1) { tm = pid % num_m; tn = pid / num_m; return; }
+// Workgroups are dealt to the 8 XCDs round-robin by id (id & 7), the (id >> 3)-th on its XCD.
+// This renumbering gives each XCD a contiguous range of logical tile numbers.
+DEV int xcd_logical(int pid, int nwg) {
     const int xcd = pid & 7, slot = pid >> 3;
     const int per = (nwg + 7) >> 3;
     int tall = nwg & 7;
     if (tall == 0) tall = 8;
-    int logical = (xcd < tall) ? xcd * per + slot : tall * per + (xcd - tall) * (per - 1) + slot;
+    return (xcd < tall) ? xcd * per + slot : tall * per + (xcd - tall) * (per - 1) + slot;
+}
+// workgroup id -> (tile_m, tile_n): XCD-contiguous ranges (unless the caller already numbered
+// the tiles that way: remap = false), then groups of GROUP_M tile rows
+DEV void tile_coords(int pid, int nwg, int num_m, int num_n, int& tm, int& tn, bool remap = true) {
+    if (GEMM_TILE_ORDER == 1) { tm = pid % num_m; tn = pid / num_m; return; }
+    const int logical = remap ? xcd_logical(pid, nwg) : pid;
     if (num_n <= 8) {
         // few column tiles: the tiles of one row panel are consecutive, so the blocks that share
         // an A panel start (and stream its K tiles) together
@@ -718,14 +724,14 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
 // split `split` (a plain launch passes blockIdx.x, gridDim.x, blockIdx.y; a grouped launch its
 // product's own numbering).
 template <int ALAY, int BLAY, int EPI, int BM, int BN, bool ROWSUM>
-DEV void mm_tile(const GemmArgs& p, int pid, int nwg, int split, char* smem) {
+DEV void mm_tile(const GemmArgs& p, int pid, int nwg, int split, char* smem, bool remap = true) {
     constexpr int STAGE = (BM + BN) * 128;
     constexpr int TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), wm = wave >> 1, wn = wave & 1;
     const int num_m = (p.M + BM - 1) / BM, num_n = (p.N + BN - 1) / BN;
     int tm, tn;
-    tile_coords(pid, nwg, num_m, num_n, tm, tn);
+    tile_coords(pid, nwg, num_m, num_n, tm, tn, remap);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = split * p.ksplit_len;
     const int nt = min(p.ksplit_len, p.K - kbeg) / MM_BK;
@@ -818,14 +824,16 @@ __global__ void __launch_bounds__(GTHREADS, ROWSUM ? 2 : 1) gemm_mm_kernel(GemmA
     mm_tile<ALAY, BLAY, EPI, BM, BN, ROWSUM>(p, blockIdx.x, gridDim.x, blockIdx.y, smem);
 }
 
-// Grouped weight-gradient products: workgroup w runs tile w - tile0 of the product whose range
-// [tile0, tile0 + ntiles) holds w (found by a binary search over the sorted ranges); every
-// product takes the whole K, so there are no split-K partials.
+// Grouped weight-gradient products: the launch's tiles are numbered XCD-first over the whole
+// product list (each XCD takes a contiguous run of whole products, so a product's operand panels
+// are fetched into one L2 instead of all eight); logical tile w runs tile w - tile0 of the
+// product whose range [tile0, tile0 + ntiles) holds it (binary search over the sorted ranges).
+// Every product takes the whole K, so there are no split-K partials.
 template <int BN>
 __global__ void __launch_bounds__(GTHREADS, 2) gemm_mm_group_kernel(GemmArgs base, const GroupProb* __restrict__ probs,
                                                                     int nprob) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int w = blockIdx.x;
+    const int w = xcd_logical(blockIdx.x, gridDim.x);
     int lo = 0, hi = nprob - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -838,7 +846,7 @@ __global__ void __launch_bounds__(GTHREADS, 2) gemm_mm_group_kernel(GemmArgs bas
     p.M = g.M; p.N = g.N;
     p.rowsum_part = nullptr;
     p.rowsum_out = g.rowsum;
-    mm_tile<1, 1, EPI_F32, 128, BN, true>(p, w - g.tile0, g.ntiles, 0, smem);
+    mm_tile<1, 1, EPI_F32, 128, BN, true>(p, w - g.tile0, g.ntiles, 0, smem, false);
 }
 
 template <int BM, int BN>
