@@ -641,39 +641,57 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
         }
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
+        // Every fragment of the chunk is read before it is needed: the V^T reads complete under
+        // the score products and the softmax instead of stalling each output product in turn.
+        // (Two of them go out with the K reads, the rest after the score products: the LDS
+        // wait counter tracks at most 15 reads in flight, and the products wait only for K.)
+        bf16x8 kf[4][2], vf[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) kf[kb][ks] = ts_nat(sK, kb * 16, ks, lane);
+#pragma unroll
+        for (int d = 0; d < 2; ++d) vf[0][d] = ts_tr(sV, d * 16, 0, 16, lane);
         floatx4 s[4][QB];
         __builtin_amdgcn_s_setprio(1);  // MFMA phase first; other waves run their softmax meanwhile
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // k step outermost, so that the two products into one accumulator are four apart
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 kf = ts_nat(sK, kb * 16, ks, lane);
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) mma8(s[kb][qb], kf, qf[qb][ks]);
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) mma8(s[kb][qb], kf[kb][ks], qf[qb][ks]);
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int d = 2; d < 4; ++d) vf[0][d] = ts_tr(sV, d * 16, 0, 16, lane);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) vf[1][d] = ts_tr(sV, d * 16, 32, 48, lane);
+        // online softmax in the log2 domain on raw scores: max first, then one fma + exp2; the
+        // causal and sequence-end mask only in the chunks that reach the diagonal or the end
+        // (one wave-uniform branch around selects)
+        if ((k0 + 63 > qw0) || (k0 + 64 > T_)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int lim = min(qw0 + qb * 16 + col, T_ - 1) - k0 - g * 4;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        s[kb][qb][i] = kb * 16 + i > lim ? -INFINITY : s[kb][qb][i];
             }
         }
-        __builtin_amdgcn_s_setprio(0);
-        // online softmax in the log2 domain on raw scores: max first, then one fma + exp2
-        const bool need_mask = (k0 + 63 > qw0) || (k0 + 64 > T_);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            const int q = qw0 + qb * 16 + col;
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = s[kb][qb][i];
-                    if (need_mask) {
-                        const int key = k0 + kb * 16 + g * 4 + i;
-                        if (key > q || key >= T_) v = -INFINITY;
-                    }
-                    s[kb][qb][i] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = group4_max(mx) * sc;
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+            mx = group4_max_swap(mx) * sc;
             // Lazy rescaling: the reference maximum moves (and o and the denominators are
             // rescaled) only when some query of the wave has a score more than 2^8 above it,
             // so the exponentials stay <= 256 and the normalization o / l, which shares the
@@ -702,11 +720,9 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
                 mma8(lacc[qb], ones, pf[qb]);
             }
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const bf16x8 vf = ts_tr(sV, d * 16, 32 * st, 32 * st + 16, lane);
+            for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) mma8(o[d][qb], vf, pf[qb]);
-            }
+                for (int qb = 0; qb < QB; ++qb) mma8(o[d][qb], vf[st][d], pf[qb]);
         }
         __builtin_amdgcn_s_setprio(0);
     }

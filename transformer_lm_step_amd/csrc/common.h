@@ -82,6 +82,16 @@ DEV float group4_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 32));
     return v;
 }
+// The same maximum from the gfx950 lane-swap instructions, without the LDS crossbar: the swap
+// of the upper half-wave of one copy with the lower half-wave of another leaves, in the two
+// results, the values of lanes l & ~32 and l | 32 (then l & ~16 and l | 16 for the swap of
+// odd with even 16-lane rows).
+DEV float group4_max_swap(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 
 // Block-wide sum for a block of NT threads (NT multiple of 64); every thread gets the result.
 template <int NT>
@@ -153,8 +163,16 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_t;
 typedef __attribute__((address_space(3))) char* lds_char_t;
 
-// s_waitcnt immediate waiting for vmcnt == 0 only (expcnt, lgkmcnt at their maxima)
+// s_waitcnt immediates: vmcnt == 0 only (expcnt, lgkmcnt at their maxima); lgkmcnt == 0 only
+// (vmcnt, expcnt at their maxima); both. Waits issued through the builtin are seen by the
+// compiler's own wait tracking: one in inline asm is not, and a kernel whose scalar argument
+// loads are first used after a loop then gets lgkmcnt(0) before every LDS-fed instruction in
+// it (the compiler cannot order LDS returns against scalar loads it believes in flight). The
+// barriers below issue both: the builtin for the tracking, the asm copy next to s_barrier so
+// that nothing the compiler moves in between escapes the wait.
 constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+constexpr int kWaitVm0Lgkm0 = 0x7 << 4;
 
 // LDS byte address of a shared-memory pointer
 DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_char_t)(p); }
@@ -187,13 +205,16 @@ DEV void dma4(const void* base, uint32_t voff, uint32_t lds) {
 // loads issued for later tiles). Afterwards every wave's loads issued before it have landed
 // and every wave's earlier LDS reads have completed.
 DEV void dma_wait_barrier() {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // Barrier for LDS traffic only: this wave's LDS accesses are complete, then every wave meets.
 // Unlike __syncthreads() it does not wait for the wave's global stores to complete, so a
 // workgroup can stage the next part of its output in LDS while earlier stores drain.
-DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+DEV void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Two transposing LDS reads (ds_read_b64_tr_b16) joined into one 8-value fragment. Within
 // each 16-lane group the instruction gives lane i, as its j-th value, element (i % 4) of the
