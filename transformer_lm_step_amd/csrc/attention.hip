@@ -572,6 +572,19 @@ DEV bf16x8 ts_tr(const char* t, int cb, int r0, int r1, int lane) {
 }
 DEV float exp2_raw(float x) { return __builtin_amdgcn_exp2f(x); }  // v_exp_f32: exp2(-inf) = 0
 
+// A fragment times a scalar, rounded back to bf16. The kernels below fold the score scale
+// log2(e)/sqrt(hs) into the operand they keep in registers (one more bf16 rounding of it), and
+// start each score accumulator at minus the offset the exponential needs (the running maximum,
+// or the base-2 log-sum-exp in the backward), so that the product itself gives the argument
+// of exp2 and the softmax needs no multiply-add per score.
+DEV bf16x8 frag_scaled(const bf16x8& f, float s) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)((float)f[e] * s);
+    return r;
+}
+DEV floatx4 splat4(float v) { return floatx4{v, v, v, v}; }
+
 // QB blocks of 16 queries per wave: 4 waves cover 64 * QB queries of one (batch, head)
 template <int QB>
 __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel(const bf16* __restrict__ qkv,
@@ -601,20 +614,23 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
         const int q = qw0 + qb * 16 + col;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            qf[qb][ks] = q < T_ ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+            qf[qb][ks] = q < T_ ? frag_scaled(frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8), sc)
+                                : frag_zero<bf16>();
     }
     // o: the output rows, unnormalized; lacc: the softmax denominators, accumulated by the
     // same products as o with a fragment of ones in place of V^T (every entry of lacc[qb] is
     // then the sum over the keys so far of query column (lane & 15)); mref: the reference
-    // maxima the exponentials are taken against
+    // maxima (base 2) the exponentials are taken against; moff: the same, 0 while still
+    // -inf, the value the score accumulators start from (negated)
     floatx4 o[4][QB], lacc[QB];
-    float mref[QB];
+    float mref[QB], moff[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) o[d][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
         lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
         mref[qb] = -INFINITY;
+        moff[qb] = 0.f;
     }
     const bf16x8 ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 
@@ -657,7 +673,7 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = splat4(-moff[qb]);
         // k step outermost, so that the two products into one accumulator are four apart
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -670,9 +686,9 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
         for (int d = 2; d < 4; ++d) vf[0][d] = ts_tr(sV, d * 16, 0, 16, lane);
 #pragma unroll
         for (int d = 0; d < 4; ++d) vf[1][d] = ts_tr(sV, d * 16, 32, 48, lane);
-        // online softmax in the log2 domain on raw scores: max first, then one fma + exp2; the
-        // causal and sequence-end mask only in the chunks that reach the diagonal or the end
-        // (one wave-uniform branch around selects)
+        // online softmax in the log2 domain: s holds scale * score - moff; max first, then one
+        // exp2 per score; the causal and sequence-end mask only in the chunks that reach the
+        // diagonal or the end (one wave-uniform branch around selects)
         if ((k0 + 63 > qw0) || (k0 + 64 > T_)) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -691,24 +707,28 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-            mx = group4_max_swap(mx) * sc;
+            mx = group4_max_swap(mx) + moff[qb];
             // Lazy rescaling: the reference maximum moves (and o and the denominators are
             // rescaled) only when some query of the wave has a score more than 2^8 above it,
             // so the exponentials stay <= 256 and the normalization o / l, which shares the
             // reference, is unchanged. The first chunk always sets it (mref = -inf).
             if (__builtin_amdgcn_ballot_w64(mx > mref[qb] + 8.f)) {
                 const float mnew = fmaxf(mref[qb], mx);
-                const float alpha = exp2_raw(mref[qb] - (mnew == -INFINITY ? 0.f : mnew));
+                const float msafe = mnew == -INFINITY ? 0.f : mnew;
+                const float alpha = exp2_raw(mref[qb] - msafe);
 #pragma unroll
                 for (int d = 0; d < 4; ++d) o[d][qb] *= alpha;
                 lacc[qb] *= alpha;
+                const float shift = msafe - moff[qb];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) s[kb][qb] -= shift;
                 mref[qb] = mnew;
+                moff[qb] = msafe;
             }
-            const float msafe = mref[qb] == -INFINITY ? 0.f : mref[qb];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s[kb][qb][i] = exp2_raw(fmaf(s[kb][qb][i], sc, -msafe));
+                for (int i = 0; i < 4; ++i) s[kb][qb][i] = exp2_raw(s[kb][qb][i]);
         }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -775,7 +795,7 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int64_t off = (int64_t)key * ld + h * HS + ks * 32 + g * 8;
-            kf[kb][ks] = key < T_ ? frag_global<bf16>(base + off + C) : frag_zero<bf16>();
+            kf[kb][ks] = key < T_ ? frag_scaled(frag_global<bf16>(base + off + C), sc) : frag_zero<bf16>();
             vf[kb][ks] = key < T_ ? frag_global<bf16>(base + off + 2 * C) : frag_zero<bf16>();
         }
     }
@@ -811,23 +831,38 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
         const char* sO = sQ + TS_BYTES;
         const float* sL = (const float*)(sQ + 2 * TS_BYTES);
         const float* sD = sL + 64;
+        // fragments read ahead of their products, k step outermost (as in the dQ kernel)
+        bf16x8 qa[4][2], oa[4][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                qa[qb][ks] = ts_nat(sQ, qb * 16, ks, lane);
+                oa[qb][ks] = ts_nat(sO, qb * 16, ks, lane);
+            }
+        // s = scale * score - L (base 2), dp = dP - D, per query row q0 + 16qb + 4g + i: the
+        // offsets start the accumulators
         floatx4 s[4][KBW], dp[4][KBW];
-        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
+            const floatx4 nl = -*(const floatx4*)(sL + qb * 16 + g * 4);
+            const floatx4 nd = -*(const floatx4*)(sD + qb * 16 + g * 4);
 #pragma unroll
-            for (int kb = 0; kb < KBW; ++kb) s[qb][kb] = dp[qb][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 qa = ts_nat(sQ, qb * 16, ks, lane);
-                const bf16x8 oa = ts_nat(sO, qb * 16, ks, lane);
-#pragma unroll
-                for (int kb = 0; kb < KBW; ++kb) {
-                    mma8(s[qb][kb], qa, kf[kb][ks]);
-                    mma8(dp[qb][kb], oa, vf[kb][ks]);
-                }
+            for (int kb = 0; kb < KBW; ++kb) {
+                s[qb][kb] = nl;
+                dp[qb][kb] = nd;
             }
         }
+        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < KBW; ++kb) {
+                    mma8(s[qb][kb], qa[qb][ks], kf[kb][ks]);
+                    mma8(dp[qb][kb], oa[qb][ks], vf[kb][ks]);
+                }
         __builtin_amdgcn_s_setprio(0);
         // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col. Only chunks
         // that cross the diagonal or the end of the sequence are masked: the two forms are
@@ -837,20 +872,18 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
             for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int ql = qb * 16 + g * 4 + i;
-                    const int q = q0 + ql;
-                    const float L = sL[ql], Dq = sD[ql];
+                    const int q = q0 + qb * 16 + g * 4 + i;
 #pragma unroll
                     for (int kb = 0; kb < KBW; ++kb) {
                         const int key = kw0 + kb * 16 + col;
-                        float a = fmaf(s[qb][kb][i], sc, -L);
+                        float a = s[qb][kb][i];
                         // masked entries get -inf added before the exponential (exp2(-inf) = 0):
                         // a select between two constants, which the compiler keeps branch-free
                         // (a select of the loaded value itself it turns into a branch per entry)
                         if constexpr (decltype(masked)::value) a += ((key <= q) & (q < T_)) ? 0.f : -INFINITY;
                         const float p = exp2_raw(a);
                         s[qb][kb][i] = p;
-                        dp[qb][kb][i] = p * (dp[qb][kb][i] - Dq);
+                        dp[qb][kb][i] *= p;
                     }
                 }
         };
@@ -929,7 +962,8 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         float dsum = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            qf[qb][ks] = ok ? frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
+            qf[qb][ks] = ok ? frag_scaled(frag_global<bf16>(base + (int64_t)q * ld + h * HS + ks * 32 + g * 8), sc)
+                            : frag_zero<bf16>();
             of[qb][ks] = ok ? frag_global<bf16>(dyb + (int64_t)q * C + h * HS + ks * 32 + g * 8) : frag_zero<bf16>();
             // D = sum_d dO o O of this query row (the softmax-gradient correction term): this
             // lane's 8 dimensions, then the 4 lane groups of the row
@@ -974,24 +1008,39 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         }
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
+        // fragments read ahead of their products (as in the forward); k step outermost, so
+        // that the two products into one accumulator are eight apart
+        bf16x8 ka[4][2], va[4][2], kat[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                ka[kb][ks] = ts_nat(sK, kb * 16, ks, lane);
+                va[kb][ks] = ts_nat(sV, kb * 16, ks, lane);
+            }
+        // s = scale * score - L (base 2), dp = dP - D: the offsets start the accumulators
         floatx4 s[4][QBW], dp[4][QBW];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int qb = 0; qb < QBW; ++qb) {
+                s[kb][qb] = splat4(-L[qb]);
+                dp[kb][qb] = splat4(-Dq[qb]);
+            }
         __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int qb = 0; qb < QBW; ++qb) s[kb][qb] = dp[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 ka = ts_nat(sK, kb * 16, ks, lane);
-                const bf16x8 va = ts_nat(sV, kb * 16, ks, lane);
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QBW; ++qb) {
-                    mma8(s[kb][qb], ka, qf[qb][ks]);
-                    mma8(dp[kb][qb], va, of[qb][ks]);
+                    mma8(s[kb][qb], ka[kb][ks], qf[qb][ks]);
+                    mma8(dp[kb][qb], va[kb][ks], of[qb][ks]);
                 }
-            }
-        }
         __builtin_amdgcn_s_setprio(0);
+        // the K^T fragments of the dQ product's first half, in flight during the exponentials
+#pragma unroll
+        for (int d = 0; d < 4; ++d) kat[0][d] = ts_tr(sK, d * 16, 0, 16, lane);
         // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col; masked and unmasked forms
         // compiled separately, as in the dK/dV kernel
         auto ds = [&](auto masked) {
@@ -1003,10 +1052,10 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int key = k0 + kb * 16 + g * 4 + i;
-                        float a = fmaf(s[kb][qb][i], sc, -L[qb]);
+                        float a = s[kb][qb][i];
                         if constexpr (decltype(masked)::value) a += ((key <= q) & (key < T_)) ? 0.f : -INFINITY;  // as in dK/dV
                         const float p = exp2_raw(a);
-                        dp[kb][qb][i] = p * (dp[kb][qb][i] - Dq[qb]);
+                        dp[kb][qb][i] *= p;
                     }
                 }
         };
@@ -1014,16 +1063,16 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         else ds(std::false_type{});
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
+        for (int d = 0; d < 4; ++d) kat[1][d] = ts_tr(sK, d * 16, 32, 48, lane);
+#pragma unroll
         for (int st = 0; st < 2; ++st) {
             bf16x8 dfr[QBW];
 #pragma unroll
             for (int qb = 0; qb < QBW; ++qb) dfr[qb] = frag_from_acc<bf16>(dp[2 * st][qb], dp[2 * st + 1][qb]);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const bf16x8 kat = ts_tr(sK, d * 16, 32 * st, 32 * st + 16, lane);
+            for (int d = 0; d < 4; ++d)
 #pragma unroll
-                for (int qb = 0; qb < QBW; ++qb) mma8(dq[d][qb], kat, dfr[qb]);
-            }
+                for (int qb = 0; qb < QBW; ++qb) mma8(dq[d][qb], kat[st][d], dfr[qb]);
         }
         __builtin_amdgcn_s_setprio(0);
     }
