@@ -831,15 +831,9 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
         const char* sO = sQ + TS_BYTES;
         const float* sL = (const float*)(sQ + 2 * TS_BYTES);
         const float* sD = sL + 64;
-        // fragments read ahead of their products, k step outermost (as in the dQ kernel)
-        bf16x8 qa[4][2], oa[4][2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) {
-                qa[qb][ks] = ts_nat(sQ, qb * 16, ks, lane);
-                oa[qb][ks] = ts_nat(sO, qb * 16, ks, lane);
-            }
+        // fragments read one k step ahead of their products, k step outermost (as in the dQ
+        // kernel)
+        bf16x8 qa[4], oa[4];
         // s = scale * score - L (base 2), dp = dP - D, per query row q0 + 16qb + 4g + i: the
         // offsets start the accumulators
         floatx4 s[4][KBW], dp[4][KBW];
@@ -853,17 +847,23 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
                 dp[qb][kb] = nd;
             }
         }
-        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) {
+                qa[qb] = ts_nat(sQ, qb * 16, ks, lane);
+                oa[qb] = ts_nat(sO, qb * 16, ks, lane);
+            }
+            __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
                 for (int kb = 0; kb < KBW; ++kb) {
-                    mma8(s[qb][kb], qa[qb][ks], kf[kb][ks]);
-                    mma8(dp[qb][kb], oa[qb][ks], vf[kb][ks]);
+                    mma8(s[qb][kb], qa[qb], kf[kb][ks]);
+                    mma8(dp[qb][kb], oa[qb], vf[kb][ks]);
                 }
-        __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_s_setprio(0);
+        }
         // P and dS; rows q = q0 + 16qb + 4g + i, column key = kw0 + 16kb + col. Only chunks
         // that cross the diagonal or the end of the sequence are masked: the two forms are
         // compiled separately, so the others carry no compares or selects.
@@ -927,7 +927,7 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
 
 // dQ for 64 * QBW queries per workgroup (16 * QBW per wave), streaming 64-key chunks of K and V.
 template <int QBW>
-__global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
+__global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 4 : 2) attn_bwd_dq_ts_kernel(const bf16* __restrict__ qkv,
                                                                    const bf16* __restrict__ y,
                                                                    const bf16* __restrict__ dy,
                                                                    const float* __restrict__ lse,
@@ -1008,16 +1008,10 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         }
         const char* sK = smem + (c & 1) * STAGE;
         const char* sV = sK + TS_BYTES;
-        // fragments read ahead of their products (as in the forward); k step outermost, so
-        // that the two products into one accumulator are eight apart
-        bf16x8 ka[4][2], va[4][2], kat[2][4];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                ka[kb][ks] = ts_nat(sK, kb * 16, ks, lane);
-                va[kb][ks] = ts_nat(sV, kb * 16, ks, lane);
-            }
+        // fragments read one k step ahead of their products, k step outermost, so that the two
+        // products into one accumulator are eight apart (and at most one k step's fragments
+        // are held: the registers decide how many waves share a SIMD)
+        bf16x8 ka[4], va[4], kat[2][4];
         // s = scale * score - L (base 2), dp = dP - D: the offsets start the accumulators
         floatx4 s[4][QBW], dp[4][QBW];
 #pragma unroll
@@ -1027,20 +1021,24 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
                 s[kb][qb] = splat4(-L[qb]);
                 dp[kb][qb] = splat4(-Dq[qb]);
             }
-        __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                ka[kb] = ts_nat(sK, kb * 16, ks, lane);
+                va[kb] = ts_nat(sV, kb * 16, ks, lane);
+            }
+            __builtin_amdgcn_s_setprio(1);  // MFMA phases at raised priority (see the forward)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QBW; ++qb) {
-                    mma8(s[kb][qb], ka[kb][ks], qf[qb][ks]);
-                    mma8(dp[kb][qb], va[kb][ks], of[qb][ks]);
+                    mma8(s[kb][qb], ka[kb], qf[qb][ks]);
+                    mma8(dp[kb][qb], va[kb], of[qb][ks]);
                 }
-        __builtin_amdgcn_s_setprio(0);
-        // the K^T fragments of the dQ product's first half, in flight during the exponentials
-#pragma unroll
-        for (int d = 0; d < 4; ++d) kat[0][d] = ts_tr(sK, d * 16, 0, 16, lane);
+            __builtin_amdgcn_s_setprio(0);
+        }
+
         // rows key = k0 + 16kb + 4g + i, column q = qw0 + 16qb + col; masked and unmasked forms
         // compiled separately, as in the dK/dV kernel
         auto ds = [&](auto masked) {
@@ -1063,7 +1061,9 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 3 : 2) attn_bwd_dq_ts_ke
         else ds(std::false_type{});
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) kat[1][d] = ts_tr(sK, d * 16, 32, 48, lane);
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) kat[st][d] = ts_tr(sK, d * 16, 32 * st, 32 * st + 16, lane);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             bf16x8 dfr[QBW];
