@@ -273,6 +273,16 @@ struct gpt2 {
     Plan P;
     char* ws = nullptr;
     hipStream_t stream = nullptr;
+    // a second stream (default priority) for work that depends only on the inputs: the
+    // embedding backward's id sort runs on it under the rest of the backward; it forks from
+    // and joins `stream` through the two events (edges in a graph capture of `stream`)
+    hipStream_t side = nullptr;
+    hipEvent_t side_fork = nullptr, side_join = nullptr;
+    ~gpt2() {
+        if (side_fork) (void)hipEventDestroy(side_fork);
+        if (side_join) (void)hipEventDestroy(side_join);
+        if (side) (void)hipStreamDestroy(side);
+    }
     int dev = 0;
     bool bf16 = false;    // product and attention operands, activations: bf16 (else fp32)
     bool res16 = false;   // residual stream and its gradient: bf16 (else fp32)
@@ -465,6 +475,16 @@ extern "C" int gpt2_create(const gpt2_config* cfg, void* d_ws, size_t ws_bytes, 
     h->bf16 = cfg->dtype != GPT2_FP32;
     h->res16 = cfg->dtype == GPT2_BF16_RES16;
     (void)hipGetDevice(&h->dev);
+    if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->side_fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->side_join, hipEventDisableTiming) != hipSuccess) {
+        // without them everything runs on the caller's stream
+        if (h->side_fork) (void)hipEventDestroy(h->side_fork);
+        if (h->side) (void)hipStreamDestroy(h->side);
+        h->side = nullptr;
+        h->side_fork = h->side_join = nullptr;
+        (void)hipGetLastError();
+    }
     if (!g_setup_done) {
         gemm_setup();
         attention_setup();
@@ -942,6 +962,15 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     float* sumscr = h->at<float>(P.sumscr);
     void* skpart = h->at<char>(P.splitk);
     const int lnblk = layernorm_backward_blocks(BT);
+    // the embedding backward's id sort depends only on the token ids: issue it first, on the
+    // side stream, so that it runs under the products below instead of alone at the end
+    const bool presorted = h->side && embed_backward_presortable(BT);
+    if (presorted) {
+        HIPTRY(hipEventRecord(h->side_fork, s), "fork side stream");
+        HIPTRY(hipStreamWaitEvent(h->side, h->side_fork, 0), "fork side stream");
+        HIPTRY(embed_backward_sort(h->at<int32_t>(P.idx), BT, h->at<char>(P.ebscratch), h->side), "embedding id sort");
+        HIPTRY(hipEventRecord(h->side_join, h->side), "join side stream");
+    }
 
     // LayerNorm backward; with bias_off >= 0 the incoming residual gradient's column sum
     // (gathered by the same kernel) is the bias gradient of the projection at that offset
@@ -1058,9 +1087,10 @@ extern "C" int gpt2_backward(gpt2_t* h, float grad_scale, int32_t accumulate) {
     // embeddings: token rows scatter-add on top of the lm_head gradient, position rows
     if (!acc && T < c.block_size)
         HIPTRY(fill(grd + L.wpe + (int64_t)T * C, (int64_t)(c.block_size - T) * C, 0.f, s), "zero wpe tail");
+    if (presorted) HIPTRY(hipStreamWaitEvent(s, h->side_join, 0), "join side stream");
     TRY(run(h, "embed_bwd", [&] {
         return embed_backward(h->at<int32_t>(P.idx), dres, grd + L.wte, grd + L.wpe, B, T, C, acc, r16,
-                              h->at<char>(P.ebscratch), s);
+                              h->at<char>(P.ebscratch), presorted ? 1 : 0, s);
     }));
     return GPT2_OK;
 }

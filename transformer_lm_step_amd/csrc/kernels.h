@@ -135,8 +135,13 @@ hipError_t mean_reduce(const float* v, int n, float* d_out, hipStream_t s);
 // dx (the residual stream's gradient) is bf16 if is_bf16, else fp32
 size_t embed_backward_scratch_bytes(int rows, int C);
 void rows_setup();
+// With presorted, the id sort of the rows was already issued by embed_backward_sort (on a
+// stream ordered before s): possible when embed_backward_presortable(rows), one sort chunk.
 hipError_t embed_backward(const int32_t* idx, const void* dx, float* dwte, float* dwpe, int B, int T,
-                          int C, int accumulate_wpe, int is_bf16, void* scratch, hipStream_t s);
+                          int C, int accumulate_wpe, int is_bf16, void* scratch, int presorted, hipStream_t s);
+bool embed_backward_presortable(int rows);
+// the id sort alone (it depends only on idx), into the same scratch
+hipError_t embed_backward_sort(const int32_t* idx, int rows, void* scratch, hipStream_t s);
 
 // global grad norm + clip coefficient, AdamW
 int norm_blocks();

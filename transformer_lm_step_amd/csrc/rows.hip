@@ -988,27 +988,51 @@ __global__ void dwpe_kernel(const S* __restrict__ dx, float* __restrict__ dwpe, 
     dwpe[i] = accumulate ? dwpe[i] + s : s;
 }
 
-template <typename S>
-static hipError_t embed_backward_t(const int32_t* idx, const S* dx, float* dwte, float* dwpe, int B, int T, int C,
-                                   int accumulate_wpe, void* scratch, hipStream_t s) {
-    const int rows = B * T;
+// the scratch's parts (layout as sized by embed_backward_scratch_bytes)
+struct EbScratch {
+    EbMeta* meta;
+    int32_t *srow, *seg_begin, *run_id, *run_seg;
+    float* part;
+};
+static EbScratch eb_scratch(void* scratch, int rows) {
+    EbScratch e;
     char* p = (char*)scratch;
-    EbMeta* meta = (EbMeta*)p;
+    e.meta = (EbMeta*)p;
     p += 256;
     const int n_max = rows < EB_CHUNK ? rows : EB_CHUNK;
-    int32_t* srow = (int32_t*)p; p += (size_t)n_max * 4;
-    int32_t* seg_begin = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
-    int32_t* run_id = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
-    int32_t* run_seg = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    e.srow = (int32_t*)p; p += (size_t)n_max * 4;
+    e.seg_begin = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    e.run_id = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
+    e.run_seg = (int32_t*)p; p += (size_t)(n_max + 1) * 4;
     size_t off = (size_t)(p - (char*)scratch);
     off = (off + 255) & ~(size_t)255;
-    float* part = (float*)((char*)scratch + off);
+    e.part = (float*)((char*)scratch + off);
+    return e;
+}
+static hipError_t eb_sort_launch(const int32_t* idx, int n, const EbScratch& e, hipStream_t s) {
+    hipLaunchKernelGGL(eb_sort_kernel, dim3(1), dim3(EB_THREADS), (size_t)2 * EB_CHUNK * 4, s, idx, n, e.meta, e.srow,
+                       e.seg_begin, e.run_id, e.run_seg);
+    return hipGetLastError();
+}
+bool embed_backward_presortable(int rows) { return rows > 0 && rows <= EB_CHUNK; }
+hipError_t embed_backward_sort(const int32_t* idx, int rows, void* scratch, hipStream_t s) {
+    if (!embed_backward_presortable(rows)) return hipErrorInvalidValue;
+    return eb_sort_launch(idx, rows, eb_scratch(scratch, rows), s);
+}
+
+template <typename S>
+static hipError_t embed_backward_t(const int32_t* idx, const S* dx, float* dwte, float* dwpe, int B, int T, int C,
+                                   int accumulate_wpe, void* scratch, int presorted, hipStream_t s) {
+    const int rows = B * T;
+    const EbScratch es = eb_scratch(scratch, rows);
+    EbMeta* meta = es.meta;
+    int32_t *srow = es.srow, *seg_begin = es.seg_begin, *run_id = es.run_id, *run_seg = es.run_seg;
+    float* part = es.part;
+    if (presorted && !embed_backward_presortable(rows)) return hipErrorInvalidValue;
     for (int r0 = 0; r0 < rows; r0 += EB_CHUNK) {
         const int n = rows - r0 < EB_CHUNK ? rows - r0 : EB_CHUNK;
-        hipLaunchKernelGGL(eb_sort_kernel, dim3(1), dim3(EB_THREADS), (size_t)2 * EB_CHUNK * 4, s, idx + r0, n, meta, srow,
-                           seg_begin, run_id, run_seg);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        hipError_t e = hipSuccess;
+        if (!presorted && (e = eb_sort_launch(idx + r0, n, es, s)) != hipSuccess) return e;
         hipLaunchKernelGGL(eb_segment_kernel<S>, dim3(2048), dim3(C / 4 < 256 ? ((C / 4 + 63) / 64) * 64 : 256), 0, s,
                            meta, srow, seg_begin, dx, r0, C, part);
         e = hipGetLastError();
@@ -1024,10 +1048,10 @@ static hipError_t embed_backward_t(const int32_t* idx, const S* dx, float* dwte,
     return hipGetLastError();
 }
 hipError_t embed_backward(const int32_t* idx, const void* dx, float* dwte, float* dwpe, int B, int T, int C,
-                          int accumulate_wpe, int is_bf16, void* scratch, hipStream_t s) {
+                          int accumulate_wpe, int is_bf16, void* scratch, int presorted, hipStream_t s) {
     if (is_bf16)
-        return embed_backward_t(idx, (const bf16*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, s);
-    return embed_backward_t(idx, (const float*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, s);
+        return embed_backward_t(idx, (const bf16*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, presorted, s);
+    return embed_backward_t(idx, (const float*)dx, dwte, dwpe, B, T, C, accumulate_wpe, scratch, presorted, s);
 }
 
 void rows_setup() {
