@@ -321,6 +321,8 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
 // Two stages: the loads of tile kt+1 are issued right after the barrier that opens the
 // multiplication of tile kt and are waited for (vmcnt) before the next barrier.
 constexpr int MM_BK = 64;   // bf16 elements of K per tile (128 bytes)
+// compute units of the device (set by gemm_setup; 256 on MI355X)
+static int kGemmCUs = 256;
 
 DEV int swz_k(int r) { return (r >> 1) & 7; }
 DEV int swz_mn(int k) { return ((k & 3) | ((k >> 1) & 4)) << 1; }
@@ -1093,23 +1095,34 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             // of 192 and they fill whole rounds of 512 workgroups (two per CU) about as well as
             // 128x128 tiles: N = 768 gives 512 tiles instead of 768, N = 2304 three rounds
             // instead of 4.5, N = 50304 = 262 x 192. 256x256 tiles measured slower everywhere.
-            bool wide = false;
+            bool wide = false, narrow = false;
             if (epi == EPI_LOGITS) {
                 wide = true;
             } else if (d.bn) {
                 wide = d.bn == 192;
-            } else if (nsplit == 1 && d.N % 192 == 0) {
+                narrow = d.bn == 64;
+            } else if (nsplit == 1) {
                 auto fill = [&](int bn) {
                     const int64_t blocks = (int64_t)((d.M + 127) / 128) * ((d.N + bn - 1) / bn);
                     const int64_t rounds = (blocks + 511) / 512;
                     return (double)blocks / (double)(rounds * 512);
                 };
-                wide = fill(192) >= fill(128) - 0.02;
+                if (d.N % 192 == 0) wide = fill(192) >= fill(128) - 0.02;
+                // 128x64 tiles (48 KB of LDS: three workgroups per CU) where 128-wide tiles
+                // would leave CUs without a workgroup (few rows: a batch of 4 sequences, the
+                // forward-only pass): more workgroups at more LDS bytes per MFMA
+                const int64_t blocks128 = (int64_t)((d.M + 127) / 128) * ((d.N + 127) / 128);
+                if (d.N % 64 == 0 && blocks128 < kGemmCUs) {
+                    narrow = true;
+                    wide = false;
+                }
             }
 #define MM_CASE(AL, BL, EP)                                                                   \
     if (d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 128>(a, nsplit, s); else
 #define MM_CASE_WIDE(AL, BL, EP)                                                              \
     if (wide && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 192>(a, nsplit, s); else
+#define MM_CASE_NARROW(AL, BL, EP)                                                            \
+    if (narrow && d.a_layout == AL && d.b_layout == BL && epi == EP) e = launch_mm<AL, BL, EP, 128, 64>(a, nsplit, s); else
             MM_CASE_WIDE(0, 0, EPI_BIAS_T)
             MM_CASE_WIDE(0, 0, EPI_LOGITS)
             MM_CASE_WIDE(0, 1, EPI_F32)
@@ -1118,6 +1131,10 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             MM_CASE_WIDE(0, 1, EPI_GELU_BWD)
             MM_CASE_WIDE(1, 1, EPI_PARTIAL)
             MM_CASE_WIDE(1, 1, EPI_F32)
+            MM_CASE_NARROW(0, 0, EPI_BIAS_T)
+            MM_CASE_NARROW(0, 0, EPI_BIAS_GELU)
+            MM_CASE_NARROW(0, 1, EPI_BIAS_T)
+            MM_CASE_NARROW(0, 1, EPI_GELU_BWD)
             MM_CASE(0, 0, EPI_BIAS_T)
             MM_CASE(0, 0, EPI_BIAS_GELU)
             MM_CASE(0, 1, EPI_GELU_BWD)
@@ -1129,6 +1146,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
             return hipErrorInvalidValue;
 #undef MM_CASE
 #undef MM_CASE_WIDE
+#undef MM_CASE_NARROW
             goto reduce;
         }
     }
@@ -1200,6 +1218,14 @@ static void set_lds_mm() {
 }
 
 void gemm_setup() {
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+            kGemmCUs = cus;
+    }
+    set_lds_mm<0, 0, EPI_BIAS_T, 128, 64>(); set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 64>();
+    set_lds_mm<0, 1, EPI_BIAS_T, 128, 64>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 64>();
     set_lds_mm<0, 0, EPI_BIAS_T, 128, 192>(); set_lds_mm<0, 0, EPI_LOGITS, 128, 192>();
     set_lds_mm<0, 1, EPI_F32, 128, 192>(); set_lds_mm<0, 1, EPI_BIAS_T, 128, 192>();
     set_lds_mm<0, 0, EPI_BIAS_GELU, 128, 192>(); set_lds_mm<0, 1, EPI_GELU_BWD, 128, 192>();
