@@ -198,6 +198,33 @@ def test_ragged_context_two_layers_bf16(T):
     _grads_cosine(st, ref_g)
 
 
+def test_sharp_attention_bf16():
+    """124M widths, 2 layers, one sequence of 1024, with the query and key rows of c_attn scaled
+    by 3.5 (scores about 12x wider): the running maximum of a wave's queries then grows by more
+    than 2^8 after the first key chunk in several hundred of layer 0's 6,528 wave-chunks, which
+    runs the forward's lazy rescale with the shift of the chunk's scores, and the backward's
+    log-sum-exp offsets are larger. (Much sharper attention leaves the bf16 bar: at a factor 6
+    the gradient cosines fall to about 0.99 with or without the scale folded into the queries.)"""
+    note("124M sharp attention L=2 bf16 B=1")
+    w = synthetic.workload("gpt2_step", n_layer=2)
+    params = synthetic.init_params(w, randomize_affine=True)
+    C = w.n_embd
+    for l in range(w.n_layer):
+        k = f"h.{l}.attn.c_attn.weight"
+        params[k] = params[k].copy()
+        params[k][:2 * C] *= 3.5
+    x, y = synthetic.micro_batches(w, 1, batch=1)[0]
+    p64 = f64(params)
+    out = O.forward(p64, w.n_layer, w.n_head, x, y)
+    ref_g = O.backward(p64, w.n_layer, w.n_head, out["cache"], 1.0)
+    st = make_step(w, "bf16", max_batch=1)
+    st.set_params(params)
+    loss, _ = st.forward(x, y)
+    assert abs(loss - float(out["loss"])) <= 2e-2
+    st.backward(1.0, False)
+    _grads_cosine(st, ref_g)
+
+
 @pytest.mark.parametrize("mode", BF16_MODES)
 def test_xl_shape_two_layers_bf16(mode):
     """1558M widths (C=1600, 25 heads, MLP 6400) with 2 layers, one sequence of 1024."""
