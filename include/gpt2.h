@@ -256,6 +256,24 @@ int gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float eps, fl
 double gpt2_cosine_lr(int64_t it, double max_lr, double min_lr, int64_t warmup_steps,
                       int64_t max_steps);
 
+/* Graph-replayable optimizer step ("Karpathy's Zero to Hero, Lecture 9" notes, "Code you'll
+ * write", training step: the learning rate set from the schedule each step, then AdamW). For a
+ * training step captured once in a HIP graph (gpt2_set_stream to the capture stream) and
+ * replayed: the scalars a host call would pass live in device memory and are read when the
+ * kernels run, so every replay advances the schedule.
+ * gpt2_schedule_step_device: with it = *d_step (0-based optimizer step, device int32):
+ *   *d_lr = gpt2_cosine_lr(it, max_lr, min_lr, warmup_steps, max_steps) (the same double
+ *   arithmetic, rounded to float), *d_t = it + 1, then *d_step = it + 1. Requires
+ *   1 <= warmup_steps < max_steps (GPT2_EINVAL otherwise). Enqueued on the handle's stream.
+ * gpt2_adamw_step_device: gpt2_adamw_step with lr = *d_lr and t = *d_t (device float and
+ *   int32, read when the update runs; t >= 1), bias corrections 1 - beta^t in double as on
+ *   the host path. d_grad_norm (device, nullable) receives the pre-clip norm. There is no
+ *   host-norm output (that would synchronize). */
+int gpt2_schedule_step_device(gpt2_t* h, int32_t* d_step, float* d_lr, int32_t* d_t, double max_lr,
+                              double min_lr, int64_t warmup_steps, int64_t max_steps);
+int gpt2_adamw_step_device(gpt2_t* h, const float* d_lr, const int32_t* d_t, float beta1, float beta2,
+                           float eps, float weight_decay, float max_grad_norm, float* d_grad_norm);
+
 /* ---------------------------------------------------------------- diagnostics */
 
 /* Message of the last error on this thread ("" if none). */

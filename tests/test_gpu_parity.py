@@ -868,6 +868,110 @@ def test_adamw_matches_oracle(dtype):
         assert rel_max(mg[k], m[k]) <= 1e-5 and rel_max(vg[k], v[k]) <= 1e-5, k
 
 
+def test_device_schedule_and_adamw_match_host_path():
+    """gpt2_schedule_step_device + gpt2_adamw_step_device against the host-scalar path on two
+    handles holding the same state, over warmup, cosine and the tail of the schedule: the
+    device learning rate equals gpt2_cosine_lr rounded to float, and parameters and moments
+    agree to the last bits the bias corrections may differ in (double pow on the two sides)."""
+    note("device schedule + adamw")
+    w = synthetic.workload("tiny")
+    params = synthetic.init_params(w, randomize_affine=True)
+    a, b = make_step(w, "bf16"), make_step(w, "bf16")
+    a.set_params(params)
+    b.set_params(params)
+    rng = np.random.default_rng(11)
+    sched = dict(max_lr=6e-4, min_lr=6e-5, warmup_steps=3, max_steps=6)
+    step0 = 1
+    d_step = torch.tensor([step0], dtype=torch.int32, device="cuda")
+    d_lr = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for it in range(step0, step0 + 7):   # warmup, cosine, past max_steps
+        grads = {k: (rng.standard_normal(x.shape) * 0.5).astype(np.float32) for k, x in params.items()}
+        gt = torch.from_numpy(a.pack(grads)).cuda()
+        G.gpt2_set_grads(a.h, gt.data_ptr(), 1)
+        G.gpt2_set_grads(b.h, gt.data_ptr(), 1)
+        lr = G.gpt2_cosine_lr(it, **sched)
+        a.adamw_step(lr, t=it + 1)
+        G.gpt2_schedule_step_device(b.h, d_step.data_ptr(), d_lr.data_ptr(), d_t.data_ptr(), **sched)
+        G.gpt2_adamw_step_device(b.h, d_lr.data_ptr(), d_t.data_ptr())
+        torch.cuda.synchronize()
+        assert int(d_step.item()) == it + 1 and int(d_t.item()) == it + 1
+        assert float(d_lr.item()) == float(np.float32(lr)), (it, float(d_lr.item()), lr)
+    pa, pb = a.params(), b.params()
+    for k in pa:
+        assert rel_max(pb[k], pa[k]) <= 1e-6, k
+    ma = torch.empty(a.n_params, dtype=torch.float32, device="cuda")
+    va, mb, vb = torch.empty_like(ma), torch.empty_like(ma), torch.empty_like(ma)
+    G.gpt2_get_moments(a.h, ma.data_ptr(), va.data_ptr(), 1)
+    G.gpt2_get_moments(b.h, mb.data_ptr(), vb.data_ptr(), 1)
+    assert torch.equal(ma, mb) and torch.equal(va, vb)   # the moments do not see the bias corrections
+    a.close()
+    b.close()
+
+
+def test_hip_graph_full_training_step():
+    """A whole training step -- schedule, forward, backward, AdamW with its scalars in device
+    memory -- captured once in a HIP graph and replayed three times, against the same calls made
+    eagerly on a second handle from the same state: every step's loss and the final parameters
+    and moments agree bit for bit, and the schedule advanced three steps."""
+    note("hip graph full training step")
+    w = synthetic.workload("gpt2_step", n_layer=2, batch=2, seq_len=256, block_size=256)
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    B, T = x.shape
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    sched = dict(max_lr=6e-4, min_lr=6e-5, warmup_steps=2, max_steps=10)
+
+    def make():
+        st = make_step(w, "bf16")
+        st.set_params(params)
+        bufs = dict(step=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    lr=torch.zeros(1, dtype=torch.float32, device="cuda"),
+                    t=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    loss=torch.zeros(1, dtype=torch.float32, device="cuda"))
+        return st, bufs
+
+    def step(st, b):
+        G.gpt2_schedule_step_device(st.h, b["step"].data_ptr(), b["lr"].data_ptr(), b["t"].data_ptr(), **sched)
+        G.gpt2_forward(st.h, xd.data_ptr(), yd.data_ptr(), B, T, None, b["loss"].data_ptr())
+        G.gpt2_backward(st.h, 1.0, 0)
+        G.gpt2_adamw_step_device(st.h, b["lr"].data_ptr(), b["t"].data_ptr())
+
+    eager, be = make()
+    losses = []
+    for _ in range(3):
+        step(eager, be)
+        torch.cuda.synchronize()
+        losses.append(be["loss"].clone())
+    graphed, bg = make()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        G.gpt2_set_stream(graphed.h, torch.cuda.current_stream().cuda_stream)
+        step(graphed, bg)
+    G.gpt2_set_stream(graphed.h, graphed.stream)
+    torch.cuda.synchronize()
+    assert int(bg["step"].item()) == 0        # capturing ran nothing
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bg["loss"], losses[rep]), rep
+    assert int(bg["step"].item()) == 3 and int(bg["t"].item()) == 3
+    for get in (G.gpt2_get_params, G.gpt2_get_grads):
+        u = torch.empty(eager.n_params, dtype=torch.float32, device="cuda")
+        v = torch.empty_like(u)
+        get(eager.h, u.data_ptr(), 1)
+        get(graphed.h, v.data_ptr(), 1)
+        assert torch.equal(u, v)
+    m1, v1, m2, v2 = (torch.empty(eager.n_params, dtype=torch.float32, device="cuda") for _ in range(4))
+    G.gpt2_get_moments(eager.h, m1.data_ptr(), v1.data_ptr(), 1)
+    G.gpt2_get_moments(graphed.h, m2.data_ptr(), v2.data_ptr(), 1)
+    assert torch.equal(m1, m2) and torch.equal(v1, v2)
+    del graph
+    eager.close()
+    graphed.close()
+
+
 def test_full_training_step_runs_and_decreases_loss():
     """Forward, backward, AdamW on the tiny model: loss goes down over a few steps on one batch
     (the overfit-a-batch sanity loop of chapter 52:38-1:06:18)."""

@@ -77,6 +77,10 @@ _SIGS = {
     "gpt2_adamw_step": (ctypes.c_int, [_P, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, ctypes.c_int32, _P,
                                        ctypes.POINTER(ctypes.c_float)]),
+    "gpt2_adamw_step_device": (ctypes.c_int, [_P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                              ctypes.c_float, ctypes.c_float, _P]),
+    "gpt2_schedule_step_device": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_double, ctypes.c_double,
+                                                 ctypes.c_int64, ctypes.c_int64]),
     "gpt2_cosine_lr": (ctypes.c_double, [ctypes.c_int64, ctypes.c_double, ctypes.c_double, ctypes.c_int64,
                                          ctypes.c_int64]),
     "gpt2_last_error": (ctypes.c_char_p, []),
@@ -237,6 +241,16 @@ def gpt2_adamw_step(h, lr, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, ma
 
 def gpt2_cosine_lr(it, max_lr=6e-4, min_lr=6e-5, warmup_steps=715, max_steps=19073) -> float:
     return _lib.gpt2_cosine_lr(it, max_lr, min_lr, warmup_steps, max_steps)
+
+
+def gpt2_adamw_step_device(h, d_lr, d_t, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_grad_norm=1.0,
+                           d_grad_norm=None) -> None:
+    _check(_lib.gpt2_adamw_step_device(h, d_lr, d_t, beta1, beta2, eps, weight_decay, max_grad_norm, d_grad_norm))
+
+
+def gpt2_schedule_step_device(h, d_step, d_lr, d_t, max_lr=6e-4, min_lr=6e-5, warmup_steps=715,
+                              max_steps=19073) -> None:
+    _check(_lib.gpt2_schedule_step_device(h, d_step, d_lr, d_t, max_lr, min_lr, warmup_steps, max_steps))
 
 
 def gpt2_timing_begin(h, name: Optional[str] = None) -> None:

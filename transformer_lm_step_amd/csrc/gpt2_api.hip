@@ -1109,13 +1109,42 @@ extern "C" int gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, fl
     const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
     TRY(run(h, "adamw", [&] {
         return adamw(h->params(), h->grads(), h->at<float>(P.m), h->at<float>(P.v), h->bf16 ? h->at<char>(P.shadow) : nullptr,
-                     N, h->L.decay_end, coef, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)std::sqrt(bc2), s);
+                     N, h->L.decay_end, coef, lr, beta1, beta2, eps, weight_decay, (float)bc1, (float)std::sqrt(bc2),
+                     nullptr, s);
     }));
     if (d_grad_norm) HIPTRY(hipMemcpyAsync(d_grad_norm, coef, 4, hipMemcpyDeviceToDevice, s), "copy norm");
     if (h_grad_norm) {
         HIPTRY(hipMemcpyAsync(h_grad_norm, coef, 4, hipMemcpyDeviceToHost, s), "copy norm");
         HIPTRY(hipStreamSynchronize(s), "synchronize");
     }
+    return GPT2_OK;
+}
+
+// The same AdamW step with its learning rate and step count read from device memory when it
+// runs, so that a step captured once in a graph keeps following the schedule on every replay.
+extern "C" int gpt2_adamw_step_device(gpt2_t* h, const float* d_lr, const int32_t* d_t, float beta1, float beta2,
+                                      float eps, float weight_decay, float max_grad_norm, float* d_grad_norm) {
+    if (!h || !d_lr || !d_t) return set_error(GPT2_EINVAL, "null argument");
+    const Plan& P = h->P;
+    hipStream_t s = h->stream;
+    float* coef = h->at<float>(P.normcoef);
+    float* hp = coef + 16;   // (lr, bc1, sqrt(bc2)) in the same 256-byte block
+    const int64_t N = h->L.n_params;
+    TRY(run(h, "grad_norm", [&] { return grad_norm(h->grads(), N, h->at<float>(P.normpart), coef, max_grad_norm, s); }));
+    HIPTRY(adamw_hparams(d_lr, d_t, beta1, beta2, hp, s), "adamw scalars");
+    TRY(run(h, "adamw", [&] {
+        return adamw(h->params(), h->grads(), h->at<float>(P.m), h->at<float>(P.v), h->bf16 ? h->at<char>(P.shadow) : nullptr,
+                     N, h->L.decay_end, coef, 0.f, beta1, beta2, eps, weight_decay, 1.f, 1.f, hp, s);
+    }));
+    if (d_grad_norm) HIPTRY(hipMemcpyAsync(d_grad_norm, coef, 4, hipMemcpyDeviceToDevice, s), "copy norm");
+    return GPT2_OK;
+}
+
+extern "C" int gpt2_schedule_step_device(gpt2_t* h, int32_t* d_step, float* d_lr, int32_t* d_t, double max_lr,
+                                         double min_lr, int64_t warmup_steps, int64_t max_steps) {
+    if (!h || !d_step || !d_lr || !d_t) return set_error(GPT2_EINVAL, "null argument");
+    if (warmup_steps < 1 || max_steps <= warmup_steps) return set_error(GPT2_EINVAL, "need 1 <= warmup_steps < max_steps");
+    HIPTRY(schedule_step(d_step, d_lr, d_t, max_lr, min_lr, warmup_steps, max_steps, h->stream), "schedule");
     return GPT2_OK;
 }
 

@@ -147,9 +147,15 @@ hipError_t embed_backward_sort(const int32_t* idx, int rows, void* scratch, hipS
 int norm_blocks();
 hipError_t grad_norm(const float* g, int64_t n, float* partial, float* d_norm_coef /* [2] */,
                      float max_norm, hipStream_t s);
+// (d_hp, when not null: device (lr, bc1, bc2_sqrt) that replace the three scalars)
 hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow_bf16, int64_t n,
                  int64_t n_decay, const float* d_norm_coef, float lr, float beta1, float beta2,
-                 float eps, float wd, float bc1, float bc2_sqrt, hipStream_t s);
+                 float eps, float wd, float bc1, float bc2_sqrt, const float* d_hp, hipStream_t s);
+// d_hp = (*d_lr, 1 - beta1^*d_t, sqrt(1 - beta2^*d_t)) in device memory
+hipError_t adamw_hparams(const float* d_lr, const int32_t* d_t, float beta1, float beta2, float* d_hp, hipStream_t s);
+// the learning-rate schedule advanced in device memory (see the kernel)
+hipError_t schedule_step(int32_t* d_step, float* d_lr, int32_t* d_t, double max_lr, double min_lr, int64_t warmup,
+                         int64_t max_steps, hipStream_t s);
 hipError_t refresh_shadow(const float* p, void* shadow_bf16, int64_t n, hipStream_t s);
 
 // device init: counter-based normals (Philox-4x32-10 + Box-Muller) times std, or constants

@@ -1151,8 +1151,14 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ shadow, int64_t n4, int64_t n_decay4,
                                                     const float* __restrict__ norm_coef, float lr, float beta1,
-                                                    float beta2, float eps, float wd, float bc1, float bc2_sqrt) {
+                                                    float beta2, float eps, float wd, float bc1, float bc2_sqrt,
+                                                    const float* __restrict__ hp) {
     const float c = norm_coef[1];
+    if (hp) {   // (lr, bc1, sqrt(bc2)) from device memory, as the schedule left them
+        lr = hp[0];
+        bc1 = hp[1];
+        bc2_sqrt = hp[2];
+    }
     const float step = lr / bc1, inv_bc2_sqrt = 1.0f / bc2_sqrt, kd = 1.0f - lr * wd;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n4; i0 += AW_UNROLL * stride) {
@@ -1178,10 +1184,53 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
 
 hipError_t adamw(float* p, const float* g, float* m, float* v, void* shadow, int64_t n, int64_t n_decay,
                  const float* d_norm_coef, float lr, float beta1, float beta2, float eps, float wd, float bc1,
-                 float bc2_sqrt, hipStream_t s) {
+                 float bc2_sqrt, const float* d_hp, hipStream_t s) {
     if ((n & 3) || (n_decay & 3)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(adamw_kernel, dim3(4096), dim3(256), 0, s, p, g, m, v, (bf16*)shadow, n / 4, n_decay / 4,
-                       d_norm_coef, lr, beta1, beta2, eps, wd, bc1, bc2_sqrt);
+                       d_norm_coef, lr, beta1, beta2, eps, wd, bc1, bc2_sqrt, d_hp);
+    return hipGetLastError();
+}
+
+// AdamW's per-step scalars from a learning rate and step count in device memory: hp = (lr,
+// 1 - beta1^t, sqrt(1 - beta2^t)), computed in double and rounded once, as the host path does.
+__global__ void adamw_hparams_kernel(const float* __restrict__ d_lr, const int32_t* __restrict__ d_t, double beta1,
+                                     double beta2, float* __restrict__ hp) {
+    if (threadIdx.x != 0) return;
+    const double t = (double)*d_t;
+    hp[0] = *d_lr;
+    hp[1] = (float)(1.0 - pow(beta1, t));
+    hp[2] = (float)sqrt(1.0 - pow(beta2, t));
+}
+hipError_t adamw_hparams(const float* d_lr, const int32_t* d_t, float beta1, float beta2, float* d_hp, hipStream_t s) {
+    hipLaunchKernelGGL(adamw_hparams_kernel, dim3(1), dim3(64), 0, s, d_lr, d_t, (double)beta1, (double)beta2, d_hp);
+    return hipGetLastError();
+}
+
+// One step of the learning-rate schedule in device memory: with it = *d_step, *d_lr = the
+// schedule's rate at it (linear warmup, cosine decay to min_lr, min_lr after max_steps; the
+// same double arithmetic as the host function), *d_t = it + 1 (AdamW's step count), and
+// *d_step = it + 1.
+__global__ void schedule_step_kernel(int32_t* __restrict__ d_step, float* __restrict__ d_lr, int32_t* __restrict__ d_t,
+                                     double max_lr, double min_lr, int64_t warmup, int64_t max_steps) {
+    if (threadIdx.x != 0) return;
+    const int64_t it = *d_step;
+    double lr;
+    if (it < warmup) {
+        lr = max_lr * (double)(it + 1) / (double)warmup;
+    } else if (it > max_steps) {
+        lr = min_lr;
+    } else {
+        const double ratio = (double)(it - warmup) / (double)(max_steps - warmup);
+        lr = min_lr + 0.5 * (1.0 + cos(3.14159265358979323846 * ratio)) * (max_lr - min_lr);
+    }
+    *d_lr = (float)lr;
+    *d_t = (int32_t)(it + 1);
+    *d_step = (int32_t)(it + 1);
+}
+hipError_t schedule_step(int32_t* d_step, float* d_lr, int32_t* d_t, double max_lr, double min_lr, int64_t warmup,
+                         int64_t max_steps, hipStream_t s) {
+    hipLaunchKernelGGL(schedule_step_kernel, dim3(1), dim3(64), 0, s, d_step, d_lr, d_t, max_lr, min_lr, warmup,
+                       max_steps);
     return hipGetLastError();
 }
 
