@@ -606,7 +606,8 @@ def main():
             "dtype": "bf16 (bf16 residual stream)", "value": round(v["value"], 1), "unit": "tokens/s",
             "ms_per_step": round(v["ms_step"], 3), "mfu": round(v["value"] * fpt / PEAK_BF16, 4),
             "steps": max(5, args.steps // 2), "warmup": 2,
-            "note": "residual stream and its gradient stored in bf16: narrower than the autocast recipe"}
+            "note": "residual stream and its gradient stored in bf16: narrower than the autocast recipe; "
+                    "timed as separate launches (compare with timing.eager)"}
     if args.copy_calib:
         dev = torch.device("cuda:0")
         src = torch.empty(args.copy_calib, dtype=torch.uint8, device=dev)
