@@ -175,7 +175,7 @@ TRAFFIC_CLASSES = {
     "gemm_qkv": ("gemm_mm_kernel<0, 0, 0,", "max"),
     "gemm_lm_head_dw": ("gemm_mm_kernel<1, 1, 4,", None),
     "gemm_dw": ("gemm_mm_group_kernel", None),
-    "cross_entropy": ("cross_entropy_tiled_kernel", None),
+    "cross_entropy": (("ce_rows_kernel", "ce_grad_kernel"), "sum"),   # its row pass + gradient pass
     "adamw": ("adamw_kernel", None),
     "attn_fwd": ("attn_fwd_ts_kernel", None),
     "layernorm_fwd": ("add_layernorm_forward_kernel", None),
@@ -223,7 +223,7 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
             out, after_ce = [], False
             for d in sorted(per):
                 k = meta[d][0]
-                if "cross_entropy_tiled_kernel" in k:
+                if "ce_grad_kernel" in k:
                     after_ce = True
                 elif name[1] in k:
                     if after_ce:
@@ -242,6 +242,15 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
 
     classes = {}
     for cls, (name, rule) in TRAFFIC_CLASSES.items():
+        if rule == "sum":   # a class of several kernels, one launch of each per class launch
+            parts = [(select(fetch, fmeta, n, None), select(write, wmeta, n, None)) for n in name]
+            if not all(fd and wd for fd, wd in parts):
+                continue
+            fb = sum(sum(fetch[d] for d in fd) / len(fd) for fd, _ in parts) * 1024.0 * sf
+            wb = sum(sum(write[d] for d in wd) / len(wd) for _, wd in parts) * 1024.0 * sw
+            classes[cls] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                            "dispatches": len(parts[-1][0])}
+            continue
         fd, wd = select(fetch, fmeta, name, rule), select(write, wmeta, name, rule)
         if not fd or not wd:
             continue
@@ -284,7 +293,8 @@ def symbol_costs(w, B, n_params, n_decay):
          2 * L * (BT * C * (2 * 4 + 2 * 2) + 8 * BT)),
         ("layernorm_forward_kernel", "first LayerNorm forward", "byte", BT * C * (4 + 2) + 8 * BT),
         ("layernorm_backward_kernel", "LayerNorm backward", "byte", cc["layernorm_bwd"][1]),
-        ("cross_entropy_tiled_kernel", "softmax cross-entropy", "byte", cc["cross_entropy"][1]),
+        ("ce_rows_kernel", "cross-entropy row pass (log-sum-exp, loss)", "byte", BT * (Vp // 192) * 8),
+        ("ce_grad_kernel", "cross-entropy gradient over the logits", "byte", cc["cross_entropy"][1] - BT * (Vp // 192) * 8),
         ("adamw_kernel", "AdamW", "byte", cc["adamw"][1]),
         ("norm_partial_kernel", "grad norm", "byte", cc["grad_norm"][1]),
         ("embed_forward_kernel", "embedding forward", "byte", cc["embed_fwd"][1]),

@@ -167,7 +167,7 @@ struct Plan {
     // offsets in bytes
     size_t params, grads, m, v, shadow, idx, tgt;
     std::vector<size_t> x_in, x_mid, h1, mean1, rstd1, qkv, att, lse, h2, mean2, rstd2, u, a;
-    size_t hf, meanf, rstdf, logits, lstats, loss_rows, loss, dres, dln, datt, Dbuf;
+    size_t hf, meanf, rstdf, logits, lstats, lse2rows, loss_rows, loss, dres, dln, datt, Dbuf;
     size_t yproj;          // a projection's output with its bias, before the residual add
     // output gradients that feed products: per layer in the bf16 modes (kept for the grouped
     // weight-gradient launch at the end of the backward), one shared buffer in fp32 mode
@@ -220,6 +220,7 @@ Plan make_plan(const gpt2_config* c) {
     P.rstdf = take(BT * 4);
     P.logits = take(BT * Vp * es);
     P.lstats = take(BT * ((Vp + 191) / 192) * 8);   // per row and 192-column tile: (max, sum)
+    P.lse2rows = take(BT * 4);                        // per row: log-sum-exp * log2(e)
     P.loss_rows = take(BT * 4);
     P.loss = take(256);
     P.mask = take(BT);
@@ -717,7 +718,7 @@ static int loss_rows_after_trunk(gpt2_t* h, int BT, float* loss_rows, float* d_l
     return run(h, "cross_entropy", [&] {
         if (h->lm_tiles)
             return cross_entropy_tiled(h->at<char>(P.logits), h->at<float>(P.lstats), h->lm_tiles, tgt, loss_rows,
-                                       d_logits, BT, Vp, h->stream, write_grad);
+                                       h->at<float>(P.lse2rows), d_logits, BT, Vp, h->stream, write_grad);
         return cross_entropy(h->at<char>(P.logits), tgt, loss_rows, d_logits, BT, Vp, h->bf16, h->stream, write_grad);
     });
 }

@@ -118,10 +118,11 @@ hipError_t cross_entropy(void* logits, const int32_t* targets, float* loss_rows,
                          int n_rows, int Vp, int is_bf16, hipStream_t s, int write_grad = 1);
 // the same for bf16 logits whose per-tile softmax statistics the lm_head product produced
 // (EPI_LOGITS: `tiles` (max, sum) pairs per row): one pass over each row instead of two, and
-// none without write_grad or logits_f32
+// none without write_grad or logits_f32; lse2_rows [n_rows] receives each row's log-sum-exp
+// times log2(e) (scratch of the gradient pass)
 hipError_t cross_entropy_tiled(void* logits, const float* stats, int tiles, const int32_t* targets,
-                               float* loss_rows, float* logits_f32, int n_rows, int Vp, hipStream_t s,
-                               int write_grad = 1);
+                               float* loss_rows, float* lse2_rows, float* logits_f32, int n_rows, int Vp,
+                               hipStream_t s, int write_grad = 1);
 // per sequence b of B (T positions): sum, count and mean of loss_rows over the positions the
 // mask selects (mask null: all); rowd [2B] doubles (sum, count); row_sum / row_mean / total
 // may be null; total = mean over every selected position of the batch
