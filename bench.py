@@ -16,8 +16,9 @@ follow the GPT-2 initialization. Prints one JSON line.
   mfu         tokens/s * (6N + 6*L*T*C) / dense bf16 MFMA peak (2.5166e15 FLOP/s)
   roofline    the kernel class with the largest share of step time (every class, single- or
               multi-shape), timed live with HIP events on the library's stream during the
-              eager timed steps: algorithmic FLOPs or bytes per launch (the class's total per
-              step over its launches per step) / mean launch time, against the MI355X peak
+              eager timed steps (a product that is one kernel records them at its own start
+              and end): algorithmic FLOPs or bytes per launch (the class's total per step over
+              its launches per step) / mean launch time, against the MI355X peak
   kernels     ms per step of every kernel class (same live timing)
   cpu_baseline  the CPU oracle (float32 numpy) on one sequence of the same
               model, forward + backward + AdamW, on this host's cores

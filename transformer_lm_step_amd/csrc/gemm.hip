@@ -22,6 +22,8 @@
 // M-grouped range of tiles.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -854,6 +856,32 @@ __global__ void __launch_bounds__(GTHREADS, 2) gemm_mm_group_kernel(GemmArgs bas
 template <int BM, int BN>
 constexpr size_t mm_lds_bytes() { return 2 * (size_t)(BM + BN) * 128; }
 
+// Per-kernel timing: while the caller has handed over an event pair (gemm_time_next), the next
+// product that is a single kernel records them at that kernel's own start and end
+// (hipExtLaunchKernel), so the interval holds the kernel alone, as a kernel trace reports it.
+static thread_local hipEvent_t t_ev0 = nullptr, t_ev1 = nullptr;
+static thread_local bool t_ev_used = false;
+void gemm_time_next(hipEvent_t start, hipEvent_t stop) {
+    t_ev0 = start;
+    t_ev1 = stop;
+    t_ev_used = false;
+}
+bool gemm_time_taken() {
+    const bool used = t_ev_used;
+    t_ev0 = t_ev1 = nullptr;
+    t_ev_used = false;
+    return used;
+}
+// launch `kernel` with the handed-over events, if any are pending (true: launched)
+static bool launch_timed(const void* kernel, dim3 grid, dim3 block, void** args, size_t lds, hipStream_t s,
+                         hipError_t* err) {
+    if (!t_ev0) return false;
+    *err = hipExtLaunchKernel(kernel, grid, block, args, lds, s, t_ev0, t_ev1, 0);
+    t_ev0 = t_ev1 = nullptr;
+    t_ev_used = *err == hipSuccess;
+    return true;
+}
+
 template <int ALAY, int BLAY, int EPI, int BM, int BN>
 static hipError_t launch_mm(const GemmArgs& a, int nsplit, hipStream_t s) {
     const int num_m = (a.M + BM - 1) / BM, num_n = (a.N + BN - 1) / BN;
@@ -863,6 +891,13 @@ static hipError_t launch_mm(const GemmArgs& a, int nsplit, hipStream_t s) {
             gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN, true><<<grid, dim3(GTHREADS), mm_lds_bytes<BM, BN>(), s>>>(a);
             return hipGetLastError();
         }
+    }
+    if (nsplit == 1 && !a.rowsum_part) {   // one kernel: timed alone when events are pending
+        void* args[] = {(void*)&a};
+        hipError_t e;
+        if (launch_timed((const void*)gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN>, grid, dim3(GTHREADS), args,
+                         mm_lds_bytes<BM, BN>(), s, &e))
+            return e;
     }
     gemm_mm_kernel<ALAY, BLAY, EPI, BM, BN><<<grid, dim3(GTHREADS), mm_lds_bytes<BM, BN>(), s>>>(a);
     return hipGetLastError();
@@ -891,10 +926,19 @@ hipError_t gemm_grouped(const GroupProb* d_probs, int nprob, int total_tiles, in
     a.alpha = alpha;
     a.beta = beta;
     a.vec = 1;
-    if (bn == 192)
+    void* args[] = {(void*)&a, (void*)&d_probs, (void*)&nprob};
+    hipError_t e;
+    if (bn == 192) {
+        if (launch_timed((const void*)gemm_mm_group_kernel<192>, dim3(total_tiles), dim3(GTHREADS), args,
+                         mm_lds_bytes<128, 192>(), s, &e))
+            return e;
         gemm_mm_group_kernel<192><<<dim3(total_tiles), dim3(GTHREADS), mm_lds_bytes<128, 192>(), s>>>(a, d_probs, nprob);
-    else
+    } else {
+        if (launch_timed((const void*)gemm_mm_group_kernel<128>, dim3(total_tiles), dim3(GTHREADS), args,
+                         mm_lds_bytes<128, 128>(), s, &e))
+            return e;
         gemm_mm_group_kernel<128><<<dim3(total_tiles), dim3(GTHREADS), mm_lds_bytes<128, 128>(), s>>>(a, d_probs, nprob);
+    }
     return hipGetLastError();
 }
 

@@ -40,6 +40,11 @@ struct GemmDesc {
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+// per-kernel timing of the products: hand over an event pair before a product call; after it,
+// gemm_time_taken() says whether the product was a single kernel that recorded the pair at its
+// own start and end (and forgets the pair either way)
+void gemm_time_next(hipEvent_t start, hipEvent_t stop);
+bool gemm_time_taken();
 // number of 192-column tiles (the C2 row length of EPI_LOGITS) if gemm() can run d with
 // EPI_LOGITS (bf16, both operands k-contiguous, whole 128 x 192 tiles), else 0
 int gemm_logits_tiles(const GemmDesc& d, int is_bf16);
