@@ -259,6 +259,38 @@ def test_step_b16_two_layers_full_gradients(mode):
     st.close()
 
 
+def test_class_timing_same_results():
+    """Per-class timing switched on: every product that is one kernel then launches through
+    hipExtLaunchKernel with its class's event pair (the live roofline figure of the benchmark).
+    The loss and every gradient must be the same bit for bit as with timing off, and every
+    class the step runs must report its launches and a positive time."""
+    note("124M bf16 B=16 L=2 class timing")
+    w = synthetic.workload("gpt2_step", n_layer=2)
+    params = synthetic.init_params(w, randomize_affine=True)
+    x, y = synthetic.micro_batches(w, 1, batch=16)[0]
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    loss0, _ = st.forward(x, y)
+    st.backward(1.0, False)
+    g0 = st.grads()
+    G.gpt2_timing_begin(st.h)
+    loss1, _ = st.forward(x, y)
+    st.backward(1.0, False)
+    G.gpt2_timing_end(st.h)
+    g1 = st.grads()
+    assert loss1 == loss0
+    for k in g0:
+        assert np.array_equal(g0[k], g1[k]), k
+    L = w.n_layer
+    expect = {"gemm_qkv": L, "gemm_attn_proj": L, "gemm_fc": L, "gemm_mlp_proj": L, "gemm_lm_head": 1,
+              "gemm_lm_head_dx": 1, "gemm_lm_head_dw": 1, "gemm_dx": 4 * L, "gemm_dw": 1, "attn_fwd": L,
+              "attn_bwd": L, "cross_entropy": 1, "layernorm_bwd": 2 * L + 1}
+    for cls, n in expect.items():
+        ms, launches = G.gpt2_timing_get(st.h, cls)
+        assert launches == n and ms > 0.0, (cls, launches, ms)
+    st.close()
+
+
 @pytest.mark.parametrize("mode,T", [("fp32", 2048), ("bf16_res16", 2048), ("fp32", 1900)])
 def test_embedding_backward_chunked(mode, T):
     """More rows than one sort chunk of the embedding backward (9 sequences of T tokens:
