@@ -316,6 +316,27 @@ def test_embedding_backward_chunked(mode, T):
         _grads_cosine(st, ref_g)
 
 
+def test_layernorm_backward_partials_sized_for_every_batch():
+    """The LayerNorm backward takes 2 rows per wave for batches of at most 8192 rows and 4
+    above, so a smaller batch can need more blocks (and partial-sum slots) than the largest
+    one: a handle with room for 130 sequences of 64 tokens (8320 rows) runs 128 of them (8192
+    rows, twice the blocks); every gradient against the oracle (fp32 check mode, 1e-4)."""
+    note("LayerNorm backward partial sets, max batch 130, B=128 T=64 fp32")
+    w = synthetic.workload("tiny", batch=128)
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    assert x.shape == (128, 64)
+    p64 = f64(params)
+    out = O.forward(p64, w.n_layer, w.n_head, x, y, want_logits=False)
+    ref_g = O.backward(p64, w.n_layer, w.n_head, out["cache"], 1.0)
+    st = make_step(w, "fp32", max_batch=130)
+    st.set_params(params)
+    loss, _ = st.forward(x, y)
+    st.backward(1.0, False)
+    assert abs(loss - out["loss"]) <= 1e-4 * abs(out["loss"])
+    _grads_fp32_check(st, ref_g)
+
+
 # ------------------------------------------------------------------ full-size invariants
 def test_full_step_b16_invariants():
     """The timed workload itself (B=16, T=1024, bf16): per-sequence logits against the oracle

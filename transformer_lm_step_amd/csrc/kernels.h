@@ -94,6 +94,7 @@ hipError_t layernorm_backward(const void* dh, const void* x, const float* mean, 
                               const float* w, void* dres, void* dres16, int accumulate_dres,
                               float* partial, int nblk, int rows, int C, int dh_bf16, int res_bf16, hipStream_t s);
 int layernorm_backward_blocks(int rows);
+int layernorm_backward_max_blocks(int max_rows);
 // out[c] (+)= sum_blk partial[blk*stride + c] for c < n (fixed order); scratch holds
 // sum_scratch_floats(n) floats
 hipError_t sum_partials(const float* partial, int nblk, int n, int64_t stride, float* out, int accumulate,

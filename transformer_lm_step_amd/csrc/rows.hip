@@ -122,6 +122,9 @@ static hipError_t ln_fwd_launch(int nv4, dim3 g, hipStream_t s, const TX* x, con
     else if (nv4 <= 128) LNF(2);
     else if (nv4 <= 192) LNF(3);
     else if (nv4 <= 256) LNF(4);
+    else if (nv4 <= 320) LNF(5);
+    else if (nv4 <= 384) LNF(6);
+    else if (nv4 <= 448) LNF(7);
     else LNF(8);
 #undef LNF
     return hipGetLastError();
@@ -187,6 +190,9 @@ static hipError_t add_ln_launch(int nv4, dim3 g, hipStream_t s, const TX* xo, co
     else if (nv4 <= 128) ALN(2);
     else if (nv4 <= 192) ALN(3);
     else if (nv4 <= 256) ALN(4);
+    else if (nv4 <= 320) ALN(5);
+    else if (nv4 <= 384) ALN(6);
+    else if (nv4 <= 448) ALN(7);
     else ALN(8);
 #undef ALN
     return hipGetLastError();
@@ -280,10 +286,21 @@ hipError_t layernorm_forward(const void* x, const float* w, const float* b, void
 // and dres = (accumulate ? dres : 0) + dx. With accumulate, the incoming dres is the
 // gradient at the output of the residual add that produced x, so its column sum is the bias
 // gradient of that add's projection; it is collected as a third partial.
-// Each wave takes LNB_ROWS consecutive rows; the block's 4 wave partials are combined in a
+// Each wave takes lnb_rows(rows) consecutive rows; the block's 4 wave partials are combined in a
 // fixed order into partial[blk][0:3C] = (dw, db, colsum(dres_in)), finished by sum_partials.
 constexpr int LNB_ROWS = 4;
-int layernorm_backward_blocks(int rows) { return (rows + 4 * LNB_ROWS - 1) / (4 * LNB_ROWS); }
+// Rows per wave: LNB_ROWS, or 2 for batches of at most 8192 rows, so that a batch of 4096 rows
+// (the 1558M-shaped step at B=4, C = 1600: 7 float4 per lane, whose registers and LDS allow two
+// workgroups per CU) fills all 512 workgroup slots in one round instead of half of them (3.84
+// -> 2.72 ms per step at that shape; 16,384 rows at C = 768 measured slower with 2).
+static int lnb_rows(int rows) { return rows <= 8192 ? 2 : LNB_ROWS; }
+int layernorm_backward_blocks(int rows) { const int k = lnb_rows(rows); return (rows + 4 * k - 1) / (4 * k); }
+// The most blocks any batch of at most max_rows rows takes (the count is not monotonic across
+// the 8192-row switch of lnb_rows): what the partial sets are sized for.
+int layernorm_backward_max_blocks(int max_rows) {
+    const int a = layernorm_backward_blocks(max_rows), b = layernorm_backward_blocks(max_rows < 8192 ? max_rows : 8192);
+    return a > b ? a : b;
+}
 
 // NV = float4 per lane needed for C (C <= 256 * NV); sized to C so the row lives in registers.
 // TD: type of dh (the operand type); TX: type of x and of the residual gradient dres (fp32, or
@@ -293,7 +310,7 @@ template <typename TD, typename TX, int NV>
 __global__ void __launch_bounds__(256) layernorm_backward_kernel(
     const TD* __restrict__ dh, const TX* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, TX* __restrict__ dres, bf16* __restrict__ dres16,
-    int accumulate, float* __restrict__ partial, int rows, int C) {
+    int accumulate, float* __restrict__ partial, int rows, int C, int nrw) {
     extern __shared__ float sred[];  // [4][3C]
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int nv = C >> 2;
@@ -304,8 +321,8 @@ __global__ void __launch_bounds__(256) layernorm_backward_kernel(
         const int c = lane + 64 * j;
         wv[j] = c < nv ? ((const float4*)w)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    const int r0 = (blockIdx.x * 4 + wave) * LNB_ROWS;
-    for (int row = r0; row < r0 + LNB_ROWS && row < rows; ++row) {
+    const int r0 = (blockIdx.x * 4 + wave) * nrw;
+    for (int row = r0; row < r0 + nrw && row < rows; ++row) {
         const float mu = mean[row], r = rstd[row];
         const TD* dr = dh + (int64_t)row * C;
         const TX* xr = x + (int64_t)row * C;
@@ -364,11 +381,14 @@ static hipError_t ln_bwd_launch(int nv4, dim3 g, size_t lds, hipStream_t s, cons
                                 const float* mean, const float* rstd, const float* w, TX* dres, bf16* dres16, int acc,
                                 float* partial, int rows, int C) {
 #define LNB(NV) hipLaunchKernelGGL((layernorm_backward_kernel<TD, TX, NV>), g, dim3(256), lds, s, dh, x, mean, rstd, w, \
-                                   dres, dres16, acc, partial, rows, C)
+                                   dres, dres16, acc, partial, rows, C, lnb_rows(rows))
     if (nv4 <= 64) LNB(1);
     else if (nv4 <= 128) LNB(2);
     else if (nv4 <= 192) LNB(3);
     else if (nv4 <= 256) LNB(4);
+    else if (nv4 <= 320) LNB(5);
+    else if (nv4 <= 384) LNB(6);
+    else if (nv4 <= 448) LNB(7);
     else LNB(8);
 #undef LNB
     return hipGetLastError();
