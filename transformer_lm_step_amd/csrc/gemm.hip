@@ -1135,10 +1135,13 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if constexpr (sizeof(T) == 2) {
         if (!d.no_dl && mm_ok(d, a.ksplit_len)) {
             if (d.rowsum && d.a_layout == 1) a.rowsum_part = d.rowsum_part;
-            // 128x192 tiles (wave tile 64x96: fewer LDS bytes per MFMA) whenever N is a multiple
-            // of 192 and they fill whole rounds of 512 workgroups (two per CU) about as well as
-            // 128x128 tiles: N = 768 gives 512 tiles instead of 768, N = 2304 three rounds
-            // instead of 4.5, N = 50304 = 262 x 192. 256x256 tiles measured slower everywhere.
+            // 128x192 tiles (wave tile 64x96: fewer LDS bytes per MFMA) where, at the 128x192
+            // tile's measured 1.15 times the rate per output of 128x128, they use the rounds of
+            // 512 workgroups (two per CU) and the output area better: N = 768 gives 512 tiles
+            // instead of 768, N = 2304 three rounds instead of 4.5, N = 50304 = 262 x 192; ragged
+            // N = 6400 (1558M-shaped MLP) 3 rounds instead of 4 (c_fc 6.11 -> 5.92 ms per step);
+            // N = 1600 at 4096 rows stays 128-wide (416 tiles against 288: 128x192 measured
+            // slower there). 256x256 tiles measured slower everywhere.
             bool wide = false, narrow = false;
             if (epi == EPI_LOGITS) {
                 wide = true;
@@ -1146,12 +1149,14 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
                 wide = d.bn == 192;
                 narrow = d.bn == 64;
             } else if (nsplit == 1) {
+                // fraction of the launched rounds' output area that is the product's own
                 auto fill = [&](int bn) {
-                    const int64_t blocks = (int64_t)((d.M + 127) / 128) * ((d.N + bn - 1) / bn);
+                    const int64_t nt = (d.N + bn - 1) / bn;
+                    const int64_t blocks = (int64_t)((d.M + 127) / 128) * nt;
                     const int64_t rounds = (blocks + 511) / 512;
-                    return (double)blocks / (double)(rounds * 512);
+                    return (double)blocks / (double)(rounds * 512) * (double)d.N / (double)(nt * bn);
                 };
-                if (d.N % 192 == 0) wide = fill(192) >= fill(128) - 0.02;
+                if (d.N % 64 == 0) wide = 1.15 * fill(192) >= fill(128);
                 // 128x64 tiles (48 KB of LDS: three workgroups per CU) where 128-wide tiles
                 // would leave CUs without a workgroup (few rows: a batch of 4 sequences, the
                 // forward-only pass): more workgroups at more LDS bytes per MFMA
