@@ -11,7 +11,8 @@ follow the GPT-2 initialization. Prints one JSON line.
   value       tokens/s of the whole job (one GPU): training steps timed as replays of the
               whole step captured once in a HIP graph (schedule on the device, forward,
               backward, AdamW with device-side scalars; the next batch copied in before each
-              replay), or as separate launches with --no-graph or where capture fails
+              replay; --mode eval: one forward-only scoring pass captured the same way), or as
+              separate launches with --no-graph or where capture fails
   timing      which of the two `value` is, and the separate-launch figure ("eager")
   mfu         tokens/s * (6N + 6*L*T*C) / dense bf16 MFMA peak (2.5166e15 FLOP/s)
   roofline    the kernel class with the largest share of step time (every class, single- or
@@ -445,6 +446,44 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
                 "launch_ms": round(ms / n, 4), "launches_per_step": n / steps, "per_launch": per_launch,
                 "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
     graph = None
+    if graph_steps and args.mode == "eval":
+        # one forward-only scoring pass captured once in a HIP graph and replayed, the next batch
+        # copied into the captured input buffers before each replay (as for the training step)
+        try:
+            orig = st.stream
+            gx, gy = torch.empty_like(xs[0]), torch.empty_like(ys[0])
+            gno = [step_no[0]]
+
+            def load_next():
+                j = gno[0] % nb
+                gx.copy_(xs[j])
+                gy.copy_(ys[j])
+                gno[0] += 1
+
+            g = torch.cuda.CUDAGraph()
+            load_next()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                G.gpt2_set_stream(h, torch.cuda.current_stream().cuda_stream)
+                G.gpt2_evaluate(h, gx.data_ptr(), gy.data_ptr(), None, B, T, None, None, d_loss.data_ptr())
+            G.gpt2_set_stream(h, orig)
+            for _ in range(2):
+                load_next()
+                g.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(graph_steps):
+                load_next()
+                g.replay()
+            torch.cuda.synchronize()
+            ge = time.perf_counter() - t1
+            graph = {"ms_per_step": ge / graph_steps * 1e3, "steps": graph_steps, "value": B * T / (ge / graph_steps)}
+            del g
+        except Exception as e:
+            G.gpt2_set_stream(h, st.stream)
+            torch.cuda.synchronize()
+            print(f"bench.py: HIP graph leg skipped ({e})", file=sys.stderr)
+            graph = None
     if graph_steps and args.mode == "train":
         # The whole training step -- the learning-rate schedule advanced on the device, the k
         # micro-steps, AdamW with its scalars read from device memory -- captured once in a HIP
@@ -566,8 +605,9 @@ def main():
     r = run_workload(args, w, args.dtype, args.steps, args.warmup, kernel_timing=not args.no_kernel_timing,
                      graph_steps=0 if args.no_graph else args.steps)
     k = r["k"]
-    # `value`: the training step as a HIP-graph replay when the capture succeeded (the same
-    # kernels and bytes as the eager launch sequence, without the per-launch gaps), else eager
+    # `value`: the training step (or scoring pass) as a HIP-graph replay when the capture
+    # succeeded (the same kernels and bytes as the eager launch sequence, without the per-launch
+    # gaps), else eager
     g = r["graph"]
     value, ms_step = (g["value"], g["ms_per_step"]) if g else (r["value"], r["ms_step"])
     fpt = model_flops_per_token(w, r["n_params"], args.mode)
@@ -600,6 +640,14 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    if args.mode == "eval":
+        out["timing"] = {
+            "timed": "hip_graph" if g else "eager",
+            "eager": {"ms_per_step": round(r["ms_step"], 3), "value": round(r["value"], 1), "steps": args.steps},
+            "note": ("one forward-only scoring pass captured once in a HIP graph; each timed pass copies the "
+                     "next batch into the captured input buffers and replays it. `eager` times the same "
+                     "passes as separate launches" if g else
+                     "the pass as separate launches (no HIP-graph leg: --no-graph or capture unavailable)")}
     if args.mode == "train":
         out["timing"] = {
             "timed": "hip_graph" if g else "eager",

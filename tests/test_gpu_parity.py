@@ -651,6 +651,47 @@ def test_hip_graph_replay_matches_eager():
     st.close()
 
 
+def test_hip_graph_evaluate_replay_matches_eager():
+    """A forward-only scoring pass (gpt2_evaluate: the same forward, per-position losses and the
+    per-sequence reduction) captured in a HIP graph and replayed three times, with eager passes
+    on other inputs and synchronizations between the replays: every replay's mean loss and
+    per-sequence sums equal the eager pass on the captured inputs bit for bit."""
+    note("hip graph replay of gpt2_evaluate")
+    w = synthetic.workload("gpt2_step", n_layer=2, batch=4, seq_len=256, block_size=256)
+    params = synthetic.init_params(w, randomize_affine=True)
+    st = make_step(w, "bf16")
+    st.set_params(params)
+    (x, y), (x2, y2) = synthetic.micro_batches(w, 2)
+    B, T = x.shape
+    xd, yd = torch.from_numpy(x).cuda(), torch.from_numpy(y).cuda()
+    xd2, yd2 = torch.from_numpy(x2).cuda(), torch.from_numpy(y2).cuda()
+    d_loss = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_sum = torch.zeros(B, dtype=torch.float32, device="cuda")
+
+    def ev(a, b):
+        G.gpt2_evaluate(st.h, a.data_ptr(), b.data_ptr(), None, B, T, d_sum.data_ptr(), None, d_loss.data_ptr())
+
+    ev(xd, yd)
+    torch.cuda.synchronize()
+    ref_loss, ref_sum = d_loss.clone(), d_sum.clone()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        G.gpt2_set_stream(st.h, torch.cuda.current_stream().cuda_stream)
+        ev(xd, yd)
+    G.gpt2_set_stream(st.h, st.stream)
+    for rep in range(3):
+        ev(xd2, yd2)                      # eager work in between, on other inputs
+        torch.cuda.synchronize()
+        assert not torch.equal(d_loss, ref_loss)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d_loss, ref_loss), rep
+        assert torch.equal(d_sum, ref_sum), rep
+    del graph
+    st.close()
+
+
 def test_evaluate_tiny_fp32_matches_oracle():
     """Forward-only scores in fp32 check mode: per-row sums and means over a ragged mask (one
     row selects nothing, one row everything) and the masked batch mean against the oracle
