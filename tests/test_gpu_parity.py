@@ -139,15 +139,24 @@ def test_124m_forward_fp32_check_mode():
 
 
 def test_124m_forward_bf16_loss_b4():
+    """The 124M forward at B=4 (4,096 rows: the N = 768 products take the few-row 128x64
+    tiles): loss against the oracle, and the logits of the last sequence at every position
+    (the oracle's forward of that sequence alone) by cosine."""
     note("124M bf16 forward B=4")
     w = synthetic.workload("gpt2_fwd")
     params = synthetic.init_params(w)
     (x, y), = synthetic.micro_batches(w, 1)
-    out = O.forward(f64(params), w.n_layer, w.n_head, x, y, want_logits=False, want_cache=False)
+    p64 = f64(params)
+    out = O.forward(p64, w.n_layer, w.n_head, x, y, want_logits=False, want_cache=False)
     st = make_step(w, "bf16")
     st.set_params(params)
-    loss, _ = st.forward(x, y)
+    loss, logits = st.forward(x, y, want_logits=True)
     assert abs(loss - float(out["loss"])) <= 2e-2, (loss, out["loss"])
+    b = x.shape[0] - 1
+    ref = O.forward(p64, w.n_layer, w.n_head, x[b:b + 1], y[b:b + 1], want_cache=False)["logits"][0]
+    lg = logits[b].float().cpu().numpy()
+    for t in range(0, x.shape[1]):
+        assert cosine(lg[t], ref[t]) >= 0.999, t
 
 
 @pytest.mark.parametrize("mode", BF16_MODES)
