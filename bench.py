@@ -154,14 +154,17 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def traffic_for(kernel_class):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources."""
+def traffic_for(kernel_class, workload, mode):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on the current sources and
+    on this workload (the counters are taken on the default training workload)."""
+    if mode != "train":
+        return None
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        if rec.get("source_sha256") != sources_sha256():
+        if rec.get("source_sha256") != sources_sha256() or rec.get("workload", "gpt2_step") != workload:
             return None
         c = rec["classes"].get(kernel_class)
         return c["bytes_per_launch"] if c else None
@@ -262,7 +265,7 @@ def traffic_from(fetch_csv, write_csv, copy_bytes, out_path):
                         "dispatches": len(fd)}
     rec = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
                      "scaled by the ratio of a device copy's known bytes to what the counter read for it",
-           "source_sha256": sources_sha256(), "copy_bytes": copy_bytes,
+           "source_sha256": sources_sha256(), "workload": "gpt2_step", "copy_bytes": copy_bytes,
            "copy_scale": {"fetch": round(sf, 4), "write": round(sw, 4)}, "classes": classes}
     with open(out_path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -442,7 +445,7 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
             achieved, peak, unit, bound = per_launch / avg_s / 1e9, PEAK_HBM / 1e9, "GB/s", "hbm"
         roof = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": round(peak, 1),
                 "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic_for(dominant) if not res16 else None,
+                "traffic": traffic_for(dominant, w.name, args.mode) if not res16 else None,
                 "launch_ms": round(ms / n, 4), "launches_per_step": n / steps, "per_launch": per_launch,
                 "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
     graph = None
