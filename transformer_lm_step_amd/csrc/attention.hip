@@ -761,12 +761,12 @@ __global__ void __launch_bounds__(A_THREADS, QB <= 2 ? 3 : 2) attn_fwd_ts_kernel
 }
 
 // dK, dV for 64 * KBW keys per workgroup (16 * KBW per wave), streaming 64-query chunks of Q, dO,
-// lse, D.
+// -lse, -D.
 template <int KBW>
 __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_kernel(const bf16* __restrict__ qkv,
                                                                     const bf16* __restrict__ dy,
-                                                                    const float* __restrict__ lse2,
-                                                                    const float* __restrict__ D,
+                                                                    const float* __restrict__ neg_lse2,
+                                                                    const float* __restrict__ neg_D,
                                                                     bf16* __restrict__ dqkv, int T_, int H, float sc,
                                                                     float scale) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // [stage][Q | dO | lse | D]
@@ -779,8 +779,8 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
     const int64_t ld = 3 * (int64_t)C;
     const bf16* base = qkv + (int64_t)b * T_ * ld;
     const bf16* dyb = dy + (int64_t)b * T_ * C;
-    const float* lse_bh = lse2 + (int64_t)bh * T_;   // base-2 log-sum-exp
-    const float* D_bh = D + (int64_t)bh * T_;
+    const float* lse_bh = neg_lse2 + (int64_t)bh * T_;   // minus the base-2 log-sum-exp
+    const float* D_bh = neg_D + (int64_t)bh * T_;         // minus D
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, g = lane >> 4;
@@ -835,12 +835,12 @@ __global__ void __launch_bounds__(A_THREADS, KBW == 1 ? 3 : 2) attn_bwd_dkv_ts_k
         // kernel)
         bf16x8 qa[4], oa[4];
         // s = scale * score - L (base 2), dp = dP - D, per query row q0 + 16qb + 4g + i: the
-        // offsets start the accumulators
+        // offsets (-L and -D as the dQ kernel stored them) start the accumulators
         floatx4 s[4][KBW], dp[4][KBW];
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) {
-            const floatx4 nl = -*(const floatx4*)(sL + qb * 16 + g * 4);
-            const floatx4 nd = -*(const floatx4*)(sD + qb * 16 + g * 4);
+            const floatx4 nl = *(const floatx4*)(sL + qb * 16 + g * 4);
+            const floatx4 nd = *(const floatx4*)(sD + qb * 16 + g * 4);
 #pragma unroll
             for (int kb = 0; kb < KBW; ++kb) {
                 s[qb][kb] = nl;
@@ -975,11 +975,12 @@ __global__ void __launch_bounds__(A_THREADS, QBW == 1 ? 4 : 2) attn_bwd_dq_ts_ke
         dsum += __shfl_xor(dsum, 32);
         L[qb] = ok ? lse[(int64_t)bh * T_ + q] * kLog2e : 0.f;
         Dq[qb] = ok ? dsum : 0.f;
-        // for the dK/dV kernel, which runs next: D, and after all B*H*T of them the log-sum-exp
-        // already in base 2 (one multiply per query here instead of one per score there)
+        // for the dK/dV kernel, which runs next: -D, and after all B*H*T of them the log-sum-exp
+        // already in base 2 and negated (one multiply per query here instead of one per score
+        // there; negated, they are the accumulators' starting values as loaded)
         if (ok && g == 0) {
-            D[(int64_t)bh * T_ + q] = dsum;
-            D[(int64_t)gridDim.y * T_ + (int64_t)bh * T_ + q] = L[qb];
+            D[(int64_t)bh * T_ + q] = -dsum;
+            D[(int64_t)gridDim.y * T_ + (int64_t)bh * T_ + q] = -L[qb];
         }
     }
     floatx4 dq[4][QBW];
