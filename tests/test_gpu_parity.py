@@ -325,6 +325,31 @@ def test_embedding_backward_chunked(mode, T):
         _grads_cosine(st, ref_g)
 
 
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+@pytest.mark.parametrize("C,H", [(1280, 20), (1408, 22)])
+def test_wide_rows(C, H, mode):
+    """Widths whose LayerNorm rows take 5 and 6 float4 per lane (C = 1280, the GPT-2 large
+    width, and C = 1408): one layer, B=2, T=64, loss and every gradient against the oracle
+    (fp32 check mode at 1e-4; bf16 at the bf16 bars), 64-wide heads, a 256-token vocabulary."""
+    note(f"wide rows {mode} C={C}")
+    w = synthetic.workload("tiny", n_layer=1, n_head=H, n_embd=C, batch=2)
+    params = synthetic.init_params(w, randomize_affine=True)
+    (x, y), = synthetic.micro_batches(w, 1)
+    p64 = f64(params)
+    out = O.forward(p64, w.n_layer, w.n_head, x, y, want_logits=False)
+    ref_g = O.backward(p64, w.n_layer, w.n_head, out["cache"], 1.0)
+    st = make_step(w, mode)
+    st.set_params(params)
+    loss, _ = st.forward(x, y)
+    st.backward(1.0, False)
+    if mode == "fp32":
+        assert abs(loss - out["loss"]) <= 1e-4 * abs(out["loss"])
+        _grads_fp32_check(st, ref_g)
+    else:
+        assert abs(loss - out["loss"]) <= 2e-2
+        _grads_cosine(st, ref_g)
+
+
 def test_layernorm_backward_partials_sized_for_every_batch():
     """The LayerNorm backward takes 2 rows per wave for batches of at most 8192 rows and 4
     above, so a smaller batch can need more blocks (and partial-sum slots) than the largest
