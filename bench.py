@@ -361,7 +361,7 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
     n_params = st.n_params
     n_decay = G.gpt2_decay_end(cfg)
     k = w.micro_steps
-    nb = max(2, k)
+    nb = max(8, k)   # distinct token batches cycled through (the loss then does not just memorize one)
     batches = synthetic.micro_batches(w, nb)
     dev = torch.device("cuda:0")
     xs = [torch.from_numpy(b[0]).to(dev) for b in batches]

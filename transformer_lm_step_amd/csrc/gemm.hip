@@ -321,7 +321,9 @@ __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_
 // its j-th value, so when the group addresses 4 k-rows x 16 columns every lane receives 4
 // consecutive k of one column. Both swizzles make those reads free of bank conflicts.
 // Two stages: the loads of tile kt+1 are issued right after the barrier that opens the
-// multiplication of tile kt and are waited for (vmcnt) before the next barrier.
+// multiplication of tile kt and are waited for (vmcnt) before the next barrier. (The few-row
+// 128x64 tiles keep three: tile kt+2 is issued there, and the wait leaves tile kt+1's loads
+// in flight.)
 constexpr int MM_BK = 64;   // bf16 elements of K per tile (128 bytes)
 // compute units of the device (set by gemm_setup; 256 on MI355X)
 static int kGemmCUs = 256;
@@ -724,6 +726,18 @@ DEV void store_staged(const GemmArgs& p, const floatx4 (&acc)[FM][FN], char* sme
     }
 }
 
+// K stages in LDS: two (one tile multiplied while the next is loaded), three for the
+// few-row 128x64 tiles (72 KB, still two workgroups per CU), whose short main loops otherwise
+// wait on each tile's load latency (B=4 MLP projection 44 -> 40 us)
+template <int BM, int BN>
+constexpr int mm_nst() { return BN == 64 ? 3 : 2; }
+// s_waitcnt vmcnt(N) lgkmcnt(0), then the barrier (N of this wave's direct loads may stay in flight)
+template <int N>
+DEV void dma_wait_barrier_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | ((N >> 4) << 14));
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 // One output tile of the LDS-streamed path: workgroup `pid` of `nwg` over the tiles of p, K
 // split `split` (a plain launch passes blockIdx.x, gridDim.x, blockIdx.y; a grouped launch its
 // product's own numbering).
@@ -763,21 +777,37 @@ DEV void mm_tile(const GemmArgs& p, int pid, int nwg, int split, char* smem, boo
     for (int i = 0; i < (ROWSUM ? FM : 1); ++i) rs[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     const bool do_rs = ROWSUM && (p.rowsum_part || p.rowsum_out) && tn == 0 && wn == 0;
 
+    constexpr int NST = mm_nst<BM, BN>();
     if (nt > 0) {
         mm_issue<BM>(baseA, offA, lds0, wave);
         mm_issue<BN>(baseB, offB, lds0 + BM * 128, wave);
+    }
+    if (NST == 3 && nt > 1) {
+        mm_issue<BM>(baseA + stepA, offA, lds0 + STAGE, wave);
+        mm_issue<BN>(baseB + stepB, offB, lds0 + STAGE + BM * 128, wave);
     }
     for (int kt = 0; kt < nt; ++kt) {
         // tile kt is in LDS once this wave's loads have landed and every wave has passed the
         // barrier, which also retires every read of the stage refilled next; a bare barrier
         // (no fence) keeps the prefetch below in flight
-        dma_wait_barrier();
-        if (kt + 1 < nt) {
-            const uint32_t st = lds0 + ((kt + 1) & 1) * STAGE;
-            mm_issue<BM>(baseA + (kt + 1) * stepA, offA, st, wave);
-            mm_issue<BN>(baseB + (kt + 1) * stepB, offB, st + BM * 128, wave);
+        if constexpr (NST == 3) {
+            // tiles kt and kt + 1 in flight: wait for all but tile kt + 1's loads
+            if (kt + 1 < nt) dma_wait_barrier_vm<(BM + BN) / 32>();
+            else dma_wait_barrier();
+            if (kt + 2 < nt) {
+                const uint32_t st = lds0 + ((kt + 2) % 3) * STAGE;
+                mm_issue<BM>(baseA + (kt + 2) * stepA, offA, st, wave);
+                mm_issue<BN>(baseB + (kt + 2) * stepB, offB, st + BM * 128, wave);
+            }
+        } else {
+            dma_wait_barrier();
+            if (kt + 1 < nt) {
+                const uint32_t st = lds0 + ((kt + 1) & 1) * STAGE;
+                mm_issue<BM>(baseA + (kt + 1) * stepA, offA, st, wave);
+                mm_issue<BN>(baseB + (kt + 1) * stepB, offB, st + BM * 128, wave);
+            }
         }
-        const char* As = smem + (kt & 1) * STAGE;
+        const char* As = smem + (NST == 3 ? kt % 3 : kt & 1) * STAGE;
         const char* Bs = As + BM * 128;
         // raised priority while this wave multiplies: the other wave on the SIMD (from the other
         // workgroup) issues its loads in the gaps instead of interleaving its own MFMA chain
@@ -854,7 +884,7 @@ __global__ void __launch_bounds__(GTHREADS, 2) gemm_mm_group_kernel(GemmArgs bas
 }
 
 template <int BM, int BN>
-constexpr size_t mm_lds_bytes() { return 2 * (size_t)(BM + BN) * 128; }
+constexpr size_t mm_lds_bytes() { return mm_nst<BM, BN>() * (size_t)(BM + BN) * 128; }
 
 // Per-kernel timing: while the caller has handed over an event pair (gemm_time_next), the next
 // product that is a single kernel records them at that kernel's own start and end
