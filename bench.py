@@ -374,10 +374,11 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
     if args.mode == "decode":
         prompt_len = 8
         n_dec = warmup + max(1, min(5, steps)) + steps
-        if prompt_len + n_dec > T:
-            raise SystemExit(f"bench.py: {prompt_len} + {n_dec} decoding positions exceed block_size {T}")
+        n_graph = graph_steps + 2 if graph_steps else 0
+        if prompt_len + n_dec + n_graph > T:
+            raise SystemExit(f"bench.py: {prompt_len} + {n_dec + n_graph} decoding positions exceed block_size {T}")
         gen = torch.Generator().manual_seed(w.seed_base + 3000)
-        uni = torch.rand((n_dec, B), generator=gen).to(dev)
+        uni = torch.rand((n_dec + n_graph, B), generator=gen).to(dev)
         toks = [xs[0][:, t].contiguous() for t in range(prompt_len)]
         G.gpt2_decode_reset(h, B)
         for t in range(prompt_len - 1):
@@ -449,6 +450,41 @@ def run_workload(args, w, dtype, steps, warmup, kernel_timing=True, roofline=Tru
                 "launch_ms": round(ms / n, 4), "launches_per_step": n / steps, "per_launch": per_launch,
                 "per_launch_unit": "FLOP" if kind == "flop" else "bytes"}
     graph = None
+    if graph_steps and args.mode == "decode":
+        # one decoding step captured once in a HIP graph (gpt2_decode_step_device: the position
+        # in device memory, advanced by the step; the drawn token written over the input token)
+        # and replayed at the following positions, a fresh uniform row copied in before each
+        try:
+            orig = st.stream
+            i0 = step_no[0]
+            d_pos = torch.tensor([G.gpt2_decode_position(h)], dtype=torch.int32, device=dev)
+            buf = bufs[i0 % 2].clone()
+            u_in = uni[i0].clone()
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                G.gpt2_set_stream(h, torch.cuda.current_stream().cuda_stream)
+                G.gpt2_decode_step_device(h, buf.data_ptr(), d_pos.data_ptr(), None, 50, u_in.data_ptr(),
+                                          buf.data_ptr())
+            G.gpt2_set_stream(h, orig)
+            for j in range(2):
+                u_in.copy_(uni[i0 + j])
+                g.replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for j in range(graph_steps):
+                u_in.copy_(uni[i0 + 2 + j])
+                g.replay()
+            torch.cuda.synchronize()
+            ge = time.perf_counter() - t1
+            graph = {"ms_per_step": ge / graph_steps * 1e3, "steps": graph_steps, "value": B / (ge / graph_steps),
+                     "positions": [int(G.gpt2_decode_position(h)), int(d_pos.item())]}
+            del g
+        except Exception as e:
+            G.gpt2_set_stream(h, st.stream)
+            torch.cuda.synchronize()
+            print(f"bench.py: HIP graph leg skipped ({e})", file=sys.stderr)
+            graph = None
     if graph_steps and args.mode == "eval":
         # one forward-only scoring pass captured once in a HIP graph and replayed, the next batch
         # copied into the captured input buffers before each replay (as for the training step)
@@ -631,8 +667,8 @@ def main():
                                + (f"{k} micro-step(s) + AdamW per step" if args.mode == "train"
                                   else "one forward-only scoring pass (no backward, no update) per step"
                                   if args.mode == "eval" else
-                                  f"one decoding step (one new token for each of B sequences, positions "
-                                  f"8..{8 + args.warmup + max(1, min(5, args.steps)) + args.steps - 1}) per step")
+                                  "one decoding step (one new token for each of B sequences, after an "
+                                  "8-token prompt; positions in `timing`) per step")
                                + ("; residual stream and its gradient fp32, product operands bf16"
                                   if args.dtype == "bf16" and w.dtype == "bf16" else
                                   "; residual stream and its gradient bf16" if w.dtype == "bf16" else ""),
@@ -643,6 +679,16 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "cus": torch.cuda.get_device_properties(0).multi_processor_count,
     }
+    if args.mode == "decode":
+        out["timing"] = {
+            "timed": "hip_graph" if g else "eager",
+            "eager": {"ms_per_step": round(r["ms_step"], 3), "value": round(r["value"], 1), "steps": args.steps},
+            "note": ("one decoding step (gpt2_decode_step_device: position in device memory) captured once in a "
+                     "HIP graph and replayed at the following positions, the drawn tokens fed back through the "
+                     "captured token buffer. `eager` times gpt2_decode_step as separate launches"
+                     f" (positions 8..{8 + args.warmup + max(1, min(5, args.steps)) + args.steps - 1}; the "
+                     f"graph's timed steps at positions {g['positions'][0] + 2}..{g['positions'][1] - 1})" if g else
+                     "the steps as separate launches (no HIP-graph leg: --no-graph or capture unavailable)")}
     if args.mode == "eval":
         out["timing"] = {
             "timed": "hip_graph" if g else "eager",

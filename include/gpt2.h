@@ -226,6 +226,18 @@ int gpt2_decode_reset(gpt2_t* h, int32_t B);
 int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_logits, int32_t top_k, const float* d_uniform,
                      int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob);
 
+/* gpt2_decode_step at the position held in device memory, for a step captured once in a HIP
+ * graph and replayed (the host's arguments of a replayed launch cannot change):
+ *   d_pos  int32 [1] device: the position p of this step; the kernels read it when they run,
+ *          and the step leaves min(p + 1, block_size) there for the next one.
+ * The caller keeps p < block_size (a larger value is clamped to block_size - 1, so the step
+ * overwrites the last cached position: no memory outside the cache is touched) and sets
+ * *d_pos to the number of positions already cached (e.g. after feeding a prompt with
+ * gpt2_decode_step). gpt2_decode_position does not count these steps. Other arguments,
+ * outputs and errors as in gpt2_decode_step. */
+int gpt2_decode_step_device(gpt2_t* h, const int32_t* d_tokens, int32_t* d_pos, float* d_logits, int32_t top_k,
+                            const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob);
+
 /* Positions in the cache (-1 without a reset or after the cache was overwritten). */
 int32_t gpt2_decode_position(const gpt2_t* h);
 

@@ -916,6 +916,76 @@ def test_decode_124m_bf16_five_sequences():
     assert G.gpt2_decode_position(st.h) == -1   # the forward overwrote the cache
 
 
+@pytest.mark.parametrize("mode", ["fp32", "bf16"])
+def test_decode_device_position_graph_matches_eager(mode):
+    """gpt2_decode_step_device captured once in a HIP graph and replayed: the position comes
+    from device memory and the step advances it there, the drawn token feeds the next step
+    through the same buffer, a fresh uniform row is copied in before each replay. After a
+    6-token prompt fed eagerly, 12 replayed steps give the same logits and drawn tokens, bit for
+    bit, as 12 eager gpt2_decode_step calls on a second handle with the same weights; the
+    device position ends at 18. fp32 check mode (the register-staged products take the row
+    offset) and bf16 (the few-row products), 2 layers at the 124M widths, 3 sequences."""
+    note(f"decode graph replay {mode}")
+    w = synthetic.workload("gpt2_step", n_layer=2, block_size=64, seq_len=64)
+    params = synthetic.init_params(w, randomize_affine=True)
+    B, n_prompt, n_gen = 3, 6, 12
+    rng = np.random.default_rng(11)
+    prompt = torch.from_numpy(rng.integers(0, w.vocab_size, (B, n_prompt)).astype(np.int32)).cuda()
+    uni = torch.from_numpy(rng.random((n_gen, B)).astype(np.float32)).cuda()
+    Vp = w.padded_vocab_size
+
+    def start():
+        st = make_step(w, mode, max_batch=B)
+        st.set_params(params)
+        G.gpt2_decode_reset(st.h, B)
+        for t in range(n_prompt - 1):
+            G.gpt2_decode_step(st.h, prompt[:, t].contiguous().data_ptr())
+        return st
+
+    # eager, host position
+    ea = start()
+    tok = prompt[:, n_prompt - 1].contiguous()
+    lg_e, nx_e = [], []
+    for i in range(n_gen):
+        lg = torch.empty((B, Vp), dtype=torch.float32, device="cuda")
+        nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+        G.gpt2_decode_step(ea.h, tok.data_ptr(), lg.data_ptr(), 50, uni[i].contiguous().data_ptr(), nxt.data_ptr())
+        torch.cuda.synchronize()
+        lg_e.append(lg.clone())
+        nx_e.append(nxt.clone())
+        tok = nxt
+    ea.close()
+
+    # captured once, replayed
+    gb = start()
+    d_pos = torch.tensor([n_prompt - 1], dtype=torch.int32, device="cuda")
+    buf = prompt[:, n_prompt - 1].contiguous().clone()
+    u_in = torch.empty(B, dtype=torch.float32, device="cuda")
+    lg_g = torch.empty((B, Vp), dtype=torch.float32, device="cuda")
+    u_in.copy_(uni[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    saved_pos = d_pos.clone()
+    saved_buf = buf.clone()
+    with torch.cuda.graph(graph):
+        G.gpt2_set_stream(gb.h, torch.cuda.current_stream().cuda_stream)
+        G.gpt2_decode_step_device(gb.h, buf.data_ptr(), d_pos.data_ptr(), lg_g.data_ptr(), 50, u_in.data_ptr(),
+                                  buf.data_ptr())
+    G.gpt2_set_stream(gb.h, gb.stream)
+    torch.cuda.synchronize()
+    d_pos.copy_(saved_pos)   # capture enqueues nothing, but restore in case it ran
+    buf.copy_(saved_buf)
+    for i in range(n_gen):
+        u_in.copy_(uni[i])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(lg_g, lg_e[i]), i
+        assert torch.equal(buf, nx_e[i]), i
+    assert int(d_pos.item()) == n_prompt - 1 + n_gen
+    del graph
+    gb.close()
+
+
 def test_decode_state_and_errors():
     """Decoding needs a reset; B is bounded by max_batch; top_k by 1..64 and the vocabulary;
     drawing needs the uniform numbers; k = 1 draws the argmax (lowest id among equal maxima)."""

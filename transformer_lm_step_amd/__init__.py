@@ -67,6 +67,7 @@ _SIGS = {
     "gpt2_evaluate_noalloc": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "gpt2_decode_reset": (ctypes.c_int, [_P, ctypes.c_int32]),
     "gpt2_decode_step": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "gpt2_decode_step_device": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "gpt2_decode_position": (ctypes.c_int32, [_P]),
     "gpt2_set_moments": (ctypes.c_int, [_P, _P, _P, ctypes.c_int]),
     "gpt2_params_device": (_P, [_P]),
@@ -221,6 +222,12 @@ def gpt2_decode_reset(h, B: int) -> None:
 def gpt2_decode_step(h, d_tokens, d_logits=None, top_k=50, d_uniform=None, d_next=None, d_topk_idx=None,
                      d_topk_prob=None) -> None:
     _check(_lib.gpt2_decode_step(h, d_tokens, d_logits, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob))
+
+
+def gpt2_decode_step_device(h, d_tokens, d_pos, d_logits=None, top_k=50, d_uniform=None, d_next=None,
+                            d_topk_idx=None, d_topk_prob=None) -> None:
+    _check(_lib.gpt2_decode_step_device(h, d_tokens, d_pos, d_logits, top_k, d_uniform, d_next, d_topk_idx,
+                                        d_topk_prob))
 
 
 def gpt2_decode_position(h) -> int:

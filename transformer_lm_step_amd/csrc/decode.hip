@@ -21,7 +21,9 @@ constexpr int DEC_THREADS = 256;
 
 template <typename T, int HS>
 __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(const T* __restrict__ qkv, int Tmax, int pos, int H,
-                                                                  float sc, T* __restrict__ y) {
+                                                                  float sc, T* __restrict__ y,
+                                                                  const int32_t* __restrict__ d_pos) {
+    if (d_pos) pos = min(max(*d_pos, 0), Tmax - 1);   // the position from device memory (LDS sized for Tmax)
     constexpr int G = DEC_THREADS / HS;    // key groups of the value sum
     extern __shared__ float dsm[];         // q [HS], partial sums [G][HS], scores [pos + 1]
     __shared__ float red[DEC_THREADS / 64];
@@ -84,19 +86,30 @@ __global__ void __launch_bounds__(DEC_THREADS) attn_decode_kernel(const T* __res
 
 size_t attention_decode_lds(int hs, int Tmax) { return (size_t)(hs + DEC_THREADS + Tmax) * 4; }
 
+// With d_pos the position is read on the device (clamped to Tmax - 1) and `pos` is ignored.
 hipError_t attention_decode(const void* qkv, void* y, int B, int Tmax, int pos, int H, int hs, int is_bf16,
-                            hipStream_t s) {
-    if (pos < 0 || pos >= Tmax || (hs != 64 && hs != 32)) return hipErrorInvalidValue;
+                            hipStream_t s, const int32_t* d_pos) {
+    if ((!d_pos && (pos < 0 || pos >= Tmax)) || (hs != 64 && hs != 32)) return hipErrorInvalidValue;
     const float sc = 1.4426950408889634f / sqrtf((float)hs);
-    const size_t lds = attention_decode_lds(hs, pos + 1);
+    const size_t lds = attention_decode_lds(hs, d_pos ? Tmax : pos + 1);
     const dim3 grid(B * H), blk(DEC_THREADS);
     if (is_bf16) {
-        if (hs == 64) attn_decode_kernel<bf16, 64><<<grid, blk, lds, s>>>((const bf16*)qkv, Tmax, pos, H, sc, (bf16*)y);
-        else attn_decode_kernel<bf16, 32><<<grid, blk, lds, s>>>((const bf16*)qkv, Tmax, pos, H, sc, (bf16*)y);
+        if (hs == 64) attn_decode_kernel<bf16, 64><<<grid, blk, lds, s>>>((const bf16*)qkv, Tmax, pos, H, sc, (bf16*)y, d_pos);
+        else attn_decode_kernel<bf16, 32><<<grid, blk, lds, s>>>((const bf16*)qkv, Tmax, pos, H, sc, (bf16*)y, d_pos);
     } else {
-        if (hs == 64) attn_decode_kernel<float, 64><<<grid, blk, lds, s>>>((const float*)qkv, Tmax, pos, H, sc, (float*)y);
-        else attn_decode_kernel<float, 32><<<grid, blk, lds, s>>>((const float*)qkv, Tmax, pos, H, sc, (float*)y);
+        if (hs == 64)
+            attn_decode_kernel<float, 64><<<grid, blk, lds, s>>>((const float*)qkv, Tmax, pos, H, sc, (float*)y, d_pos);
+        else
+            attn_decode_kernel<float, 32><<<grid, blk, lds, s>>>((const float*)qkv, Tmax, pos, H, sc, (float*)y, d_pos);
     }
+    return hipGetLastError();
+}
+
+__global__ void decode_advance_kernel(int32_t* __restrict__ d_pos, int pos_end) {
+    if (threadIdx.x == 0) *d_pos = min(*d_pos + 1, pos_end);
+}
+hipError_t decode_advance(int32_t* d_pos, int pos_end, hipStream_t s) {
+    hipLaunchKernelGGL(decode_advance_kernel, dim3(1), dim3(64), 0, s, d_pos, pos_end);
     return hipGetLastError();
 }
 

@@ -48,6 +48,9 @@ struct GemmArgs {
     float* rowsum_out;          // with one split: the row sums of A written (beta: added) here directly
     int vec;                    // 1: full tiles may use 8/16-byte epilogue accesses
     int vec8;                   // 1: also 8-element (16-byte bf16) epilogue accesses
+    const int32_t* c_row_dev;   // few-row products: output row offset from device memory, or null
+    int64_t c_row_bytes;
+    int c_row_max;
 };
 
 template <int BM, int BN>
@@ -231,6 +234,7 @@ DEV void store_tile(const GemmArgs& p, const floatx4 (&acc)[FM][FN], int mw, int
 
 template <typename T, int ALAY, int BLAY, int EPI, int BM, int BN>
 __global__ void __launch_bounds__(GTHREADS, (BM * BN > 128 * 128) ? 1 : 2) gemm_kernel(GemmArgs p) {
+    if (p.c_row_dev) p.C = (char*)p.C + (int64_t)min(max(*p.c_row_dev, 0), p.c_row_max) * p.c_row_bytes;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     constexpr int BK = 128 / sizeof(T);
     constexpr int KSTEPS = BK / 32;
@@ -1101,10 +1105,12 @@ __global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
     __syncthreads();
     const int m = threadIdx.x;
     if (m < p.M) {
+        GemmArgs q = p;
+        if (p.c_row_dev) q.C = (char*)p.C + (int64_t)min(max(*p.c_row_dev, 0), p.c_row_max) * p.c_row_bytes;
         const float4 v = make_float4(res[m][0], res[m][1], res[m][2], res[m][3]);
         typename EpiIn<EPI>::T in;
-        if (epi_reads<EPI>(p) && epi_vec(p, m, n0)) in = epi_load<EPI>(p, m, n0);
-        epi4<EPI>(p, m, n0, v, in);
+        if (epi_reads<EPI>(q) && epi_vec(q, m, n0)) in = epi_load<EPI>(q, m, n0);
+        epi4<EPI>(q, m, n0, v, in);
     }
 }
 
@@ -1151,9 +1157,13 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     }
     int epi = d.epi;
     if (epi == EPI_LOGITS && !gemm_logits_tiles(d, sizeof(T) == 2)) return hipErrorInvalidValue;
+    a.c_row_dev = d.c_row_dev;
+    a.c_row_bytes = d.c_row_bytes;
+    a.c_row_max = d.c_row_max;
     if constexpr (sizeof(T) == 2) {
         if (skinny_ok<T>(d, nsplit)) return launch_skinny<T>(a, epi, s);
     }
+    if (nsplit > 1 && d.c_row_dev) return hipErrorInvalidValue;   // a device row offset: one split only
     if (nsplit > 1) {
         // partials, then a fixed-order reduce into the fp32 output
         a.C = d.partial; a.ldc = d.N; a.part_stride = (int64_t)d.M * d.N;
@@ -1163,7 +1173,7 @@ static hipError_t dispatch(const GemmDesc& d, hipStream_t s) {
     if (bm == 0) gemm_pick_tile(d.M, d.N, nsplit, sizeof(T) == 2, &bm, &bn);
     hipError_t e = hipSuccess;
     if constexpr (sizeof(T) == 2) {
-        if (!d.no_dl && mm_ok(d, a.ksplit_len)) {
+        if (!d.no_dl && mm_ok(d, a.ksplit_len) && !d.c_row_dev) {
             if (d.rowsum && d.a_layout == 1) a.rowsum_part = d.rowsum_part;
             // 128x192 tiles (wave tile 64x96: fewer LDS bytes per MFMA) where, at the 128x192
             // tile's measured 1.15 times the rate per output of 128x128, they use the rounds of

@@ -850,13 +850,15 @@ extern "C" int gpt2_decode_reset(gpt2_t* h, int32_t B) {
 // One new position of every cached sequence: the blocks run on B rows (one per sequence),
 // the qkv product writes its rows straight into the cache (row b*block_size + pos of the
 // layer's qkv buffer), and the attention reads the cache.
-extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_logits, int32_t top_k,
-                                const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob) {
+// One decoding step at the host's position (d_pos null) or at the position in device memory
+// *d_pos (clamped to block_size - 1 by the kernels, then advanced on the device).
+static int decode_impl(gpt2_t* h, const int32_t* d_tokens, int32_t* d_pos, float* d_logits, int32_t top_k,
+                       const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob) {
     if (!h || !d_tokens) return set_error(GPT2_EINVAL, "null argument");
     if (!h->dec_B) return set_error(GPT2_ESTATE, "decoding needs gpt2_decode_reset first");
     const gpt2_config& c = h->cfg;
-    const int B = h->dec_B, pos = h->dec_pos, Tmax = c.block_size;
-    if (pos >= Tmax) return set_error(GPT2_EINVAL, "the cache is full (block_size=%d positions)", Tmax);
+    const int B = h->dec_B, pos = d_pos ? 0 : h->dec_pos, Tmax = c.block_size;
+    if (!d_pos && pos >= Tmax) return set_error(GPT2_EINVAL, "the cache is full (block_size=%d positions)", Tmax);
     const bool sample = d_next || d_topk_idx || d_topk_prob;
     if (sample && (top_k < 1 || top_k > GPT2_TOPK_MAX || top_k > c.padded_vocab_size))
         return set_error(GPT2_EINVAL, "top_k=%d outside [1, %d]", top_k, GPT2_TOPK_MAX);
@@ -873,7 +875,8 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
     HIPTRY(hipMemcpyAsync(idx, d_tokens, (size_t)B * 4, hipMemcpyDeviceToDevice, s), "copy tokens");
     h->dec_B = 0;   // until this step has been enqueued completely
     TRY(run(h, "embed_fwd", [&] {
-        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, r16, s);
+        return embed_forward(idx, prm + L.wte, prm + L.wpe + (int64_t)pos * C, h->at<char>(P.x_in[0]), B, 1, C, r16, s,
+                             d_pos, Tmax - 1);
     }));
     TRY(run(h, "layernorm_fwd", [&] {
         return layernorm_forward(h->at<char>(P.x_in[0]), prm + L.ln1_w[0], prm + L.ln1_b[0], h->at<char>(P.h1[0]),
@@ -886,9 +889,10 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         g.M = B; g.N = 3 * C; g.K = C;
         g.epi = EPI_BIAS_T; g.C = h->at<char>(P.qkv[l]) + (size_t)pos * 3 * C * es; g.ldc = (int64_t)Tmax * 3 * C;
         g.bias = prm + L.b_qkv[l];
+        if (d_pos) { g.c_row_dev = d_pos; g.c_row_bytes = (int64_t)3 * C * es; g.c_row_max = Tmax - 1; }
         TRY(run(h, "gemm_qkv", [&] { return gemm(g, bf, s); }));
         TRY(run(h, "attn_decode", [&] {
-            return attention_decode(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), B, Tmax, pos, H, hs, bf, s);
+            return attention_decode(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), B, Tmax, pos, H, hs, bf, s, d_pos);
         }));
         g = GemmDesc();
         g.A = h->at<char>(P.att[l]); g.lda = C;
@@ -935,9 +939,22 @@ extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_log
         TRY(run(h, "topk_sample", [&] {
             return topk_sample(h->at<char>(P.logits), B, Vp, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob, bf, s);
         }));
+    if (d_pos) HIPTRY(decode_advance(d_pos, Tmax, s), "advance position");
     h->dec_B = B;
-    h->dec_pos = pos + 1;
+    if (!d_pos) h->dec_pos = pos + 1;
     return GPT2_OK;
+}
+
+extern "C" int gpt2_decode_step(gpt2_t* h, const int32_t* d_tokens, float* d_logits, int32_t top_k,
+                                const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx, float* d_topk_prob) {
+    return decode_impl(h, d_tokens, nullptr, d_logits, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob);
+}
+
+extern "C" int gpt2_decode_step_device(gpt2_t* h, const int32_t* d_tokens, int32_t* d_pos, float* d_logits,
+                                       int32_t top_k, const float* d_uniform, int32_t* d_next, int32_t* d_topk_idx,
+                                       float* d_topk_prob) {
+    if (!d_pos) return set_error(GPT2_EINVAL, "d_pos is null");
+    return decode_impl(h, d_tokens, d_pos, d_logits, top_k, d_uniform, d_next, d_topk_idx, d_topk_prob);
 }
 
 extern "C" int32_t gpt2_decode_position(const gpt2_t* h) { return h && h->dec_B ? h->dec_pos : -1; }

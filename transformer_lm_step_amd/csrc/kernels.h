@@ -37,6 +37,11 @@ struct GemmDesc {
     // bias gradient of a weight-gradient product; rowsum_part holds nsplit*M floats
     float* rowsum = nullptr;
     float* rowsum_part = nullptr;
+    // few-row products only (decoding): the output starts min(*c_row_dev, c_row_max) * c_row_bytes
+    // bytes past C, a row offset read from device memory when the kernel runs
+    const int32_t* c_row_dev = nullptr;
+    int64_t c_row_bytes = 0;
+    int c_row_max = 0;
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
@@ -75,7 +80,8 @@ size_t gemm_lds_bytes();
 // ------------------------------------------------------------------ elementwise / rows
 // x [B*T, C] = wte[idx] + wpe[t], x in bf16 if x_bf16 else fp32 (the residual stream's type)
 hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, void* x, int B, int T,
-                         int C, int x_bf16, hipStream_t s);
+                         int C, int x_bf16, hipStream_t s, const int32_t* d_pos = nullptr,
+                         int pos_max = 0);
 // LayerNorm forward: out = (x - mean) * rstd * w + b ; saves mean, rstd (fp32). x is bf16 if
 // x_bf16 (the bf16 residual stream) else fp32; out is bf16 if out_bf16 else fp32.
 hipError_t layernorm_forward(const void* x, const float* w, const float* b, void* out, float* mean,
@@ -184,7 +190,9 @@ void attention_setup();
 // attention of the query at position pos of each of B sequences over the cached keys/values
 // at 0..pos; qkv rows (b, t) -> b*Tmax + t (3C wide), y(T) [B, C]
 hipError_t attention_decode(const void* qkv, void* y, int B, int Tmax, int pos, int H, int hs, int is_bf16,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* d_pos = nullptr);
+// *d_pos = min(*d_pos + 1, pos_end): the next decoding position, advanced on the device
+hipError_t decode_advance(int32_t* d_pos, int pos_end, hipStream_t s);
 size_t attention_decode_lds(int hs, int Tmax);
 // top-k of each logits row (T) [B, Vp] (larger first, ties by lower id), their renormalized
 // softmax, and the inverse-CDF draw with u[b] in [0, 1); every output pointer may be null

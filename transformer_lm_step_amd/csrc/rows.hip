@@ -32,14 +32,16 @@ template <> DEV float4 load4<bf16>(const bf16* p) {
 // ================================================================== embedding forward
 // x[b,t,:] = wte[idx[b,t],:] + wpe[t,:] ("Code you'll write", forward pass: token and
 // position embeddings are added), stored in the storage type. One wave per token row.
+// With d_pos (one new position per sequence, T_ = 1) the position is read from device memory,
+// clamped to pos_max.
 template <typename T>
 __global__ void embed_forward_kernel(const int32_t* __restrict__ idx, const float* __restrict__ wte,
                                      const float* __restrict__ wpe, T* __restrict__ x, int rows,
-                                     int T_, int C) {
+                                     int T_, int C, const int32_t* __restrict__ d_pos, int pos_max) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
-    const int t = row % T_;
+    const int t = d_pos ? min(max(*d_pos, 0), pos_max) : row % T_;
     const int64_t id = idx[row];
     const int nv = C >> 2;
     const float4* e = (const float4*)(wte + id * C);
@@ -52,14 +54,15 @@ __global__ void embed_forward_kernel(const int32_t* __restrict__ idx, const floa
 }
 
 hipError_t embed_forward(const int32_t* idx, const float* wte, const float* wpe, void* x, int B, int T,
-                         int C, int is_bf16, hipStream_t s) {
+                         int C, int is_bf16, hipStream_t s, const int32_t* d_pos, int pos_max) {
     const int rows = B * T;
+    if (d_pos && T != 1) return hipErrorInvalidValue;
     if (is_bf16)
         hipLaunchKernelGGL(embed_forward_kernel<bf16>, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe, (bf16*)x,
-                           rows, T, C);
+                           rows, T, C, d_pos, pos_max);
     else
         hipLaunchKernelGGL(embed_forward_kernel<float>, dim3((rows + 3) / 4), dim3(256), 0, s, idx, wte, wpe,
-                           (float*)x, rows, T, C);
+                           (float*)x, rows, T, C, d_pos, pos_max);
     return hipGetLastError();
 }
 
