@@ -31,6 +31,30 @@ template <typename T> DEV T from_f(float x);
 template <> DEV float from_f<float>(float x) { return x; }
 template <> DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
 
+// 4 consecutive values of a storage-type row as fp32, and back
+template <typename T> DEV void store4(T* p, float a, float b, float c, float d);
+template <> DEV void store4<float>(float* p, float a, float b, float c, float d) { *(float4*)p = make_float4(a, b, c, d); }
+template <> DEV void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+    bf16x4 v;
+    v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+    *(bf16x4*)p = v;
+}
+// 4 fp32 values as they read back after a store in type T (rounded to bf16 for bf16)
+template <typename T> DEV float4 load4_rounded(float a, float b, float c, float d);
+template <> DEV float4 load4_rounded<float>(float a, float b, float c, float d) { return make_float4(a, b, c, d); }
+template <> DEV float4 load4_rounded<bf16>(float a, float b, float c, float d) {
+    return make_float4((float)(bf16)a, (float)(bf16)b, (float)(bf16)c, (float)(bf16)d);
+}
+template <typename T> DEV float4 load4(const T* p);
+template <> DEV float4 load4<float>(const float* p) { return *(const float4*)p; }
+template <> DEV float4 load4<bf16>(const bf16* p) {
+    const bf16x4 v = *(const bf16x4*)p;
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+
+// nn.LayerNorm epsilon
+constexpr float LN_EPS = 1e-5f;
+
 // 8-value fragment type of a storage type
 template <typename T> struct FragT;
 template <> struct FragT<bf16> { typedef bf16x8 type; };

@@ -1059,9 +1059,10 @@ static bool mm_ok(const GemmDesc& d, int ksplit_len) {
 // measured slower: at k = 768 most of their lanes have no chunk.)
 constexpr int SK_MAX_M = 16;
 constexpr int SK_THREADS = 256;
+constexpr int SK_LN_MAX_K = 2048;   // LayerNorm-fused form: [SK_MAX_M][K] bf16 rows in LDS (64 KB)
 
-template <typename T, int EPI>
-__global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
+template <typename T, int EPI, bool LDS_A>
+DEV void skinny_body(const GemmArgs& p, const char* sa) {
     constexpr int E = 16 / sizeof(T);        // elements per 16-byte chunk
     __shared__ float res[SK_MAX_M][4];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -1075,7 +1076,8 @@ __global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
         // are never stored), so a chunk costs one round trip, not one per row
         const T* arow[SK_MAX_M];
 #pragma unroll
-        for (int m = 0; m < SK_MAX_M; ++m) arow[m] = (const T*)p.A + (int64_t)min(m, p.M - 1) * p.lda;
+        for (int m = 0; m < SK_MAX_M; ++m)
+            arow[m] = LDS_A ? (const T*)sa + (int64_t)min(m, p.M - 1) * p.K : (const T*)p.A + (int64_t)min(m, p.M - 1) * p.lda;
 #pragma unroll 2
         for (int k = lane * E; k < p.K; k += 64 * E) {
             const uint4 wr = ld16(w + k);
@@ -1114,6 +1116,67 @@ __global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
     }
 }
 
+template <typename T, int EPI>
+__global__ void __launch_bounds__(SK_THREADS) gemm_skinny_kernel(GemmArgs p) {
+    skinny_body<T, EPI, false>(p, nullptr);
+}
+
+// The few-row product of decoding with the residual add and LayerNorm that precede c_attn and
+// c_fc fused in: every workgroup forms the M rows x + y of the residual stream (TX: its type;
+// y the bf16 projection output, or none), normalizes them exactly as the LayerNorm kernel
+// does (one wave per row, the same lane partition and summation order, so the same bits) into
+// bf16 rows in LDS, and multiplies those; workgroup 0 also stores x + y as the new stream.
+// 23 of a decoding step's 25 LayerNorm launches go away.
+template <typename TX, int EPI, int NV>
+__global__ void __launch_bounds__(SK_THREADS) gemm_skinny_ln_kernel(GemmArgs p, SkinnyLn ln) {
+    extern __shared__ __attribute__((aligned(16))) char sk_a[];   // [M][K] bf16
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int C = p.K, nv = C >> 2;
+    const bool store_x = blockIdx.x == 0 && ln.x_out;
+    for (int m = wave; m < p.M; m += SK_THREADS / 64) {
+        const int64_t ro = (int64_t)m * C;
+        float4 v[NV];
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = lane + 64 * j;
+            v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < nv) {
+                float4 a = load4<TX>((const TX*)ln.x + ro + 4 * c);
+                if (ln.y) {
+                    const float4 d = load4<bf16>((const bf16*)ln.y + ro + 4 * c);
+                    a = make_float4(a.x + d.x, a.y + d.y, a.z + d.z, a.w + d.w);
+                }
+                if (store_x) store4<TX>((TX*)ln.x_out + ro + 4 * c, a.x, a.y, a.z, a.w);
+                v[j] = load4_rounded<TX>(a.x, a.y, a.z, a.w);
+            }
+            sum += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+        }
+        const float mu = wave_sum(sum) / (float)C;
+        float s2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nv) {
+                const float a = v[j].x - mu, bb = v[j].y - mu, cc = v[j].z - mu, d = v[j].w - mu;
+                s2 += (a * a + bb * bb) + (cc * cc + d * d);
+            }
+        }
+        const float r = 1.0f / sqrtf(wave_sum(s2) / (float)C + LN_EPS);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int c = lane + 64 * j;
+            if (c < nv) {
+                const float4 ww = ((const float4*)ln.w)[c], bb = ((const float4*)ln.b)[c];
+                store4<bf16>((bf16*)sk_a + ro + 4 * c, (v[j].x - mu) * r * ww.x + bb.x, (v[j].y - mu) * r * ww.y + bb.y,
+                             (v[j].z - mu) * r * ww.z + bb.z, (v[j].w - mu) * r * ww.w + bb.w);
+            }
+        }
+    }
+    __syncthreads();
+    skinny_body<bf16, EPI, true>(p, sk_a);
+}
+
 template <typename T>
 static bool skinny_ok(const GemmDesc& d, int nsplit) {
     constexpr int E = 16 / sizeof(T);
@@ -1129,6 +1192,52 @@ static hipError_t launch_skinny(const GemmArgs& a, int epi, hipStream_t s) {
     const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
     if (epi == EPI_BIAS_T) gemm_skinny_kernel<T, EPI_BIAS_T><<<grid, blk, 0, s>>>(a);
     else gemm_skinny_kernel<T, EPI_BIAS_GELU><<<grid, blk, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <typename TX, int EPI>
+static void launch_skinny_ln(const GemmArgs& a, const SkinnyLn& ln, int nv4, size_t lds, hipStream_t s) {
+    const dim3 grid((a.N + 3) / 4), blk(SK_THREADS);
+#define SKL(NV) gemm_skinny_ln_kernel<TX, EPI, NV><<<grid, blk, lds, s>>>(a, ln)
+    if (nv4 <= 64) SKL(1);
+    else if (nv4 <= 128) SKL(2);
+    else if (nv4 <= 192) SKL(3);
+    else if (nv4 <= 256) SKL(4);
+    else if (nv4 <= 320) SKL(5);
+    else if (nv4 <= 384) SKL(6);
+    else if (nv4 <= 448) SKL(7);
+    else SKL(8);
+#undef SKL
+}
+
+int gemm_skinny_ln_ok(const GemmDesc& d, int is_bf16) {
+    if (!is_bf16 || !skinny_ok<bf16>(d, 1) || d.lda != d.K || d.K > SK_LN_MAX_K || d.K % 8) return 0;
+    return 1;
+}
+
+hipError_t gemm_skinny_ln(const GemmDesc& d, const SkinnyLn& ln, int x_bf16, hipStream_t s) {
+    if (!gemm_skinny_ln_ok(d, 1) || !ln.x || !ln.w || !ln.b) return hipErrorInvalidValue;
+    auto al = [](const void* q) { return ((uintptr_t)q & 15) == 0; };
+    if (!al(ln.w) || !al(ln.b) || ((uintptr_t)ln.x & 7) || ((uintptr_t)ln.y & 7) || ((uintptr_t)ln.x_out & 7))
+        return hipErrorInvalidValue;
+    GemmArgs a{};
+    a.A = nullptr; a.B = d.B; a.lda = d.K; a.ldb = d.ldb;
+    a.M = d.M; a.N = d.N; a.K = d.K;
+    a.C = d.C; a.ldc = d.ldc; a.C2 = d.C2; a.bias = d.bias;
+    a.alpha = d.alpha; a.beta = d.beta;
+    a.ksplit_len = d.K;
+    a.vec = d.ldc % 4 == 0 && al(d.C) && al(d.C2) && al(d.bias);
+    a.vec8 = a.vec && d.ldc % 8 == 0;
+    a.c_row_dev = d.c_row_dev; a.c_row_bytes = d.c_row_bytes; a.c_row_max = d.c_row_max;
+    const size_t lds = (size_t)d.M * d.K * 2;
+    const int nv4 = d.K / 4;
+    if (x_bf16) {
+        if (d.epi == EPI_BIAS_T) launch_skinny_ln<bf16, EPI_BIAS_T>(a, ln, nv4, lds, s);
+        else launch_skinny_ln<bf16, EPI_BIAS_GELU>(a, ln, nv4, lds, s);
+    } else {
+        if (d.epi == EPI_BIAS_T) launch_skinny_ln<float, EPI_BIAS_T>(a, ln, nv4, lds, s);
+        else launch_skinny_ln<float, EPI_BIAS_GELU>(a, ln, nv4, lds, s);
+    }
     return hipGetLastError();
 }
 

@@ -882,7 +882,8 @@ static int decode_impl(gpt2_t* h, const int32_t* d_tokens, int32_t* d_pos, float
         return layernorm_forward(h->at<char>(P.x_in[0]), prm + L.ln1_w[0], prm + L.ln1_b[0], h->at<char>(P.h1[0]),
                                  h->at<float>(P.mean1[0]), h->at<float>(P.rstd1[0]), B, C, r16, bf, s);
     }));
-    for (int l = 0; l < c.n_layer; ++l) {
+    // the descriptors of one layer's products (the fused forms take the LayerNorm in their A rows)
+    auto qkv_desc = [&](int l) {
         GemmDesc g;
         g.A = h->at<char>(P.h1[l]); g.lda = C; g.a_layout = 0;
         g.B = h->wop(L.w_qkv[l]); g.ldb = C; g.b_layout = 0;
@@ -890,41 +891,70 @@ static int decode_impl(gpt2_t* h, const int32_t* d_tokens, int32_t* d_pos, float
         g.epi = EPI_BIAS_T; g.C = h->at<char>(P.qkv[l]) + (size_t)pos * 3 * C * es; g.ldc = (int64_t)Tmax * 3 * C;
         g.bias = prm + L.b_qkv[l];
         if (d_pos) { g.c_row_dev = d_pos; g.c_row_bytes = (int64_t)3 * C * es; g.c_row_max = Tmax - 1; }
-        TRY(run(h, "gemm_qkv", [&] { return gemm(g, bf, s); }));
-        TRY(run(h, "attn_decode", [&] {
-            return attention_decode(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), B, Tmax, pos, H, hs, bf, s, d_pos);
-        }));
-        g = GemmDesc();
-        g.A = h->at<char>(P.att[l]); g.lda = C;
-        g.B = h->wop(L.w_o[l]); g.ldb = C;
-        g.M = B; g.N = C; g.K = C;
-        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_o[l];
-        TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
-        TRY(run(h, "layernorm_fwd", [&] {
-            return add_layernorm_forward(h->at<char>(P.x_in[l]), y, h->at<char>(P.x_mid[l]), prm + L.ln2_w[l],
-                                         prm + L.ln2_b[l], h->at<char>(P.h2[l]), h->at<float>(P.mean2[l]),
-                                         h->at<float>(P.rstd2[l]), B, C, r16, bf, s);
-        }));
-        g = GemmDesc();
+        return g;
+    };
+    auto fc_desc = [&](int l) {
+        GemmDesc g;
         g.A = h->at<char>(P.h2[l]); g.lda = C;
         g.B = h->wop(L.w_fc[l]); g.ldb = C;
         g.M = B; g.N = F; g.K = C;
         g.epi = EPI_BIAS_GELU; g.C = h->at<char>(P.u[l]); g.C2 = h->at<char>(P.a[l]); g.ldc = F; g.bias = prm + L.b_fc[l];
-        TRY(run(h, "gemm_fc", [&] { return gemm(g, bf, s); }));
-        g = GemmDesc();
-        g.A = h->at<char>(P.a[l]); g.lda = F;
-        g.B = h->wop(L.w_pr[l]); g.ldb = F;
-        g.M = B; g.N = C; g.K = F;
-        g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_pr[l];
-        TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
-        const bool last = l + 1 == c.n_layer;
-        TRY(run(h, "layernorm_fwd", [&] {
-            return add_layernorm_forward(h->at<char>(P.x_mid[l]), y, h->at<char>(P.x_in[l + 1]),
-                                         prm + (last ? L.lnf_w : L.ln1_w[l + 1]), prm + (last ? L.lnf_b : L.ln1_b[l + 1]),
-                                         h->at<char>(last ? P.hf : P.h1[l + 1]),
-                                         h->at<float>(last ? P.meanf : P.mean1[l + 1]),
-                                         h->at<float>(last ? P.rstdf : P.rstd1[l + 1]), B, C, r16, bf, s);
+        return g;
+    };
+    // residual add + LayerNorm inside the following product (bf16, few rows), else separate
+    const bool fuse = gemm_skinny_ln_ok(qkv_desc(0), bf) && gemm_skinny_ln_ok(fc_desc(0), bf);
+    for (int l = 0; l < c.n_layer; ++l) {
+        {
+            const GemmDesc g = qkv_desc(l);
+            if (fuse && l > 0) {
+                const SkinnyLn ln{h->at<char>(P.x_mid[l - 1]), y, h->at<char>(P.x_in[l]), prm + L.ln1_w[l],
+                                  prm + L.ln1_b[l]};
+                TRY(run(h, "gemm_qkv", [&] { return gemm_skinny_ln(g, ln, r16, s); }));
+            } else {
+                TRY(run(h, "gemm_qkv", [&] { return gemm(g, bf, s); }));
+            }
+        }
+        TRY(run(h, "attn_decode", [&] {
+            return attention_decode(h->at<char>(P.qkv[l]), h->at<char>(P.att[l]), B, Tmax, pos, H, hs, bf, s, d_pos);
         }));
+        {
+            GemmDesc g;
+            g.A = h->at<char>(P.att[l]); g.lda = C;
+            g.B = h->wop(L.w_o[l]); g.ldb = C;
+            g.M = B; g.N = C; g.K = C;
+            g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_o[l];
+            TRY(run(h, "gemm_attn_proj", [&] { return gemm(g, bf, s); }));
+        }
+        if (fuse) {
+            const SkinnyLn ln{h->at<char>(P.x_in[l]), y, h->at<char>(P.x_mid[l]), prm + L.ln2_w[l], prm + L.ln2_b[l]};
+            const GemmDesc g = fc_desc(l);
+            TRY(run(h, "gemm_fc", [&] { return gemm_skinny_ln(g, ln, r16, s); }));
+        } else {
+            TRY(run(h, "layernorm_fwd", [&] {
+                return add_layernorm_forward(h->at<char>(P.x_in[l]), y, h->at<char>(P.x_mid[l]), prm + L.ln2_w[l],
+                                             prm + L.ln2_b[l], h->at<char>(P.h2[l]), h->at<float>(P.mean2[l]),
+                                             h->at<float>(P.rstd2[l]), B, C, r16, bf, s);
+            }));
+            const GemmDesc g = fc_desc(l);
+            TRY(run(h, "gemm_fc", [&] { return gemm(g, bf, s); }));
+        }
+        {
+            GemmDesc g;
+            g.A = h->at<char>(P.a[l]); g.lda = F;
+            g.B = h->wop(L.w_pr[l]); g.ldb = F;
+            g.M = B; g.N = C; g.K = F;
+            g.epi = EPI_BIAS_T; g.C = y; g.ldc = C; g.bias = prm + L.b_pr[l];
+            TRY(run(h, "gemm_mlp_proj", [&] { return gemm(g, bf, s); }));
+        }
+        const bool last = l + 1 == c.n_layer;
+        if (last || !fuse)
+            TRY(run(h, "layernorm_fwd", [&] {
+                return add_layernorm_forward(h->at<char>(P.x_mid[l]), y, h->at<char>(P.x_in[l + 1]),
+                                             prm + (last ? L.lnf_w : L.ln1_w[l + 1]), prm + (last ? L.lnf_b : L.ln1_b[l + 1]),
+                                             h->at<char>(last ? P.hf : P.h1[l + 1]),
+                                             h->at<float>(last ? P.meanf : P.mean1[l + 1]),
+                                             h->at<float>(last ? P.rstdf : P.rstd1[l + 1]), B, C, r16, bf, s);
+            }));
     }
     {
         GemmDesc g;

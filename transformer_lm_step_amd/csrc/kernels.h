@@ -45,6 +45,18 @@ struct GemmDesc {
 };
 
 hipError_t gemm(const GemmDesc& d, int is_bf16, hipStream_t s);
+// Decoding: a few-row bf16 product (EPI_BIAS_T or EPI_BIAS_GELU, A contiguous [M, K]) whose A
+// rows are LayerNorm(x + y) of the residual stream, computed inside the product; x_out (if
+// not null) receives x + y. y may be null (no add). gemm_skinny_ln_ok says whether d qualifies.
+struct SkinnyLn {
+    const void* x;      // residual stream rows [M, K] (fp32, or bf16 with x_bf16)
+    const void* y;      // projection output rows [M, K] bf16, or null
+    void* x_out;        // x + y (the stream's type), or null
+    const float* w;     // LayerNorm weight and bias [K]
+    const float* b;
+};
+int gemm_skinny_ln_ok(const GemmDesc& d, int is_bf16);
+hipError_t gemm_skinny_ln(const GemmDesc& d, const SkinnyLn& ln, int x_bf16, hipStream_t s);
 // per-kernel timing of the products: hand over an event pair before a product call; after it,
 // gemm_time_taken() says whether the product was a single kernel that recorded the pair at its
 // own start and end (and forgets the pair either way)
