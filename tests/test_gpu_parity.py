@@ -916,6 +916,31 @@ def test_decode_124m_bf16_five_sequences():
     assert G.gpt2_decode_position(st.h) == -1   # the forward overwrote the cache
 
 
+@pytest.mark.parametrize("k", [1, 50, 64])
+def test_decode_all_logits_equal(k):
+    """Ties everywhere: with wte = 0 every logit of the tied lm_head is exactly 0 (bf16, the
+    124M widths, 2 layers, 4 sequences), so the k most probable tokens are the k lowest ids,
+    each with probability 1/k, and the draw is the oracle sampler's on the same row."""
+    note(f"decode all-equal logits k={k}")
+    w = synthetic.workload("gpt2_step", n_layer=2)
+    params = synthetic.init_params(w)
+    params["wte"][:] = 0.0
+    st = make_step(w, "bf16", max_batch=4)
+    st.set_params(params)
+    st.decode_reset(4)
+    u = np.array([0.0, 0.31, 0.71, 0.999], np.float32)   # no multiple of 1/k: no cumulative boundary
+    logits, nxt, ids, probs = st.decode_step(np.array([3, 50000, 0, 17], np.int32), uniform=u, top_k=k)
+    lg = logits.cpu().numpy()
+    assert np.all(lg == 0.0)
+    nxt, ids, probs = nxt.cpu().numpy(), ids.cpu().numpy(), probs.cpu().numpy()
+    for b in range(4):
+        assert np.array_equal(ids[b], np.arange(k)), b
+        np.testing.assert_allclose(probs[b], np.full(k, 1.0 / k), rtol=0, atol=1e-7)
+        tok, rids, _ = O.topk_sample(lg[b], k, float(u[b]))
+        assert np.array_equal(rids, np.arange(k))
+        assert nxt[b] == tok, b
+
+
 @pytest.mark.parametrize("mode", ["fp32", "bf16"])
 def test_decode_device_position_graph_matches_eager(mode):
     """gpt2_decode_step_device captured once in a HIP graph and replayed: the position comes

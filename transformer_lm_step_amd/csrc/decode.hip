@@ -122,7 +122,7 @@ hipError_t decode_advance(int32_t* d_pos, int pos_end, hipStream_t s) {
 // one if rounding leaves every cumulative sum at or below u).
 //
 // Selection: radix select of the k-th largest order-preserving 32-bit key in four 8-bit passes
-// (LDS histograms), then an ordered compaction (block scans in
+// (LDS histograms; two for bf16 rows, whose keys' low 16 bits are set by the sign alone), then an ordered compaction (block scans in
 // token order) of the keys above it plus the lowest-id keys equal to it, then one wave sorts
 // the k entries.
 constexpr int TK_THREADS = 1024;
@@ -153,47 +153,71 @@ DEV int block_excl_scan(int v, int* total, int* wsum) {
     return before + inc - v;
 }
 
-// IN_LDS (bf16 rows of at most TK_LDS_MAX ids): the row is first copied into LDS with 16-byte
-// loads, so the five passes below read LDS; otherwise they read the row from global memory.
 // Thread t owns the contiguous ids [per t, per t + per), so the compaction keeps token order.
-constexpr int TK_LDS_MAX = 65536;
+// IN_REG (bf16 rows of at most TK_REG_MAX ids): per is a multiple of 8, and each thread loads
+// its ids once with 16-byte loads into registers (up to TK_REG_CHUNKS x 8 values), which every
+// pass below then reads; otherwise the passes read the row from global memory.
+constexpr int TK_REG_CHUNKS = 8;
+constexpr int TK_REG_MAX = TK_THREADS * 8 * TK_REG_CHUNKS;
 
-template <typename T, bool IN_LDS>
+// the order key of element e (0..7) of a 16-byte chunk of bf16 values
+DEV uint32_t chunk_key(const uint4& q, int e) {
+    const uint32_t w = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
+    return order_key(__uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)));
+}
+// the float whose order key is `key`
+DEV float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+template <typename T, bool IN_REG>
 __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __restrict__ logits, int Vp, int k,
                                                                  const float* __restrict__ u,
                                                                  int32_t* __restrict__ next,
                                                                  int32_t* __restrict__ topk_idx,
                                                                  float* __restrict__ topk_prob) {
-    constexpr int E = 16 / sizeof(T);
-    extern __shared__ __attribute__((aligned(16))) char tk_row[];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t s_state[3];
     __shared__ int wsum[TK_THREADS / 64];
     __shared__ int sel_idx[TOPK_MAX];
-    __shared__ float sel_val[TOPK_MAX];
+    __shared__ uint32_t sel_key[TOPK_MAX];
     const int b = blockIdx.x, tid = threadIdx.x;
     const T* z = logits + (int64_t)b * Vp;
-    const T* src = z;
-    if constexpr (IN_LDS) {
-        T* row = (T*)tk_row;
-#pragma unroll 8
-        for (int c = tid; c < Vp / E; c += TK_THREADS) *(uint4*)(row + c * E) = ld16(z + c * E);
-        __syncthreads();
-        src = row;
-    }
-    const int per = (Vp + TK_THREADS - 1) / TK_THREADS;
+    int per = (Vp + TK_THREADS - 1) / TK_THREADS;
+    if constexpr (IN_REG) per = (per + 7) & ~7;
     const int j0 = min(Vp, tid * per), j1 = min(Vp, j0 + per);
-    auto key_at = [&](int j) { return order_key(to_f<T>(src[j])); };
+    uint4 rowc[IN_REG ? TK_REG_CHUNKS : 1];
+    if constexpr (IN_REG) {
+#pragma unroll
+        for (int c = 0; c < TK_REG_CHUNKS; ++c)
+            if (j0 + 8 * c < j1) rowc[c] = ld16(z + j0 + 8 * c);
+    }
+    // f(j, key) over the thread's ids in ascending order
+    auto for_keys = [&](auto f) {
+        if constexpr (IN_REG) {
+#pragma unroll
+            for (int c = 0; c < TK_REG_CHUNKS; ++c)
+                if (j0 + 8 * c < j1) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f(j0 + 8 * c + e, chunk_key(rowc[c], e));
+                }
+        } else {
+            for (int j = j0; j < j1; ++j) f(j, order_key(to_f<T>(z[j])));
+        }
+    };
 
     uint32_t prefix = 0, mask = 0;
     int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    // a bf16 value widens to a float with 16 zero low bits, so its key's low 16 bits are 0000
+    // (positive: key = bits | sign bit) or ffff (negative: key = ~bits); passes over them would
+    // put every remaining key in one bin and leave `need` as it is
+    constexpr int LAST_SHIFT = sizeof(T) == 2 ? 16 : 0;
+    for (int shift = 24; shift >= LAST_SHIFT; shift -= 8) {
         if (tid < 256) hist[tid] = 0;
         __syncthreads();
-        for (int j = j0; j < j1; ++j) {
-            const uint32_t key = key_at(j);
+        for_keys([&](int, uint32_t key) {
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
+        });
         __syncthreads();
         if (tid == 0) {
             int cum = 0, dgt = 255;
@@ -211,34 +235,33 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
         need = (int)s_state[2];
         __syncthreads();
     }
+    if constexpr (LAST_SHIFT == 16) prefix |= (prefix & 0x80000000u) ? 0u : 0xffffu;
     // prefix is now the k-th largest key; the keys above it and the `need` lowest-id keys equal
     // to it are the selection
     int n_gt = 0, n_eq = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = key_at(j);
+    for_keys([&](int, uint32_t key) {
         n_gt += key > prefix;
         n_eq += key == prefix;
-    }
+    });
     int tot;
     const int eq_before = block_excl_scan(n_eq, &tot, wsum);
     const int eq_take = max(0, min(n_eq, need - eq_before));
     const int pos0 = block_excl_scan(n_gt + eq_take, &tot, wsum);
     int p = pos0, eq_seen = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = key_at(j);
+    for_keys([&](int j, uint32_t key) {
         bool take = key > prefix;
         if (key == prefix) take = eq_seen++ < eq_take;
         if (take) {
             sel_idx[p] = j;
-            sel_val[p] = to_f<T>(src[j]);
+            sel_key[p] = key;
             ++p;
         }
-    }
+    });
     __syncthreads();
     if (tid >= 64) return;
     // one wave: bitonic sort of the k entries (padding sorts last) by larger value, then lower id
     const int lane = tid;
-    uint64_t e = lane < k ? ((uint64_t)(~order_key(sel_val[lane])) << 32) | (uint32_t)sel_idx[lane] : ~(uint64_t)0;
+    uint64_t e = lane < k ? ((uint64_t)(~sel_key[lane]) << 32) | (uint32_t)sel_idx[lane] : ~(uint64_t)0;
     for (int sz = 2; sz <= 64; sz <<= 1) {
         for (int st = sz >> 1; st > 0; st >>= 1) {
             const uint64_t o = ((uint64_t)__shfl_xor((int)(e >> 32), st) << 32) | (uint32_t)__shfl_xor((int)(uint32_t)e, st);
@@ -247,8 +270,8 @@ __global__ void __launch_bounds__(TK_THREADS) topk_sample_kernel(const T* __rest
         }
     }
     const int id = (int)(uint32_t)e;
-    // the value again from the row (exact: the row is unchanged)
-    const float zv = lane < k ? to_f<T>(src[id]) : -INFINITY;
+    // the logit back from its key (exact)
+    const float zv = lane < k ? key_value(~(uint32_t)(e >> 32)) : -INFINITY;
     const float zmax = __shfl(zv, 0);
     const float pr = lane < k ? expf(zv - zmax) : 0.f;
     float cdf = pr;
@@ -273,19 +296,13 @@ hipError_t topk_sample(const void* logits, int B, int Vp, int k, const float* u,
                        float* topk_prob, int is_bf16, hipStream_t s) {
     if (k < 1 || k > TOPK_MAX || k > Vp || Vp % 8) return hipErrorInvalidValue;
     const dim3 grid(B), blk(TK_THREADS);
-    if (is_bf16 && Vp <= TK_LDS_MAX)
-        topk_sample_kernel<bf16, true><<<grid, blk, (size_t)Vp * 2, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx,
-                                                                         topk_prob);
+    if (is_bf16 && Vp <= TK_REG_MAX)
+        topk_sample_kernel<bf16, true><<<grid, blk, 0, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx, topk_prob);
     else if (is_bf16)
         topk_sample_kernel<bf16, false><<<grid, blk, 0, s>>>((const bf16*)logits, Vp, k, u, next, topk_idx, topk_prob);
     else
         topk_sample_kernel<float, false><<<grid, blk, 0, s>>>((const float*)logits, Vp, k, u, next, topk_idx, topk_prob);
     return hipGetLastError();
-}
-
-void decode_setup() {
-    (void)hipFuncSetAttribute((const void*)topk_sample_kernel<bf16, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              TK_LDS_MAX * 2);
 }
 
 }  // namespace gpt2k
